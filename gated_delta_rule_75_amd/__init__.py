@@ -1,0 +1,166 @@
+"""MI355X (gfx950) Kimi Delta Attention: chunked prefill, append-prefill and decode.
+
+Thin Python binding over the C ABI in ``include/kda.h`` (library ``_kda.so``).  This
+module only checks and marshals torch tensors (device memory) and the current HIP stream;
+every step of the computation runs in the library's HIP kernels.
+
+Per sequence and head, with state S in R^{d_k x d_v} and alpha = exp(g) per key channel
+("Kimi K3, explained", "The math", gated delta rule equation, transposed):
+    S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import KdaError  # noqa: F401
+
+__all__ = ["prefill_chunked", "append_prefill", "decode_step", "workspace_size", "is_supported", "version",
+           "KdaError"]
+
+_DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
+
+
+def version() -> str:
+    return _lib.load().kda_version().decode()
+
+
+def is_supported(op: int, dtype: torch.dtype, dk: int, dv: int, chunk: int = 64) -> bool:
+    return bool(_lib.load().kda_is_supported(op, _DT[dtype], dk, dv, chunk))
+
+
+def workspace_size(op: int, n: int, t: int, h: int, dk: int, dv: int, dtype: torch.dtype, chunk: int) -> int:
+    ws = _lib.load().kda_workspace_size(op, n, t, h, dk, dv, _DT[dtype], chunk)
+    if ws == 2 ** 64 - 1:
+        raise KdaError(_lib.KDA_ERR_UNSUPPORTED, f"unsupported op={op} dtype={dtype} dk={dk} dv={dv} chunk={chunk}")
+    return int(ws)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtype=None, shape=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def prefill_chunked(q, k, v, g, beta, state=None, *, chunk=64, out=None, state_out=None, final_state=True,
+                    workspace=None):
+    """Chunked prefill of B equal-length sequences.
+
+    q, k [B,T,H,dk], v [B,T,H,dv] (float32 or bfloat16), g [B,T,H,dk] float32 (log alpha),
+    beta [B,T,H] (same dtype as q), state [B,H,dk,dv] float32 or None.
+    Returns (o [B,T,H,dv] float32, S_T [B,H,dk,dv] float32 or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    dev = q.device
+    _check(q, "q", dt, (B, T, H, dk), dev)
+    _check(k, "k", dt, (B, T, H, dk), dev)
+    _check(v, "v", dt, (B, T, H, dv), dev)
+    _check(g, "g", torch.float32, (B, T, H, dk), dev)
+    _check(beta, "beta", dt, (B, T, H), dev)
+    _check(state, "state", torch.float32, (B, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, (B, T, H, dv), dev)
+    if state_out is None and final_state:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(state_out, "state_out", torch.float32, (B, H, dk, dv), dev)
+    ws_bytes = workspace_size(_lib.KDA_OP_PREFILL, B, T, H, dk, dv, dt, chunk)
+    ws = _workspace(ws_bytes, dev, workspace)
+    L = _lib.load()
+    _lib.check(L.kda_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
+                                     _ptr(state_out), B, T, H, dk, dv, _DT[dt], chunk, _ptr(ws), ws_bytes,
+                                     _stream(dev)))
+    return out, state_out
+
+
+def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=None, state_out=None,
+                   final_state=True, workspace=None):
+    """Append-prefill of N packed segments (token-major [T_total, H, d]) on carried states.
+
+    cu_seqlens: int32 GPU tensor [N+1] (0, ..., T_total).  state [N,H,dk,dv] float32 or None.
+    Returns (o [T_total,H,dv] float32, S_T [N,H,dk,dv] float32 or None)."""
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    dev = q.device
+    _check(q, "q", dt, (T, H, dk), dev)
+    _check(k, "k", dt, (T, H, dk), dev)
+    _check(v, "v", dt, (T, H, dv), dev)
+    _check(g, "g", torch.float32, (T, H, dk), dev)
+    _check(beta, "beta", dt, (T, H), dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    _check(state, "state", torch.float32, (N, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, (T, H, dv), dev)
+    if state_out is None and final_state:
+        state_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(state_out, "state_out", torch.float32, (N, H, dk, dv), dev)
+    ws_bytes = workspace_size(_lib.KDA_OP_APPEND, N, T, H, dk, dv, dt, chunk)
+    ws = _workspace(ws_bytes, dev, workspace)
+    L = _lib.load()
+    _lib.check(L.kda_append_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+                                    _ptr(state), _ptr(out), _ptr(state_out), H, dk, dv, _DT[dt], chunk, _ptr(ws),
+                                    ws_bytes, _stream(dev)))
+    return out, state_out
+
+
+def decode_step(q, k, v, g, beta, state, *, out=None, state_out=None):
+    """One decode step for N sequences: q, k, g [N,H,dk], v [N,H,dv], beta [N,H], state [N,H,dk,dv].
+
+    The state is updated in place unless ``state_out`` is given.  Returns o [N,H,dv] float32."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    dev = q.device
+    _check(q, "q", dt, (N, H, dk), dev)
+    _check(k, "k", dt, (N, H, dk), dev)
+    _check(v, "v", dt, (N, H, dv), dev)
+    _check(g, "g", torch.float32, (N, H, dk), dev)
+    _check(beta, "beta", dt, (N, H), dev)
+    _check(state, "state", torch.float32, (N, H, dk, dv), dev)
+    if state_out is None:
+        state_out = state
+    _check(state_out, "state_out", torch.float32, (N, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, (N, H, dv), dev)
+    L = _lib.load()
+    _lib.check(L.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(state_out),
+                                 _ptr(out), N, H, dk, dv, _DT[dt], _stream(dev)))
+    return out

@@ -1,0 +1,67 @@
+"""ctypes loader of the in-tree HIP library ``_kda.so`` (declarations: include/kda.h).
+
+The library is loaded after ``import torch`` so that it binds to the HIP runtime torch
+already loaded (one runtime per process).  A missing library is an error: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime first)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_kda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_MISALIGNED = 0, -1, -2, -3
+KDA_ERR_ALIAS, KDA_ERR_WORKSPACE, KDA_ERR_HIP = -4, -5, -6
+KDA_F32, KDA_BF16 = 0, 1
+KDA_OP_PREFILL, KDA_OP_APPEND, KDA_OP_DECODE = 0, 1, 2
+
+# every symbol include/kda.h declares
+EXPORTS = ("kda_prefill_chunked", "kda_append_prefill", "kda_decode_step", "kda_workspace_size",
+           "kda_is_supported", "kda_status_string", "kda_last_error", "kda_version")
+
+_LIB = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def load():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"KDA HIP library not built: {LIB_PATH} (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.kda_prefill_chunked.restype = ctypes.c_int
+    L.kda_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.kda_append_prefill.restype = ctypes.c_int
+    L.kda_append_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, i32, i32, i32, i32, i32, vp, sz,
+                                     vp]
+    L.kda_decode_step.restype = ctypes.c_int
+    L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.kda_workspace_size.restype = sz
+    L.kda_workspace_size.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32]
+    L.kda_is_supported.restype = ctypes.c_int
+    L.kda_is_supported.argtypes = [i32, i32, i32, i32, i32]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_status_string.argtypes = [ctypes.c_int]
+    L.kda_last_error.restype = ctypes.c_char_p
+    L.kda_last_error.argtypes = []
+    L.kda_version.restype = ctypes.c_char_p
+    L.kda_version.argtypes = []
+    _LIB = L
+    return L
+
+
+def check(status: int):
+    if status != KDA_OK:
+        L = load()
+        msg = L.kda_last_error().decode() or L.kda_status_string(status).decode()
+        raise KdaError(status, msg)

@@ -1,0 +1,253 @@
+// C ABI of the KDA library: argument validation, kernel selection, launch and
+// status reporting.  Declarations and contracts: include/kda.h.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return KDA_OK;
+}
+
+bool env_flag(const char* name) {
+    const char* v = std::getenv(name);
+    return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(Span a, Span b) {
+    if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+int check_hip(hipError_t e, hipStream_t s, const char* what) {
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    if (env_flag("KDA_DEBUG_SYNC")) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s (debug sync): %s", what, hipGetErrorString(e));
+    }
+    return ok();
+}
+
+// Host-side stand-in for a launch failure, for tests of the error path only.
+bool injected_launch_failure() { return env_flag("KDA_TEST_FAIL_LAUNCH"); }
+
+bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+// Which chunked implementation serves (dtype, dk, dv, chunk): 2 = matrix cores, 1 = fp32, 0 = none.
+int prefill_path(int32_t dtype, int32_t dk, int32_t dv, int32_t chunk) {
+    if (kda::chunk_mfma_supported(dtype == KDA_BF16, dk, dv, chunk)) return 2;
+    if (kda::chunk_f32_supported(dk, dv, chunk)) return 1;
+    return 0;
+}
+
+size_t ws_size(int32_t op, int64_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t dtype, int32_t chunk) {
+    if (op == KDA_OP_DECODE) return 0;
+    if (prefill_path(dtype, dk, dv, chunk) != 2) return 0;
+    const bool fixed = op == KDA_OP_PREFILL;
+    const int64_t T_total = fixed ? N * T : T;
+    return kda::chunk_mfma_workspace(N, fixed ? T : 0, T_total, fixed, H, chunk);
+}
+
+int run_prefill(const kda::PrefillArgs& a, int32_t dtype, hipStream_t s, const char* name) {
+    const int path = prefill_path(dtype, a.dk, a.dv, a.chunk);
+    if (injected_launch_failure()) return fail(KDA_ERR_HIP, "%s: injected launch failure (KDA_TEST_FAIL_LAUNCH)", name);
+    hipError_t e = path == 2 ? kda::launch_chunk_mfma(a, s) : kda::launch_chunk_f32(a, s);
+    return check_hip(e, s, name);
+}
+
+// Alignment: q, k and g are read with 16-byte vector loads by the prefill kernels
+// (qkg_align = 16); every other tensor only needs its element alignment.
+int validate_common(const void* q, const void* k, const void* v, const float* g, const void* beta, int64_t tokens,
+                    int32_t H, int32_t dk, int32_t dv, int32_t dtype, size_t qkg_align) {
+    if (H <= 0 || dk <= 0 || dv <= 0) return fail(KDA_ERR_INVALID_ARG, "H, d_k, d_v must be positive");
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "dtype must be KDA_F32 or KDA_BF16");
+    if (tokens > 0 && (!q || !k || !v || !g || !beta))
+        return fail(KDA_ERR_INVALID_ARG, "q, k, v, g and beta are required");
+    const size_t esz = dtype == KDA_BF16 ? 2 : 4;
+    const size_t qa = qkg_align > esz ? qkg_align : esz;
+    if (!aligned_to(q, qa) || !aligned_to(k, qa) || !aligned_to(g, qkg_align > 4 ? qkg_align : 4))
+        return fail(KDA_ERR_MISALIGNED, "q, k and g must be %zu-byte aligned", qa);
+    if (!aligned_to(v, esz) || !aligned_to(beta, esz))
+        return fail(KDA_ERR_MISALIGNED, "v and beta must be aligned to their element size");
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_version(void) { return "kda-mi355x 0.1.0 (gfx950)"; }
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+const char* kda_status_string(int status) {
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported shape, dtype or chunk size";
+    case KDA_ERR_MISALIGNED: return "pointer not aligned as required";
+    case KDA_ERR_ALIAS: return "output buffers overlap inputs";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int kda_is_supported(int32_t op, int32_t dtype, int32_t d_k, int32_t d_v, int32_t chunk) {
+    if (!valid_dtype(dtype)) return 0;
+    if (op == KDA_OP_DECODE) return kda::decode_supported(d_k, d_v) ? 1 : 0;
+    if (op == KDA_OP_PREFILL || op == KDA_OP_APPEND) return prefill_path(dtype, d_k, d_v, chunk) ? 1 : 0;
+    return 0;
+}
+
+size_t kda_workspace_size(int32_t op, int64_t B_or_N, int64_t T, int32_t H, int32_t d_k, int32_t d_v,
+                          int32_t dtype, int32_t chunk) {
+    if (B_or_N < 0 || T < 0 || H <= 0 || !kda_is_supported(op, dtype, d_k, d_v, chunk)) return (size_t)-1;
+    return ws_size(op, B_or_N, T, H, d_k, d_v, dtype, chunk);
+}
+
+int kda_prefill_chunked(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                        const float* state_in, float* out, float* state_out, int64_t B, int64_t T, int32_t H,
+                        int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk, void* workspace,
+                        size_t workspace_bytes, void* hip_stream) {
+    static const char* name = "kda_prefill_chunked";
+    if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARG, "%s: B and T must be >= 0", name);
+    if (int rc = validate_common(q, k, v, g, beta, B * T, H, d_k, d_v, dtype, 16)) return rc;
+    if (!prefill_path(dtype, d_k, d_v, chunk))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype=%d d_k=%d d_v=%d chunk=%d not implemented", name, dtype, d_k, d_v,
+                    chunk);
+    if (B * T > 0 && !out) return fail(KDA_ERR_INVALID_ARG, "%s: out is required", name);
+    if (!aligned_to(out, 4) || !aligned_to(state_in, 4) || !aligned_to(state_out, 4) || !aligned_to(workspace, 256))
+        return fail(KDA_ERR_MISALIGNED, "%s: out and states must be 4-byte, workspace 256-byte aligned", name);
+    const size_t esz = dtype == KDA_BF16 ? 2 : 4;
+    const size_t tokens = (size_t)(B * T);
+    const size_t sbytes = (size_t)B * H * d_k * d_v * 4;
+    const Span sin{state_in, state_in ? sbytes : 0}, sout{state_out, state_out ? sbytes : 0};
+    const Span o{out, tokens * H * d_v * 4};
+    const Span ins[] = {{q, tokens * H * d_k * esz}, {k, tokens * H * d_k * esz}, {v, tokens * H * d_v * esz},
+                        {g, tokens * H * d_k * 4},   {beta, tokens * H * esz},    sin};
+    for (const Span& in : ins)
+        if (overlap(o, in) || (overlap(sout, in) && in.p != state_in))
+            return fail(KDA_ERR_ALIAS, "%s: out/state_out overlap an input", name);
+    if (overlap(o, sout)) return fail(KDA_ERR_ALIAS, "%s: out overlaps state_out", name);
+    if (overlap(sin, sout) && state_in != state_out)
+        return fail(KDA_ERR_ALIAS, "%s: state_out partially overlaps state_in", name);
+    const size_t need = ws_size(KDA_OP_PREFILL, B, T, H, d_k, d_v, dtype, chunk);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(KDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    kda::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = state_in; a.o = out; a.sT = state_out;
+    a.cu = nullptr; a.N = B; a.T_fixed = T; a.T_total = B * T;
+    a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.bf16 = dtype == KDA_BF16;
+    a.ws = workspace; a.ws_bytes = workspace_bytes;
+    return run_prefill(a, dtype, static_cast<hipStream_t>(hip_stream), name);
+}
+
+int kda_append_prefill(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                       const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in, float* out,
+                       float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+    static const char* name = "kda_append_prefill";
+    if (N < 0 || T_total < 0) return fail(KDA_ERR_INVALID_ARG, "%s: N and T_total must be >= 0", name);
+    if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens is required", name);
+    if (int rc = validate_common(q, k, v, g, beta, T_total, H, d_k, d_v, dtype, 16)) return rc;
+    if (!prefill_path(dtype, d_k, d_v, chunk))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype=%d d_k=%d d_v=%d chunk=%d not implemented", name, dtype, d_k, d_v,
+                    chunk);
+    if (T_total > 0 && !out) return fail(KDA_ERR_INVALID_ARG, "%s: out is required", name);
+    if (!aligned_to(out, 4) || !aligned_to(state_in, 4) || !aligned_to(state_out, 4) || !aligned_to(workspace, 256))
+        return fail(KDA_ERR_MISALIGNED, "%s: out and states must be 4-byte, workspace 256-byte aligned", name);
+    const size_t esz = dtype == KDA_BF16 ? 2 : 4;
+    const size_t tokens = (size_t)T_total;
+    const size_t sbytes = (size_t)N * H * d_k * d_v * 4;
+    const Span sin{state_in, state_in ? sbytes : 0}, sout{state_out, state_out ? sbytes : 0};
+    const Span o{out, tokens * H * d_v * 4};
+    const Span ins[] = {{q, tokens * H * d_k * esz}, {k, tokens * H * d_k * esz}, {v, tokens * H * d_v * esz},
+                        {g, tokens * H * d_k * 4},   {beta, tokens * H * esz},    {cu_seqlens, (size_t)(N + 1) * 4},
+                        sin};
+    for (const Span& in : ins)
+        if (overlap(o, in) || (overlap(sout, in) && in.p != state_in))
+            return fail(KDA_ERR_ALIAS, "%s: out/state_out overlap an input", name);
+    if (overlap(o, sout)) return fail(KDA_ERR_ALIAS, "%s: out overlaps state_out", name);
+    if (overlap(sin, sout) && state_in != state_out)
+        return fail(KDA_ERR_ALIAS, "%s: state_out partially overlaps state_in", name);
+    const size_t need = ws_size(KDA_OP_APPEND, N, T_total, H, d_k, d_v, dtype, chunk);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(KDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    kda::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = state_in; a.o = out; a.sT = state_out;
+    a.cu = cu_seqlens; a.N = N; a.T_fixed = 0; a.T_total = T_total;
+    a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.bf16 = dtype == KDA_BF16;
+    a.ws = workspace; a.ws_bytes = workspace_bytes;
+    return run_prefill(a, dtype, static_cast<hipStream_t>(hip_stream), name);
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                    const float* state_in, float* state_out, float* out, int32_t N, int32_t H, int32_t d_k,
+                    int32_t d_v, int32_t dtype, void* hip_stream) {
+    static const char* name = "kda_decode_step";
+    if (N < 0) return fail(KDA_ERR_INVALID_ARG, "%s: N must be >= 0", name);
+    if (int rc = validate_common(q, k, v, g, beta, N, H, d_k, d_v, dtype, 1)) return rc;
+    if (!kda::decode_supported(d_k, d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d not implemented", name, d_k, d_v);
+    if (N > 0 && (!state_in || !state_out || !out))
+        return fail(KDA_ERR_INVALID_ARG, "%s: state_in, state_out and out are required", name);
+    if (!aligned_to(out, 4) || !aligned16(state_in) || !aligned16(state_out))
+        return fail(KDA_ERR_MISALIGNED, "%s: states must be 16-byte aligned, out 4-byte aligned", name);
+    const size_t esz = dtype == KDA_BF16 ? 2 : 4;
+    const size_t sbytes = (size_t)N * H * d_k * d_v * 4;
+    const Span sin{state_in, sbytes}, sout{state_out, sbytes}, o{out, (size_t)N * H * d_v * 4};
+    const Span ins[] = {{q, (size_t)N * H * d_k * esz}, {k, (size_t)N * H * d_k * esz}, {v, (size_t)N * H * d_v * esz},
+                        {g, (size_t)N * H * d_k * 4},   {beta, (size_t)N * H * esz},    sin};
+    for (const Span& in : ins)
+        if (overlap(o, in) || (overlap(sout, in) && in.p != state_in))
+            return fail(KDA_ERR_ALIAS, "%s: out/state_out overlap an input", name);
+    if (overlap(o, sout)) return fail(KDA_ERR_ALIAS, "%s: out overlaps state_out", name);
+    if (overlap(sin, sout) && state_in != state_out)
+        return fail(KDA_ERR_ALIAS, "%s: state_out partially overlaps state_in", name);
+    if (injected_launch_failure()) return fail(KDA_ERR_HIP, "%s: injected launch failure (KDA_TEST_FAIL_LAUNCH)", name);
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s_in = state_in; a.s_out = state_out; a.o = out;
+    a.N = N; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    return check_hip(kda::launch_decode(a, s), s, name);
+}
+
+}  // extern "C"

@@ -1,0 +1,549 @@
+// KDA chunked prefill on the gfx950 matrix cores (bfloat16 storage, d_k = d_v = 128,
+// 64-token chunks).
+//
+// Method ("Kimi K3, explained": "Training in chunks", "The math"): inside a chunk the
+// product of per-token decay-and-erase transitions becomes dense products plus one
+// unit-lower-triangular inverse, and only the state crosses chunk boundaries.  With
+// G[r] = sum_{s<=r} g_s per key channel (restarting at the chunk), S0 the entering
+// state and L the chunk length:
+//   A[r,s] = beta_r sum_c k_rc k_sc exp(G_rc - G_sc)  (s < r)     T = (I + A)^{-1}
+//   M[r,s] =        sum_c q_rc k_sc exp(G_rc - G_sc)  (s <= r)
+//   K+ = K * exp(G),  Q+ = Q * exp(G),  K' = K * exp(G_{L-1} - G),  gamma = exp(G_{L-1})
+//   D  = T Diag(beta) (V - K+ S0)          (per-token corrections)
+//   O  = Q+ S0 + M D
+//   S1 = Diag(gamma) S0 + K'^T D
+//
+// Two kernels:
+//  * prep (one workgroup per chunk and head, all chunks in parallel): the decay
+//    factors, the gated Gram matrices A and M (fp16 matrix-core products with fp32
+//    accumulation), T by blocked forward substitution (fp32 matrix-core products),
+//    and the fp16 operand tiles K+, Q+, K'^T, T, M plus fp32 gamma, written to the
+//    workspace already in the lane order of the matrix-core operand registers.
+//  * state (one workgroup per sequence, head and 16-column value block; value
+//    columns never interact): walks the chunks in order with the fp32 state block in
+//    registers, four waves each owning 16 tokens of the chunk (R, D, O) and 32 key
+//    channels of the state (the update).
+//
+// Decay factors never overflow: the Gram matrices use per-16-token reference points.
+// For rows r in token block i and columns s in block j < i,
+//   exp(G_r - G_s) = exp(G_r - P_i) * exp(P_i - P_{j+1}) * exp(P_{j+1} - G_s)
+// (P_i = G at the end of block i-1), every factor <= 1.  Inside a diagonal block the
+// reference is the block's 8th token; those factors are bounded by the decay of at
+// most 8 tokens, which must stay below e^10 for fp16 (checked per chunk; a chunk that
+// violates it poisons its outputs with NaN rather than returning wrong numbers).
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int C = 64;   // tokens per chunk
+constexpr int DK = 128;
+constexpr int DV = 128;
+constexpr int BV = 16;  // value columns per state workgroup
+constexpr int NVB = DV / BV;
+
+// chunk record in the workspace (bytes); tiles are 64 lanes x 16 bytes
+constexpr int kTile = 1024;
+constexpr int kOffKp = 0;                 // 16 tiles (token block tb, k-step ks): tb*4+ks
+constexpr int kOffQp = 16 * kTile;        // 16 tiles
+constexpr int kOffKdT = 32 * kTile;       // 16 tiles (channel block cb, k-step ks): cb*2+ks
+constexpr int kOffT = 48 * kTile;         // 8 tiles (row block rb, k-step kb): rb*2+kb
+constexpr int kOffM = 56 * kTile;         // 8 tiles
+constexpr int kOffGamma = 64 * kTile;     // 128 floats
+constexpr int kRecord = 64 * kTile + 512; // 66048 bytes (multiple of 256)
+
+__device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Sequence bounds and chunk -> workspace slot.
+struct SeqMap {
+    const int32_t* cu;
+    int64_t T_fixed;
+    int64_t nck_fixed;  // chunks per sequence when fixed-length
+    int64_t N;
+
+    __device__ __forceinline__ void bounds(int64_t n, int64_t& bos, int64_t& eos) const {
+        if (cu) {
+            bos = cu[n];
+            eos = cu[n + 1];
+        } else {
+            bos = n * T_fixed;
+            eos = bos + T_fixed;
+        }
+    }
+    // first slot of sequence n; slots of n are base(n) .. base(n) + chunks(n) - 1
+    __device__ __forceinline__ int64_t base(int64_t n) const {
+        return cu ? (int64_t)cu[n] / C + n : n * nck_fixed;
+    }
+    // slot -> (sequence, chunk index); false for a slot no chunk uses
+    __device__ __forceinline__ bool locate(int64_t slot, int64_t& n, int64_t& c) const {
+        if (!cu) {
+            n = slot / nck_fixed;
+            c = slot % nck_fixed;
+            return n < N;
+        }
+        int64_t lo = 0, hi = N - 1;
+        if (N <= 0 || base(0) > slot) return false;
+        while (lo < hi) {  // largest n with base(n) <= slot
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (base(mid) <= slot) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+        c = slot - base(n);
+        int64_t bos, eos;
+        bounds(n, bos, eos);
+        return c * C < eos - bos;
+    }
+};
+
+// ------------------------------------------------------------------------------------------
+// prep kernel: one workgroup (4 waves) per (slot, head)
+// ------------------------------------------------------------------------------------------
+struct PrepLds {
+    float tot[4][DK];              // per-block sum of g
+    float gmid[4][DK];             // within-block cumulative g at the block's 8th token
+    _Float16 kc[3][4][64][8];      // column operands of blocks 0..2, fragment order
+    _Float16 kdT[DK][C + 8];       // K'^T
+    float A[C][C + 1];             // beta-scaled strictly lower Gram, fp32
+    float M[C][C + 1];
+    float T[C][C + 1];
+    float X[4][16][17];            // per-wave scratch for the inverse
+    int unsafe;
+};
+
+__device__ __forceinline__ float bf(uint16_t b) { return bf16_to_f32(b); }
+
+// 16x16 = A(16x16) * B(16x16), fp32 operands from LDS, four 16x16x4 steps.
+__device__ __forceinline__ floatx4 mm16(const float* Ap, int lda, const float* Bp, int ldb, floatx4 acc, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x4f32(Ap[r * lda + 4 * ks + kq], Bp[(4 * ks + kq) * ldb + r], acc);
+    return acc;
+}
+
+__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, SeqMap sm) {
+    __shared__ PrepLds L;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int H = a.H;
+    const int h = blockIdx.y;
+    const int64_t slot = blockIdx.x;
+    int64_t n, c;
+    if (!sm.locate(slot, n, c)) return;  // uniform over the workgroup
+    int64_t bos, eos;
+    sm.bounds(n, bos, eos);
+    const int64_t t0 = bos + c * C;
+    const int Lc = (int)((eos - t0) < C ? (eos - t0) : C);
+    unsigned char* rec = static_cast<unsigned char*>(a.ws) + (slot * H + h) * (int64_t)kRecord;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    const uint16_t* k = static_cast<const uint16_t*>(a.k);
+    const uint16_t* beta = static_cast<const uint16_t*>(a.beta);
+
+    if (threadIdx.x == 0) L.unsafe = 0;
+
+    // ---- load this lane's token (16w + lr) and its 32 channels 32*ks + 8*lg + i
+    const int r = 16 * w + lr;
+    const bool valid = r < Lc;
+    const int64_t rowk = ((t0 + r) * H + h) * (int64_t)DK;
+    float kf[4][8], qf[4][8], gl[4][8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int c0 = 32 * ks + 8 * lg;
+        if (valid) {
+            const uint4 kv = *reinterpret_cast<const uint4*>(k + rowk + c0);
+            const uint4 qv = *reinterpret_cast<const uint4*>(q + rowk + c0);
+            const float4 g0 = *reinterpret_cast<const float4*>(a.g + rowk + c0);
+            const float4 g1 = *reinterpret_cast<const float4*>(a.g + rowk + c0 + 4);
+            const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kf[ks][2 * i] = bf(kw[i] & 0xFFFF);
+                kf[ks][2 * i + 1] = bf(kw[i] >> 16);
+                qf[ks][2 * i] = bf(qw[i] & 0xFFFF);
+                qf[ks][2 * i + 1] = bf(qw[i] >> 16);
+            }
+            gl[ks][0] = g0.x; gl[ks][1] = g0.y; gl[ks][2] = g0.z; gl[ks][3] = g0.w;
+            gl[ks][4] = g1.x; gl[ks][5] = g1.y; gl[ks][6] = g1.z; gl[ks][7] = g1.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kf[ks][i] = qf[ks][i] = gl[ks][i] = 0.f;
+        }
+    }
+
+    // ---- within-block inclusive cumulative sum of g over the 16 tokens (lanes lr)
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float y = __shfl_up(gl[ks][i], d, 16);
+                if (lr >= d) gl[ks][i] += y;
+            }
+    }
+    if (lr == 15) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) L.tot[w][32 * ks + 8 * lg + i] = gl[ks][i];
+    }
+    if (lr == 7) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) L.gmid[w][32 * ks + 8 * lg + i] = gl[ks][i];
+    }
+    __syncthreads();
+
+    // ---- factors and operand tiles
+    half8 KR[4], QR[4], KRd[4], QRd[4], KCd[4];
+    bool unsafe = false;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        half8 kp, qp, kc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ch = 32 * ks + 8 * lg + i;
+            float P = 0.f, Ctot = 0.f;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float t = L.tot[b][ch];
+                if (b < w) P += t;
+                Ctot += t;
+            }
+            const float Dw = L.tot[w][ch];
+            const float gloc = gl[ks][i];
+            const float gm = L.gmid[w][ch];
+            const float eloc = fast_exp(gloc);                    // exp(G_r - P_w)
+            const float ecol = fast_exp(Dw - gloc);               // exp(P_{w+1} - G_r)
+            const float eP = fast_exp(P);                         // exp(P_w)
+            const float etail = fast_exp(Ctot - P - Dw);          // exp(G_{L-1} - P_{w+1})
+            const float dr = gloc - gm, dc = gm - gloc;           // diagonal-block exponents
+            unsafe |= (dr > 10.f) || (dc > 10.f);
+            const float erd = fast_exp(dr), ecd = fast_exp(dc);
+            const float kk = kf[ks][i], qq = qf[ks][i];
+            kp[i] = (_Float16)(kk * eloc * eP);
+            qp[i] = (_Float16)(qq * eloc * eP);
+            L.kdT[ch][r] = (_Float16)(kk * ecol * etail);
+            KR[ks][i] = (_Float16)(kk * eloc);
+            QR[ks][i] = (_Float16)(qq * eloc);
+            kc[i] = (_Float16)(kk * ecol);
+            KRd[ks][i] = (_Float16)(kk * erd);
+            QRd[ks][i] = (_Float16)(qq * erd);
+            KCd[ks][i] = (_Float16)(kk * ecd);
+        }
+        *reinterpret_cast<half8*>(rec + kOffKp + (w * 4 + ks) * kTile + lane * 16) = kp;
+        *reinterpret_cast<half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16) = qp;
+        if (w < 3) *reinterpret_cast<half8*>(&L.kc[w][ks][lane][0]) = kc;
+    }
+    if (unsafe) L.unsafe = 1;  // benign race: every writer stores 1
+    __syncthreads();
+
+    // ---- gated Gram matrices, row block w (tiles (w, j) for j <= w)
+    float brow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * w + 4 * lg + i;
+        brow[i] = rr < Lc ? bf(beta[(t0 + rr) * H + h]) : 0.f;
+    }
+    for (int j = 0; j < 4; ++j) {
+        floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+        if (j < w) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                half8 bcol = *reinterpret_cast<const half8*>(&L.kc[j][ks][lane][0]);
+                if (j + 1 < w) {  // scale by exp(P_w - P_{j+1}), the decay of blocks j+1 .. w-1
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int ch = 32 * ks + 8 * lg + i;
+                        float z = 0.f;
+                        for (int b = j + 1; b < w; ++b) z += L.tot[b][ch];
+                        bcol[i] = (_Float16)((float)bcol[i] * fast_exp(z));
+                    }
+                }
+                accA = mfma16x16x32(KR[ks], bcol, accA);
+                accM = mfma16x16x32(QR[ks], bcol, accM);
+            }
+        } else if (j == w) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                accA = mfma16x16x32(KRd[ks], KCd[ks], accA);
+                accM = mfma16x16x32(QRd[ks], KCd[ks], accM);
+            }
+        }
+        // accumulator: column s = lr of block j, rows 4*lg + i of block w
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 16 * w + 4 * lg + i, ss = 16 * j + lr;
+            L.A[rr][ss] = (ss < rr) ? brow[i] * accA[i] : 0.f;
+            L.M[rr][ss] = (ss <= rr) ? accM[i] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (lane = column)
+    if (lane < 16) {
+        const int j = lane, o = 16 * w;
+        float tc[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < rr; ++s) acc += L.A[o + rr][o + s] * tc[s];
+            tc[rr] = rr < j ? 0.f : (rr == j ? 1.f : -acc);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) L.T[o + rr][o + j] = tc[rr];
+    }
+    // zero the strictly upper blocks of T
+    for (int e = threadIdx.x; e < C * C; e += 256) {
+        const int rr = e / C, ss = e % C;
+        if ((ss >> 4) > (rr >> 4)) L.T[rr][ss] = 0.f;
+    }
+    __syncthreads();
+    // off-diagonal blocks: T_ij = -T_ii * (sum_{m=j}^{i-1} A_im T_mj), by distance i - j
+    for (int dist = 1; dist < 4; ++dist) {
+        const int j = w, i = w + dist;
+        if (i < 4) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int m = j; m < i; ++m) acc = mm16(&L.A[16 * i][16 * m], C + 1, &L.T[16 * m][16 * j], C + 1, acc, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) L.X[w][4 * lg + e][lr] = acc[e];
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+            floatx4 t = {0.f, 0.f, 0.f, 0.f};
+            t = mm16(&L.T[16 * i][16 * i], C + 1, &L.X[w][0][0], 17, t, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) L.T[16 * i + 4 * lg + e][16 * j + lr] = -t[e];
+        }
+        __syncthreads();
+    }
+
+    // ---- write T, M (8 tiles each) and K'^T (16 tiles) as fp16 operand tiles
+    for (int t = w; t < 8; t += 4) {
+        const int rb = t >> 1, kb = t & 1;
+        half8 tv, mv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            tv[i] = (_Float16)L.T[16 * rb + lr][32 * kb + 8 * lg + i];
+            mv[i] = (_Float16)L.M[16 * rb + lr][32 * kb + 8 * lg + i];
+        }
+        *reinterpret_cast<half8*>(rec + kOffT + t * kTile + lane * 16) = tv;
+        *reinterpret_cast<half8*>(rec + kOffM + t * kTile + lane * 16) = mv;
+    }
+    for (int t = w; t < 16; t += 4) {
+        const int cb = t >> 1, ks = t & 1;
+        const half8 kd = *reinterpret_cast<const half8*>(&L.kdT[16 * cb + lr][32 * ks + 8 * lg]);
+        *reinterpret_cast<half8*>(rec + kOffKdT + t * kTile + lane * 16) = kd;
+    }
+    if (w == 0) {
+        float* gam = reinterpret_cast<float*>(rec + kOffGamma);
+        const float poison = L.unsafe ? __builtin_nanf("") : 0.f;
+        for (int ch = lane; ch < DK; ch += 64)
+            gam[ch] = fast_exp(L.tot[0][ch] + L.tot[1][ch] + L.tot[2][ch] + L.tot[3][ch]) + poison;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// state kernel: one workgroup (4 waves) per (sequence, head, 16-column value block)
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
+    __shared__ _Float16 S_lds[BV][DK + 8];  // state block as matrix-core B operand: [column][channel]
+    __shared__ _Float16 R_lds[BV][C + 8];   // [column][token]
+    __shared__ _Float16 D_lds[BV][C + 8];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int H = a.H;
+
+    // workgroup -> (sequence, head, value block); the 8 value blocks of a (sequence, head)
+    // land on one XCD (workgroups are dealt to the 8 XCDs round-robin) so they share its L2
+    const int64_t L_id = blockIdx.x;
+    const int64_t nh_total = sm.N * H;
+    int64_t nh;
+    int vb;
+    if ((nh_total & 7) == 0) {
+        const int64_t xcd = L_id & 7, u = L_id >> 3;
+        vb = (int)(u & 7);
+        nh = xcd + 8 * (u >> 3);
+    } else {
+        vb = (int)(L_id % NVB);
+        nh = L_id / NVB;
+    }
+    const int64_t n = nh / H;
+    const int h = (int)(nh % H);
+    int64_t bos, eos;
+    sm.bounds(n, bos, eos);
+    const int64_t nchunks = (eos - bos + C - 1) / C;
+    const int64_t slot0 = sm.base(n);
+    const uint16_t* v = static_cast<const uint16_t*>(a.v);
+    const uint16_t* beta = static_cast<const uint16_t*>(a.beta);
+    const int64_t sbase = nh * (int64_t)DK * DV + vb * BV;
+
+    // fp32 state rows owned by this wave: channel blocks 2w, 2w+1 (accumulator layout)
+    floatx4 Sf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int cb = 2 * w + t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = 16 * cb + 4 * lg + i;
+            Sf[t][i] = a.s0 ? a.s0[sbase + (int64_t)ch * DV + lr] : 0.f;
+        }
+        half4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = (_Float16)Sf[t][i];
+        *reinterpret_cast<half4*>(&S_lds[lr][16 * cb + 4 * lg]) = hv;
+    }
+    __syncthreads();
+
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const unsigned char* rec =
+            static_cast<const unsigned char*>(a.ws) + ((slot0 + c) * H + h) * (int64_t)kRecord;
+        const int64_t t0 = bos + c * C;
+        const int Lc = (int)((eos - t0) < C ? (eos - t0) : C);
+        half8 kp[4], qp[4], kd[2][2], tt[2], mm[2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            kp[ks] = *reinterpret_cast<const half8*>(rec + kOffKp + (w * 4 + ks) * kTile + lane * 16);
+            qp[ks] = *reinterpret_cast<const half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                kd[t][ks] = *reinterpret_cast<const half8*>(rec + kOffKdT + ((2 * w + t) * 2 + ks) * kTile + lane * 16);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            tt[kb] = *reinterpret_cast<const half8*>(rec + kOffT + (w * 2 + kb) * kTile + lane * 16);
+            mm[kb] = *reinterpret_cast<const half8*>(rec + kOffM + (w * 2 + kb) * kTile + lane * 16);
+        }
+        float gam[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float4 gv = *reinterpret_cast<const float4*>(rec + kOffGamma + (16 * (2 * w + t) + 4 * lg) * 4);
+            gam[t][0] = gv.x; gam[t][1] = gv.y; gam[t][2] = gv.z; gam[t][3] = gv.w;
+        }
+        float vv[4], bb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 16 * w + 4 * lg + i;
+            const bool ok = rr < Lc;
+            vv[i] = ok ? bf(v[((t0 + rr) * H + h) * (int64_t)DV + vb * BV + lr]) : 0.f;
+            bb[i] = ok ? bf(beta[(t0 + rr) * H + h]) : 0.f;
+        }
+
+        // X = K+ S0, Y = Q+ S0 for this wave's 16 tokens
+        floatx4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const half8 sb = *reinterpret_cast<const half8*>(&S_lds[lr][32 * ks + 8 * lg]);
+            X = mfma16x16x32(kp[ks], sb, X);
+            Y = mfma16x16x32(qp[ks], sb, Y);
+        }
+        half4 rh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rh[i] = (_Float16)(bb[i] * (vv[i] - X[i]));
+        *reinterpret_cast<half4*>(&R_lds[lr][16 * w + 4 * lg]) = rh;
+        __syncthreads();
+
+        // D = T R (rows of this wave's token block)
+        floatx4 Dacc = {0.f, 0.f, 0.f, 0.f};
+        const int nkb = w >= 2 ? 2 : 1;
+        for (int kb = 0; kb < nkb; ++kb) {
+            const half8 rb = *reinterpret_cast<const half8*>(&R_lds[lr][32 * kb + 8 * lg]);
+            Dacc = mfma16x16x32(tt[kb], rb, Dacc);
+        }
+        half4 dh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dh[i] = (_Float16)Dacc[i];
+        *reinterpret_cast<half4*>(&D_lds[lr][16 * w + 4 * lg]) = dh;
+        __syncthreads();
+
+        // O = Q+ S0 + M D
+        half8 db[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) db[kb] = *reinterpret_cast<const half8*>(&D_lds[lr][32 * kb + 8 * lg]);
+        floatx4 O = Y;
+        for (int kb = 0; kb < nkb; ++kb) O = mfma16x16x32(mm[kb], db[kb], O);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 16 * w + 4 * lg + i;
+            if (rr < Lc) a.o[((t0 + rr) * H + h) * (int64_t)DV + vb * BV + lr] = O[i];
+        }
+
+        // S1 = Diag(gamma) S0 + K'^T D for this wave's 32 channels
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            floatx4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = gam[t][i] * Sf[t][i];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) acc = mfma16x16x32(kd[t][kb], db[kb], acc);
+            Sf[t] = acc;
+            half4 hv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = (_Float16)acc[i];
+            *reinterpret_cast<half4*>(&S_lds[lr][16 * (2 * w + t) + 4 * lg]) = hv;
+        }
+        __syncthreads();
+    }
+
+    if (a.sT) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ch = 16 * (2 * w + t) + 4 * lg + i;
+                a.sT[sbase + (int64_t)ch * DV + lr] = Sf[t][i];
+            }
+    }
+}
+
+SeqMap make_map(const PrefillArgs& a) {
+    SeqMap sm;
+    sm.cu = a.cu;
+    sm.T_fixed = a.T_fixed;
+    sm.nck_fixed = a.cu ? 0 : (a.T_fixed + C - 1) / C;
+    sm.N = a.N;
+    return sm;
+}
+
+int64_t num_slots(int64_t N, int64_t T_fixed, int64_t T_total, bool fixed) {
+    return fixed ? N * ((T_fixed + C - 1) / C) : T_total / C + N + 1;
+}
+
+}  // namespace
+
+bool chunk_mfma_supported(int bf16, int dk, int dv, int chunk) {
+    return bf16 && dk == DK && dv == DV && chunk == C;
+}
+
+size_t chunk_mfma_workspace(int64_t N, int64_t T_fixed, int64_t T_total, bool fixed, int H, int chunk) {
+    (void)chunk;
+    return (size_t)num_slots(N, T_fixed, T_total, fixed) * (size_t)H * (size_t)kRecord;
+}
+
+hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
+    if (a.N * a.H == 0) return hipSuccess;
+    const SeqMap sm = make_map(a);
+    const int64_t slots = num_slots(a.N, a.T_fixed, a.T_total, a.cu == nullptr);
+    if (slots > 0 && a.T_total > 0) {
+        hipLaunchKernelGGL(prep_kernel, dim3((unsigned)slots, (unsigned)a.H), dim3(256), 0, s, a, sm);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(a.N * a.H * NVB)), dim3(256), 0, s, a, sm);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI layer (kda_api.cpp) and the kernel
+// translation units.  Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Sequences of a prefill/append call.  Either `cu` (device int32 [N+1]) is set,
+// or every sequence has `T_fixed` tokens and sequence n starts at n * T_fixed.
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    const float* s0;  // [N, H, dk, dv] or nullptr
+    float* o;         // [T_total, H, dv]
+    float* sT;        // [N, H, dk, dv] or nullptr
+    const int32_t* cu;
+    int64_t N;
+    int64_t T_fixed;
+    int64_t T_total;
+    int H, dk, dv, chunk;
+    int bf16;  // storage type of q, k, v, beta
+    void* ws;
+    size_t ws_bytes;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    const float* s_in;
+    float* s_out;
+    float* o;
+    int64_t N;
+    int H, dk, dv;
+    int bf16;
+};
+
+// generic fp32-arithmetic chunked kernel (any supported shape, either storage type)
+bool chunk_f32_supported(int dk, int dv, int chunk);
+hipError_t launch_chunk_f32(const PrefillArgs& a, hipStream_t s);
+
+// matrix-core chunked path (bfloat16 storage, dk = dv = 128, chunk = 64)
+bool chunk_mfma_supported(int bf16, int dk, int dv, int chunk);
+size_t chunk_mfma_workspace(int64_t N, int64_t T_fixed, int64_t T_total, bool fixed, int H, int chunk);
+hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s);
+
+// decode step
+bool decode_supported(int dk, int dv);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace kda

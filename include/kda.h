@@ -1,0 +1,141 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * What is computed ("Kimi K3, explained", vibeengines.com/paper/kimi-k3,
+ * sections "How Kimi Delta Attention works, step by step" and "The math",
+ * gated delta rule equation; the page writes the state as d_v x d_k, this
+ * library stores its transpose):
+ *
+ *   per sequence and head, state S in R^{d_k x d_v} (row = key channel,
+ *   column = value channel), alpha_t = exp(g_t) per key channel:
+ *       S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *       o_t = S_t^T q_t                      (read after the write)
+ *
+ * Prefill and append-prefill evaluate this recurrence in chunks of `chunk`
+ * tokens ("Training in chunks": inside a chunk the product of decay-and-erase
+ * transitions becomes dense products plus one triangular solve; only S
+ * crosses chunk boundaries).  Decode applies one token per sequence at a cost
+ * independent of the context length ("The decode wall"; "KDA: trade the cache
+ * for a fixed-size state").
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors are
+ *     contiguous and row-major.  Alignment: for prefill and append, q, k and g
+ *     16 bytes and the workspace 256 bytes; for decode, both states 16 bytes;
+ *     every other pointer its element size.
+ *   - q, k, v and beta have the storage type `dtype` (KDA_F32: float,
+ *     KDA_BF16: bfloat16).  g = log(alpha) is always float (fp32, values <= 0
+ *     expected, not checked), states and outputs are always float.
+ *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream).  The library never synchronises (unless KDA_DEBUG_SYNC=1 is set
+ *     in the environment), never allocates or frees device memory, and keeps
+ *     no pointer after returning.  The caller keeps every buffer alive until
+ *     the stream has drained.
+ *   - Return value: KDA_OK or a negative kda_status.  Arguments are validated
+ *     on the host before any device work; a failed call launches nothing.
+ *     Device-resident data (cu_seqlens contents, gate ranges, NaN/Inf) is not
+ *     inspected.  kda_last_error() gives a message for the calling thread.
+ *   - bfloat16 path numerics: products inside a chunk use fp16 matrix-core
+ *     operands with fp32 accumulation; the state, the decays and all outputs are
+ *     fp32.  Values of v, of the state and of the intermediate corrections must
+ *     stay within fp16 range (|x| < 6e4); within every 8-token window the
+ *     per-channel decay must satisfy sum(-g) <= 10 (alpha >= ~0.29 on average).
+ *     The fp32 path has no such limits.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad cu_seqlens count, ... */
+    KDA_ERR_UNSUPPORTED = -2, /* (dtype, d_k, d_v, chunk) combination not implemented */
+    KDA_ERR_MISALIGNED = -3,  /* a pointer is not aligned as required (see Conventions) */
+    KDA_ERR_ALIAS = -4,       /* outputs overlap inputs, or state_out partially overlaps state_in */
+    KDA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than kda_workspace_size() */
+    KDA_ERR_HIP = -6          /* the HIP runtime reported an error (message in kda_last_error) */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum { KDA_OP_PREFILL = 0, KDA_OP_APPEND = 1, KDA_OP_DECODE = 2 } kda_op;
+
+/*
+ * Chunked prefill of B equal-length sequences of T tokens.
+ *   q, k       [B, T, H, d_k]   dtype
+ *   v          [B, T, H, d_v]   dtype
+ *   g          [B, T, H, d_k]   float, log of the per-channel forget gate alpha
+ *   beta       [B, T, H]        dtype, write strength
+ *   state_in   [B, H, d_k, d_v] float, or NULL for a zero initial state
+ *   out        [B, T, H, d_v]   float
+ *   state_out  [B, H, d_k, d_v] float, or NULL; may equal state_in (in place),
+ *              must not partially overlap it
+ *   chunk      tokens per chunk: 16, 32 or 64 (64 for the bfloat16 d=128 path)
+ *   workspace  device scratch of at least kda_workspace_size(KDA_OP_PREFILL, B, T, ...)
+ *              bytes (NULL allowed when that size is 0); contents need no
+ *              initialisation and are clobbered.
+ * T = 0 copies state_in to state_out (zeros when state_in is NULL).
+ */
+int kda_prefill_chunked(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                        const float* state_in, float* out, float* state_out, int64_t B, int64_t T,
+                        int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                        void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Append-prefill of N packed variable-length segments, each continuing from
+ * its own carried state (the append-prefill workload: a long new segment on
+ * top of a kept history).
+ *   q, k, g    [T_total, H, d_k]; v [T_total, H, d_v]; beta [T_total, H]
+ *   cu_seqlens DEVICE int32 [N + 1]: cu[0] = 0, non-decreasing, cu[N] = T_total
+ *              (segment n is tokens cu[n] .. cu[n+1]-1; not checked on device)
+ *   state_in   [N, H, d_k, d_v] float or NULL (zeros); state_out as in prefill
+ *   out        [T_total, H, d_v] float
+ * Empty segments pass their state through unchanged.
+ */
+int kda_append_prefill(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                       const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in,
+                       float* out, float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                       int32_t chunk, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * One decode step: one new token for each of N sequences.
+ *   q, k, g    [N, H, d_k]; v [N, H, d_v]; beta [N, H]
+ *   state_in   [N, H, d_k, d_v] float (required)
+ *   state_out  [N, H, d_k, d_v] float (required); may equal state_in for an
+ *              in-place update, must not partially overlap it
+ *   out        [N, H, d_v] float
+ * Each state element is read once and written once.
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                    const float* state_in, float* state_out, float* out, int32_t N, int32_t H,
+                    int32_t d_k, int32_t d_v, int32_t dtype, void* hip_stream);
+
+/* Workspace bytes an op needs (B_or_N sequences, T tokens per sequence for
+ * KDA_OP_PREFILL or T_total for KDA_OP_APPEND).  0 for KDA_OP_DECODE.
+ * Returns (size_t)-1 for an unsupported or invalid combination. */
+size_t kda_workspace_size(int32_t op, int64_t B_or_N, int64_t T, int32_t H, int32_t d_k, int32_t d_v,
+                          int32_t dtype, int32_t chunk);
+
+/* 1 if (op, dtype, d_k, d_v, chunk) is implemented, else 0. */
+int kda_is_supported(int32_t op, int32_t dtype, int32_t d_k, int32_t d_v, int32_t chunk);
+
+/* Static description of a kda_status value. */
+const char* kda_status_string(int status);
+
+/* Message describing the last failed call on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Library version string. */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,92 @@
+"""C-ABI contract on the host: the library loads and exports every symbol include/kda.h declares;
+argument validation rejects bad calls before any device work (no GPU needed: every call here
+fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from gated_delta_rule_75_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("HIP library not built")
+    return _lib, _lib.load()
+
+
+def test_exports_match_header():
+    _l, L = _lib()
+    header = open(os.path.join(ROOT, "include", "kda.h")).read()
+    declared = set(re.findall(r"\b(kda_[a-z_]+)\s*\(", header))
+    assert declared == set(_l.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    _l, L = _lib()
+    assert L.kda_version().decode().startswith("kda-mi355x")
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert L.kda_status_string(s)
+    assert L.kda_status_string(-99) == b"unknown status"
+
+
+def test_supported_and_workspace():
+    _l, L = _lib()
+    assert L.kda_is_supported(0, 1, 128, 128, 64) == 1
+    assert L.kda_is_supported(0, 0, 16, 16, 16) == 1
+    assert L.kda_is_supported(0, 1, 96, 128, 64) == 0
+    assert L.kda_is_supported(2, 1, 128, 128, 0) == 1
+    assert L.kda_workspace_size(2, 4, 0, 32, 128, 128, 1, 64) == 0
+    ws = L.kda_workspace_size(0, 1, 8192, 32, 128, 128, 1, 64)
+    assert ws == 128 * 32 * 66048
+    assert L.kda_workspace_size(0, 1, 8192, 32, 96, 128, 1, 64) == 2 ** 64 - 1
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def test_validation_errors_launch_nothing():
+    _l, L = _lib()
+    P = FAKE
+    # unsupported head size
+    rc = L.kda_prefill_chunked(P, P, P, P, P, None, P, None, 1, 64, 2, 96, 128, 1, 64, None, 0, None)
+    assert rc == _l.KDA_ERR_UNSUPPORTED and b"d_k=96" in L.kda_last_error()
+    # negative sizes / bad dtype
+    assert L.kda_prefill_chunked(P, P, P, P, P, None, P, None, -1, 64, 2, 16, 16, 0, 16, None, 0, None) == -1
+    assert L.kda_prefill_chunked(P, P, P, P, P, None, P, None, 1, 64, 2, 16, 16, 7, 16, None, 0, None) == -1
+    # missing inputs
+    assert L.kda_prefill_chunked(None, P, P, P, P, None, P, None, 1, 64, 2, 16, 16, 0, 16, None, 0, None) == -1
+    # misaligned (q must be 16-byte aligned for prefill; decode states too)
+    assert L.kda_prefill_chunked(P + 4, P, P, P, P, None, P, None, 1, 64, 2, 16, 16, 0, 16, None, 0, None) == -3
+    assert L.kda_decode_step(P, P, P, P, P, 1 << 41, (1 << 41) + 4, 1 << 42, 1, 1, 16, 16, 0, None) == -3
+    # workspace too small for the matrix-core path
+    big = 1 << 40
+    rc = L.kda_prefill_chunked(P, P, P, P, P, None, big, None, 1, 64, 2, 128, 128, 1, 64, None, 0, None)
+    assert rc == _l.KDA_ERR_WORKSPACE
+    # output overlapping an input
+    rc = L.kda_prefill_chunked(P, P, P, P, P, None, P, None, 1, 64, 2, 16, 16, 0, 16, None, 0, None)
+    assert rc == _l.KDA_ERR_ALIAS
+    # state_out partially overlapping state_in (decode)
+    S = 1 << 41
+    rc = L.kda_decode_step(P, P + 4096, P + 8192, P + 12288, P + 16384, S, S + 16, 1 << 42, 1, 1, 16, 16, 0, None)
+    assert rc == _l.KDA_ERR_ALIAS
+    # decode without a state
+    assert L.kda_decode_step(P, P, P, P, P, None, None, P, 1, 1, 16, 16, 0, None) == -1
+    # append without cu_seqlens
+    assert L.kda_append_prefill(P, P, P, P, P, None, 1, 10, None, P, None, 2, 16, 16, 0, 16, None, 0, None) == -1
+
+
+def test_injected_launch_failure_reports_hip_error(monkeypatch):
+    _l, L = _lib()
+    monkeypatch.setenv("KDA_TEST_FAIL_LAUNCH", "1")
+    # valid, non-overlapping fake buffers: validation passes, then the injected failure returns
+    # before anything touches the device
+    base = 1 << 40
+    ptrs = [base + i * (1 << 30) for i in range(8)]
+    rc = L.kda_decode_step(*ptrs[:5], ptrs[5], ptrs[5], ptrs[6], 1, 1, 16, 16, 0, None)
+    assert rc == _l.KDA_ERR_HIP and b"injected" in L.kda_last_error()

@@ -1,0 +1,195 @@
+"""GPU parity of the HIP path against the fp64 oracle (small and medium sizes, edge cases).
+
+Tolerance (per sequence-head slice, max|gpu - oracle| / max|oracle|): 2e-3 for bfloat16
+storage (fp16 matrix-core operands, fp32 state), 1e-5 for fp32 storage (fp32 arithmetic).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_75_amd as kda
+import oracle
+import synth
+from _gpu import dev, host, make_inputs, upload
+from _util import assert_close
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+def _w(dtype="bf16", H=4, d=128, chunk=64, seed=1, s0_std=0.0, gate=None):
+    w = synth.Workload("t", seed, H=H, dk=d, dv=d, dtype=dtype, chunk=chunk, s0_std=s0_std)
+    if gate is not None:
+        w.gate = gate
+    return w
+
+
+def _run_prefill(w, B, T, with_state):
+    st, wide = make_inputs(w, B * T)
+    s0 = synth.gen_state(w, B) if with_state else None
+    q, k, v, g, b = upload(w, st, (B, T))
+    S0 = dev(s0, "f32") if s0 is not None else None
+    o, sT = kda.prefill_chunked(q, k, v, g, b, S0, chunk=w.chunk)
+    torch.cuda.synchronize()
+    cu = np.arange(B + 1) * T
+    oref, sref = oracle.recurrence(*wide, cu, s0)
+    return host(o).reshape(B * T, w.H, w.dv), host(sT), oref, sref, cu
+
+
+@pytest.mark.parametrize("dtype,d,chunk,B,T,with_state", [
+    ("f32", 16, 16, 1, 64, False),      # the tiny fp32 workload's shape
+    ("f32", 16, 16, 2, 37, True),
+    ("f32", 32, 32, 1, 100, True),
+    ("f32", 64, 16, 1, 70, False),
+    ("f32", 128, 32, 1, 70, True),
+    ("bf16", 64, 32, 2, 50, True),      # bf16 storage through the fp32 kernel
+    ("bf16", 128, 64, 1, 64, False),    # one full chunk
+    ("bf16", 128, 64, 1, 1000, False),  # several chunks + ragged tail
+    ("bf16", 128, 64, 2, 333, True),
+    ("bf16", 128, 64, 1, 1, True),      # a single token
+    ("bf16", 128, 64, 1, 0, True),      # empty: state passes through
+])
+def test_prefill_matches_oracle(dtype, d, chunk, B, T, with_state):
+    print(f"prefill dtype={dtype} d={d} chunk={chunk} B={B} T={T} state={with_state}", flush=True)
+    w = _w(dtype, H=3, d=d, chunk=chunk, seed=11 + T, s0_std=0.02 if with_state else 0.0)
+    o, s, oref, sref, cu = _run_prefill(w, B, T, with_state)
+    if T > 0:
+        assert_close(o, oref, TOL[dtype], cu, "o")
+    assert_close(s, sref, TOL[dtype], None, "S_T")
+
+
+def test_tiny_workload_exact_shape():
+    """The tiny fp32 workload: B=1, H=2, T=64, d=16, chunk 16, zero initial state."""
+    w = synth.workload("tiny")
+    o, s, oref, sref, cu = _run_prefill(w, 1, w.T, False)
+    assert_close(o, oref, 1e-5, cu, "o")
+    assert_close(s, sref, 1e-5, None, "S_T")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("f32", 16), ("bf16", 64), ("f32", 32)])
+def test_decode_steps_match_oracle(dtype, d):
+    print(f"decode dtype={dtype} d={d}", flush=True)
+    w = _w(dtype, H=4, d=d, seed=5, s0_std=0.02)
+    w.q_unit = False
+    N, steps = 6, 5
+    s0 = synth.gen_state(w, N)
+    S = dev(s0, "f32")
+    sref = s0.astype(np.float64)
+    for t in range(steps):
+        st, wide = make_inputs(w, N, offset_tokens=t * N)
+        q, k, v, g, b = upload(w, st)
+        o = kda.decode_step(q, k, v, g, b, S)  # in place
+        torch.cuda.synchronize()
+        oref, sref = oracle.decode_step(*wide, sref)
+        assert_close(host(o), oref, 1e-5, np.arange(N + 1), f"o step {t}")
+    assert_close(host(S), sref, 1e-5, None, "state")
+
+
+def test_decode_out_of_place_equals_in_place():
+    w = _w("bf16", H=2, seed=6, s0_std=0.02)
+    N = 3
+    s0 = synth.gen_state(w, N)
+    st, _ = make_inputs(w, N)
+    q, k, v, g, b = upload(w, st)
+    A = dev(s0, "f32")
+    B = dev(s0, "f32")
+    Bout = torch.empty_like(B)
+    o1 = kda.decode_step(q, k, v, g, b, A)
+    o2 = kda.decode_step(q, k, v, g, b, B, state_out=Bout)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(A, Bout)
+    assert torch.equal(B, dev(s0, "f32"))  # input untouched
+
+
+def test_append_varlen_matches_oracle_and_boundaries():
+    """Packed segments with empty, one-token, exact-chunk and ragged lengths; distinct carried
+    states; canary bytes around the outputs stay untouched."""
+    w = _w("bf16", H=3, seed=21, s0_std=0.02)
+    lengths = [0, 1, 63, 64, 65, 300, 0, 130]
+    cu = synth.cu_seqlens(lengths)
+    T, N = int(cu[-1]), len(lengths)
+    st, wide = make_inputs(w, T)
+    s0 = synth.gen_state(w, N)
+    q, k, v, g, b = upload(w, st)
+    S0 = dev(s0, "f32")
+    canary = 12345.0
+    obuf = torch.full((T + 2, w.H, w.dv), canary, device="cuda")
+    sbuf = torch.full((N + 2, w.H, w.dk, w.dv), canary, device="cuda")
+    o, sT = kda.append_prefill(q, k, v, g, b, torch.from_numpy(cu).cuda(), S0,
+                               out=obuf[1:T + 1], state_out=sbuf[1:N + 1])
+    torch.cuda.synchronize()
+    assert torch.all(obuf[0] == canary) and torch.all(obuf[T + 1] == canary)
+    assert torch.all(sbuf[0] == canary) and torch.all(sbuf[N + 1] == canary)
+    oref, sref = oracle.recurrence(*wide, cu, s0)
+    assert_close(host(o), oref, 2e-3, cu, "o")
+    assert_close(host(sT), sref, 2e-3, None, "S_T")
+    # empty segments pass their state through bit for bit
+    for n in (0, 6):
+        assert torch.equal(sT[n], S0[n])
+
+
+def test_append_isolation_and_determinism():
+    """NaN-poisoning one segment leaves every other segment's outputs and states bitwise unchanged;
+    two identical calls give identical bits."""
+    w = _w("bf16", H=2, seed=31, s0_std=0.02)
+    lengths = [70, 129, 5]
+    cu = synth.cu_seqlens(lengths)
+    T, N = int(cu[-1]), len(lengths)
+    st, _ = make_inputs(w, T)
+    s0 = synth.gen_state(w, N)
+    q, k, v, g, b = upload(w, st)
+    cu_d = torch.from_numpy(cu).cuda()
+    S0 = dev(s0, "f32")
+    o1, s1 = kda.append_prefill(q, k, v, g, b, cu_d, S0)
+    o2, s2 = kda.append_prefill(q, k, v, g, b, cu_d, S0)
+    v2 = v.clone()
+    v2[cu[1]:cu[2]] = float("nan")
+    o3, s3 = kda.append_prefill(q, k, v2, g, b, cu_d, S0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.isnan(o3[cu[1]:cu[2]]).any()
+    for n in (0, 2):
+        assert torch.equal(o3[cu[n]:cu[n + 1]], o1[cu[n]:cu[n + 1]])
+        assert torch.equal(s3[n], s1[n])
+
+
+def test_prefill_equals_append_and_decode_composition():
+    """prefill(T1+T2) = append(T2) on the state after prefill(T1), and prefill of T tokens =
+    T decode steps, within the bf16-path tolerance."""
+    w = _w("bf16", H=2, seed=41)
+    T1, T2 = 200, 77
+    st, wide = make_inputs(w, T1 + T2)
+    q, k, v, g, b = upload(w, st, (1, T1 + T2))
+    o, s = kda.prefill_chunked(q, k, v, g, b)
+    o1, s1 = kda.prefill_chunked(q[:, :T1].contiguous(), k[:, :T1].contiguous(), v[:, :T1].contiguous(),
+                                 g[:, :T1].contiguous(), b[:, :T1].contiguous())
+    cu = torch.tensor([0, T2], dtype=torch.int32, device="cuda")
+    o2, s2 = kda.append_prefill(q[0, T1:].contiguous(), k[0, T1:].contiguous(), v[0, T1:].contiguous(),
+                                g[0, T1:].contiguous(), b[0, T1:].contiguous(), cu, s1)
+    torch.cuda.synchronize()
+    whole = host(o)[0]
+    split = np.concatenate([host(o1)[0], host(o2)])
+    assert_close(split, whole, 2e-3, None, "append composition o")
+    assert_close(host(s2), host(s), 2e-3, None, "append composition S")
+    # decode stepping from zero state over the first 40 tokens
+    S = torch.zeros((1, w.H, w.dk, w.dv), device="cuda")
+    outs = []
+    for t in range(40):
+        outs.append(kda.decode_step(q[:, t], k[:, t], v[:, t], g[:, t], b[:, t], S))
+    torch.cuda.synchronize()
+    dec = np.stack([host(x)[0] for x in outs])
+    assert_close(dec, host(o)[0, :40], 2e-3, None, "prefill vs decode")
+
+
+def test_strong_decay_is_flagged_not_wrong():
+    """Per-channel decays beyond the fp16 range of the matrix-core path (8-token decay > e^10)
+    must not produce silently wrong numbers: outputs of such chunks are NaN."""
+    w = _w("bf16", H=1, seed=51)
+    T = 64
+    st, _ = make_inputs(w, T)
+    q, k, v, g, b = upload(w, st, (1, T))
+    g = torch.full_like(g, -3.0)
+    o, s = kda.prefill_chunked(q, k, v, g, b)
+    torch.cuda.synchronize()
+    assert torch.isnan(s).all()
