@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""KDA benchmark on one MI355X.
+
+Headline: chunked-prefill tokens/s at T = 65,536 tokens, H = 32 heads, d_k = d_v = 128,
+bfloat16 q/k/v/beta, fp32 log-decay, fp32 state and outputs, chunk 64 (one step = one full
+prefill of that batch: decay factors, gated Gram matrices, UT transform, WY factors, the
+sequential state pass and the epilogue).  In the same run: the batched decode step at
+256 sequences x 32 heads (1000 consecutive in-place steps), reported as steps/s and HBM GB/s.
+
+Timing: W untimed warmup steps, then exactly K steps bracketed by torch.cuda.synchronize();
+per-kernel durations come from HIP events the library records around each of its kernel
+launches on the call's stream (kda_timing_begin/kda_timing_end).  Inputs are resident in HBM
+before timing starts.  Every timed run is parity-checked against the fp64 oracle on a sample.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix-core peak
+# algorithmic bytes per unit (bf16 q/k/v/beta, fp32 g, fp32 o, fp32 state)
+PREFILL_BYTES_PER_TOKEN_HEAD = 256 + 256 + 256 + 512 + 2 + 512          # 1794
+PREP_BYTES_PER_TOKEN_HEAD = 256 + 256 + 512 + 2                         # q, k, g, beta read by the prep kernel
+STATE_BYTES_PER_TOKEN_HEAD = 256 + 2 + 512                              # v, beta read, o written by the state pass
+PREFILL_FLOP_PER_TOKEN_HEAD = 139264                                    # chunked form, d=128, C=64
+DECODE_BYTES_PER_SEQ_HEAD = 65536 + 65536 + 768 + 512 + 2 + 512         # 132866
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed prefill steps")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--T", type=int, default=65536, help="prefill tokens")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--decode-warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-prefill", action="store_true")
+    return ap.parse_args()
+
+
+def upload(x, dtype, device):
+    import numpy as np
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def slice_err(x, y):
+    """max over heads of max|x-y| / max|y| over the head's slice; x, y [T, H, dv]."""
+    import numpy as np
+
+    d = np.abs(x - y).max(axis=(0, 2))
+    m = np.abs(y).max(axis=(0, 2))
+    return float((d / np.where(m > 0, m, 1)).max())
+
+
+def bench_prefill(args, res):
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_75_amd as kda
+    import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.workload("metric")
+    T, H, dk, dv = args.T, w.H, w.dk, w.dv
+    log(f"[prefill] generating T={T} H={H} d={dk} bf16 inputs")
+    q, k, v, g, b = synth.gen_tokens(w, T)
+    tq, tk, tv, tb = (upload(x, "bf16", dev).reshape(1, T, *x.shape[1:]) for x in (q, k, v, b))
+    tg = upload(g, "f32", dev).reshape(1, T, H, dk)
+    out = torch.empty((1, T, H, dv), dtype=torch.float32, device=dev)
+    sT = torch.empty((1, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(0, 1, T, H, dk, dv, torch.bfloat16, 64), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.prefill_chunked(tq, tk, tv, tg, tb, None, out=out, state_out=sT, workspace=ws)
+
+    log(f"[prefill] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[prefill] timing {args.steps} steps")
+    with kda.kernel_timing() as kt:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    elapsed = t1 - t0
+    per = {}
+    for name, ms in kt.records:
+        per.setdefault(name, []).append(ms)
+    avg = {n: sum(x) / len(x) for n, x in per.items()}
+    th = T * H
+    path_ms = sum(avg.values())
+    achieved = PREFILL_BYTES_PER_TOKEN_HEAD * th / (path_ms * 1e-3) / 1e9
+    kernels = []
+    for name, alg in (("kda_prep", PREP_BYTES_PER_TOKEN_HEAD), ("kda_state", STATE_BYTES_PER_TOKEN_HEAD)):
+        if name in avg:
+            kernels.append({"kernel": name, "launches": len(per[name]), "avg_ms": round(avg[name], 4),
+                            "algorithmic_bytes": alg * th,
+                            "achieved_GBps": round(alg * th / (avg[name] * 1e-3) / 1e9, 1)})
+    tflops = PREFILL_FLOP_PER_TOKEN_HEAD * th / (path_ms * 1e-3) / 1e12
+    res["value"] = T * args.steps / elapsed
+    res["ms_per_step"] = elapsed * 1e3 / args.steps
+    res["roofline"] = {
+        "bound": "hbm", "kernel": "kda_prep+kda_state (one prefill pass)",
+        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+        "algorithmic_bytes_per_launch": PREFILL_BYTES_PER_TOKEN_HEAD * th,
+        "avg_pass_ms": round(path_ms, 4),
+        "mfma_algorithmic_tflops": round(tflops, 1),
+        "mfma_frac_of_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+    }
+    res["kernels"] = kernels
+    log(f"[prefill] {res['value'] / 1e6:.2f} M tokens/s, {res['ms_per_step']:.3f} ms/step, kernels {avg}")
+
+    # parity of the timed output on a token sample (all heads) + CPU baseline from the same oracle run
+    wide_all = (q, k, v, g, b)
+    return out, sT, wide_all
+
+
+def oracle_sample(args, res, out, wide_all):
+    import numpy as np
+
+    import oracle
+    import synth
+
+    q, k, v, g, b = wide_all
+    H = q.shape[1]
+    threads = oracle.default_threads()
+
+    def run(Ts):
+        sl = slice(0, Ts)
+        ins = [synth.to_f64(q[sl], "bf16"), synth.to_f64(k[sl], "bf16"), synth.to_f64(v[sl], "bf16"),
+               g[sl].astype(np.float64), synth.to_f64(b[sl], "bf16")]
+        t0 = time.perf_counter()
+        o, s = oracle.recurrence(*ins, threads=threads)
+        return o, time.perf_counter() - t0
+
+    _, tc = run(256)
+    rate = 256 / max(tc, 1e-6)
+    Ts = int(min(q.shape[0], max(512, rate * args.cpu_seconds)))
+    Ts = max(64, Ts - Ts % 64)
+    log(f"[oracle] calibration {rate:.0f} tokens/s on {threads} threads; sample {Ts} tokens x {H} heads")
+    o_ref, t = run(Ts)
+    o_gpu = out[0, :Ts].detach().cpu().numpy().astype(np.float64)
+    err = slice_err(o_gpu, o_ref)
+    res["cpu_baseline"] = {"value": round(Ts / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                           "sample": f"first {Ts} tokens x {H} heads of the T={q.shape[0]} prefill workload "
+                                     f"(fp64 token recurrence, {t:.1f} s)"}
+    res["parity"] = {"prefill_tokens_checked": Ts, "heads": H, "max_slice_rel_err": err, "tol": 2e-3,
+                     "ok": bool(err <= 2e-3)}
+    log(f"[oracle] {Ts / t:.1f} tokens/s; parity max err {err:.2e}")
+
+
+def bench_decode(args, res):
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_75_amd as kda
+    import oracle
+    import synth
+    from gated_delta_rule_75_amd import _lib
+
+    dev = torch.device("cuda:0")
+    w = synth.workload("decode")
+    N, H, dk, dv, steps = w.decode_N, w.H, w.dk, w.dv, args.decode_steps
+    total = args.decode_warmup + steps
+    log(f"[decode] generating N={N} H={H} d={dk}, {total} steps of inputs + state")
+    q, k, v, g, b = synth.gen_tokens(w, total * N)
+    s0 = synth.gen_state(w, N)
+    tq, tk, tv, tb = (upload(x, "bf16", dev).reshape(total, N, *x.shape[1:]) for x in (q, k, v, b))
+    tg = upload(g, "f32", dev).reshape(total, N, H, dk)
+    S = upload(s0, "f32", dev)
+    out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    L = _lib.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args_list = [(tq[i].data_ptr(), tk[i].data_ptr(), tv[i].data_ptr(), tg[i].data_ptr(), tb[i].data_ptr())
+                 for i in range(total)]
+    sp, op = S.data_ptr(), out.data_ptr()
+
+    def step(i):
+        rc = L.kda_decode_step(*args_list[i], sp, sp, op, N, H, dk, dv, _lib.KDA_BF16, stream)
+        if rc:
+            _lib.check(rc)
+
+    for i in range(args.decode_warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[decode] timing {steps} steps")
+    with kda.kernel_timing() as kt:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.decode_warmup, total):
+            step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms = [m for n, m in kt.records if n == "kda_decode"]
+    avg = sum(ms) / len(ms)
+    bytes_step = DECODE_BYTES_PER_SEQ_HEAD * N * H
+    gbps_wall = steps * bytes_step / elapsed / 1e9
+    gbps_kernel = bytes_step / (avg * 1e-3) / 1e9
+    res["decode"] = {"workload": f"decode step, {N} sequences x {H} heads, d={dk}, in-place fp32 state",
+                     "steps": steps, "steps_per_s": round(steps / elapsed, 1),
+                     "ms_per_step": round(elapsed * 1e3 / steps, 4), "hbm_GBps": round(gbps_wall, 1),
+                     "kernel_avg_ms": round(avg, 4)}
+    res["roofline_decode"] = {"bound": "hbm", "kernel": "kda_decode", "achieved": round(gbps_kernel, 1),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps_kernel / HBM_PEAK_GBPS, 4),
+                              "traffic": None, "algorithmic_bytes_per_launch": bytes_step}
+    log(f"[decode] {steps / elapsed:.1f} steps/s, {gbps_wall:.1f} GB/s wall, kernel avg {avg * 1e3:.1f} us "
+        f"({gbps_kernel:.1f} GB/s)")
+
+    if args.no_cpu_baseline:
+        return
+    # CPU-baseline leg: the oracle steps sampled (sequence, head) pairs through every step
+    # (warmup included); its results also check the timed run
+    pairs = [(0, 0), (17, 5), (128, 31), (255, 12)]
+    t_or = 0.0
+    Sg = S.detach().cpu().numpy()
+    og = out.detach().cpu().numpy()
+    worst = 0.0
+    for n, h in pairs:
+        sl = lambda x: x.reshape(total, N, H, -1)[:, n, h, :]  # noqa: E731
+        qi = synth.to_f64(sl(q), "bf16")[:, None, :]
+        ki = synth.to_f64(sl(k), "bf16")[:, None, :]
+        vi = synth.to_f64(sl(v), "bf16")[:, None, :]
+        gi = sl(g).astype(np.float64)[:, None, :]
+        bi = synth.to_f64(b.reshape(total, N, H)[:, n, h], "bf16")[:, None]
+        t0 = time.perf_counter()
+        o_ref, s_ref = oracle.recurrence(qi, ki, vi, gi, bi, None, s0[n, h][None, None].astype(np.float64))
+        t_or += time.perf_counter() - t0
+        es = np.abs(Sg[n, h] - s_ref[0, 0]).max() / np.abs(s_ref[0, 0]).max()
+        eo = np.abs(og[n, h] - o_ref[-1, 0]).max() / np.abs(o_ref[-1, 0]).max()
+        worst = max(worst, es, eo)
+    res["parity"] = dict(res.get("parity", {}), decode_pairs_checked=len(pairs), decode_steps_checked=total,
+                         decode_max_rel_err=float(worst), decode_ok=bool(worst <= 2e-3))
+    # one (sequence, head) step is 1/(N*H) of a batch step
+    res.setdefault("cpu_baseline", {})["decode"] = {
+        "value": round(len(pairs) * total / t_or / (N * H), 3), "unit": "steps/s (batch 256 x 32 heads)",
+        "sample": f"{len(pairs)} (sequence, head) pairs x {total} steps, single-threaded fp64 recurrence",
+        "cores": 1}
+    log(f"[decode] parity max err {worst:.2e}")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    res = {
+        "metric": "KDA prefill tokens/s (d=128, T=64K) + decode steps/s & HBM GB/s at batch 256",
+        "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16-mfma/f32", "storage_dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; shapes and distributions of the workloads)",
+        "config": {"workload": f"KDA chunked prefill B=1 T={args.T} H=32 d_k=d_v=128 chunk=64, bf16 q/k/v/beta, "
+                               "fp32 log-decay/state/output; plus decode 256 seq x 32 heads x 1000 steps",
+                   "global_batch": 1, "seq_len": args.T, "heads": 32, "head_dim": 128, "chunk": 64},
+    }
+    out = None
+    if not args.skip_prefill:
+        out, sT, wide_all = bench_prefill(args, res)
+        if not args.no_cpu_baseline:
+            oracle_sample(args, res, out, wide_all)
+        del out, sT, wide_all
+        torch.cuda.empty_cache()
+    if not args.skip_decode:
+        bench_decode(args, res)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

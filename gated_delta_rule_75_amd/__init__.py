@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import KdaError  # noqa: F401
 
 __all__ = ["prefill_chunked", "append_prefill", "decode_step", "workspace_size", "is_supported", "version",
-           "KdaError"]
+           "KdaError", "kernel_timing"]
 
 _DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
 
@@ -34,6 +34,33 @@ def workspace_size(op: int, n: int, t: int, h: int, dk: int, dv: int, dtype: tor
     if ws == 2 ** 64 - 1:
         raise KdaError(_lib.KDA_ERR_UNSUPPORTED, f"unsupported op={op} dtype={dtype} dk={dk} dv={dv} chunk={chunk}")
     return int(ws)
+
+
+class kernel_timing:
+    """Context manager: per-kernel HIP-event timings of every library kernel launched inside it
+    (on the calling thread).  After exit, ``records`` is a list of (kernel name, ms) in launch
+    order; exiting waits for the recorded events."""
+
+    MAX_RECORDS = 1 << 16
+
+    def __init__(self):
+        self.records = []
+
+    def __enter__(self):
+        _lib.check(_lib.load().kda_timing_begin())
+        return self
+
+    def __exit__(self, *exc):
+        import ctypes
+
+        ids = (ctypes.c_int32 * self.MAX_RECORDS)()
+        ms = (ctypes.c_float * self.MAX_RECORDS)()
+        n = _lib.load().kda_timing_end(ids, ms, self.MAX_RECORDS)
+        if n < 0:
+            _lib.check(n)
+        self.records = [(_lib.KERNEL_NAMES.get(ids[i], str(ids[i])), float(ms[i]))
+                        for i in range(min(n, self.MAX_RECORDS))]
+        return False
 
 
 def _ptr(t):

@@ -20,7 +20,9 @@ KDA_OP_PREFILL, KDA_OP_APPEND, KDA_OP_DECODE = 0, 1, 2
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_prefill_chunked", "kda_append_prefill", "kda_decode_step", "kda_workspace_size",
-           "kda_is_supported", "kda_status_string", "kda_last_error", "kda_version")
+           "kda_is_supported", "kda_status_string", "kda_last_error", "kda_version", "kda_timing_begin",
+           "kda_timing_end")
+KERNEL_NAMES = {1: "kda_prep", 2: "kda_state", 3: "kda_chunk_f32", 4: "kda_decode"}
 
 _LIB = None
 
@@ -56,6 +58,10 @@ def load():
     L.kda_last_error.argtypes = []
     L.kda_version.restype = ctypes.c_char_p
     L.kda_version.argtypes = []
+    L.kda_timing_begin.restype = ctypes.c_int
+    L.kda_timing_begin.argtypes = []
+    L.kda_timing_end.restype = ctypes.c_int
+    L.kda_timing_end.argtypes = [vp, vp, i32]
     _LIB = L
     return L
 

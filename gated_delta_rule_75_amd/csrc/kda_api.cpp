@@ -9,8 +9,54 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "kda_internal.h"
+
+// ---------------------------------------------------------------------------------------
+// per-kernel event timing (diagnostics), per calling thread
+// ---------------------------------------------------------------------------------------
+namespace {
+struct TimingState {
+    bool on = false;
+    bool failed = false;
+    struct Rec {
+        int id;
+        hipEvent_t start, stop;
+    };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;
+    size_t used = 0;
+
+    hipEvent_t take() {
+        if (used == pool.size()) {
+            hipEvent_t e = nullptr;
+            if (hipEventCreate(&e) != hipSuccess) {
+                failed = true;
+                return nullptr;
+            }
+            pool.push_back(e);
+        }
+        return pool[used++];
+    }
+};
+thread_local TimingState g_timing;
+}  // namespace
+
+namespace kda {
+bool timing_on() { return g_timing.on; }
+void timed_begin(int kernel_id, hipStream_t s) {
+    TimingState::Rec r{kernel_id, g_timing.take(), g_timing.take()};
+    if (!r.start || !r.stop || hipEventRecord(r.start, s) != hipSuccess) {
+        g_timing.failed = true;
+        return;
+    }
+    g_timing.recs.push_back(r);
+}
+void timed_end(hipStream_t s) {
+    if (g_timing.recs.empty() || hipEventRecord(g_timing.recs.back().stop, s) != hipSuccess) g_timing.failed = true;
+}
+}  // namespace kda
 
 namespace {
 
@@ -109,6 +155,35 @@ int validate_common(const void* q, const void* k, const void* v, const float* g,
 extern "C" {
 
 const char* kda_version(void) { return "kda-mi355x 0.1.0 (gfx950)"; }
+
+int kda_timing_begin(void) {
+    g_timing.on = true;
+    g_timing.failed = false;
+    g_timing.recs.clear();
+    g_timing.used = 0;
+    return ok();
+}
+
+int kda_timing_end(int32_t* kernel_ids, float* ms, int32_t max_records) {
+    g_timing.on = false;
+    if (g_timing.failed) return fail(KDA_ERR_HIP, "kda_timing_end: an event could not be created or recorded");
+    int32_t n = 0;
+    for (const auto& r : g_timing.recs) {
+        float t = 0.f;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+        if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_timing_end: %s", hipGetErrorString(e));
+        if (n < max_records) {
+            if (kernel_ids) kernel_ids[n] = r.id;
+            if (ms) ms[n] = t;
+        }
+        ++n;
+    }
+    g_timing.recs.clear();
+    g_timing.used = 0;
+    ok();
+    return n;
+}
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 

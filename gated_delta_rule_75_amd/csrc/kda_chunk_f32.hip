@@ -180,6 +180,8 @@ template <int DK, int DV, int C>
 hipError_t launch_shape(const PrefillArgs& a, hipStream_t s) {
     constexpr size_t bytes = F32Lds<DK, C>::kBytes;
     const dim3 grid(static_cast<unsigned>(a.N * a.H * (DV / kBV)));
+    const bool timed = timing_on();
+    if (timed) timed_begin(kKernelChunkF32, s);
     if (a.bf16) {
         auto fn = chunk_f32_kernel<DK, DV, C, uint16_t>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -193,7 +195,9 @@ hipError_t launch_shape(const PrefillArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(fn, grid, dim3(kThreads), bytes, s, a);
     }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (timed) timed_end(s);
+    return e;
 }
 
 constexpr size_t kLdsLimit = 160 * 1024;

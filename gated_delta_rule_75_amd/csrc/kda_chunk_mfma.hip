@@ -106,24 +106,9 @@ struct SeqMap {
     }
 };
 
-// ------------------------------------------------------------------------------------------
-// prep kernel: one workgroup (4 waves) per (slot, head)
-// ------------------------------------------------------------------------------------------
-struct PrepLds {
-    float tot[4][DK];              // per-block sum of g
-    float gmid[4][DK];             // within-block cumulative g at the block's 8th token
-    _Float16 kc[3][4][64][8];      // column operands of blocks 0..2, fragment order
-    _Float16 kdT[DK][C + 8];       // K'^T
-    float A[C][C + 1];             // beta-scaled strictly lower Gram, fp32
-    float M[C][C + 1];
-    float T[C][C + 1];
-    float X[4][16][17];            // per-wave scratch for the inverse
-    int unsafe;
-};
-
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_to_f32(b); }
 
-// 16x16 = A(16x16) * B(16x16), fp32 operands from LDS, four 16x16x4 steps.
+// 16x16 = A(16x16) * B(16x16), fp32 operands from LDS (row strides lda, ldb), four 16x16x4 steps.
 __device__ __forceinline__ floatx4 mm16(const float* Ap, int lda, const float* Bp, int ldb, floatx4 acc, int lane) {
     const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
@@ -131,7 +116,45 @@ __device__ __forceinline__ floatx4 mm16(const float* Ap, int lda, const float* B
     return acc;
 }
 
-__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, SeqMap sm) {
+// ------------------------------------------------------------------------------------------
+// prep kernel: one workgroup (4 waves) per (slot, head); wave w owns token block w
+// ------------------------------------------------------------------------------------------
+struct PrepLds {
+    // per key channel, per 16-token block b (all fp32):
+    float tot[4][DK];     // D_b = sum of g over block b
+    float gmid[4][DK];    // within-block cumulative g at the block's 8th token
+    float eP[4][DK];      // exp(P_b), P_b = G at the end of block b-1 (0 for b = 0)
+    float etail[4][DK];   // exp(G_{L-1} - P_{b+1}), decay after block b to the chunk end
+    float emr[4][DK];     // exp(-gmid_b): diagonal-block row factor = exp(gloc) * emr
+    float emc[4][DK];     // exp(gmid_b - D_b): diagonal-block column factor = exp(D_b - gloc) * emc
+    float Z[3][DK];       // decay between blocks: pairs (2,0), (3,1): exp(D_1), exp(D_2); (3,0): exp(D_1 + D_2)
+    _Float16 kdT[DK][C + 8];       // K'^T (transposed through LDS)
+    _Float16 M[C][C + 8];          // M, fp16
+    float AT[C][C + 1];            // A below the block diagonal; T on and above it (see inverse)
+    union {
+        _Float16 kc[3][4][64][8];  // off-diagonal column operands of blocks 0..2, fragment order
+        float X[4][16][17];        // per-wave scratch of the inverse
+    } u;
+    int unsafe;
+};
+
+__device__ __forceinline__ float dpp_row_shr(float x, int d) {
+    // lanes whose source is outside their 16-lane row read 0 (bound_ctrl)
+    switch (d) {
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+    case 4: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+    }
+}
+
+// T block (i, j), i >= j: diagonal blocks sit on the diagonal of AT, blocks below it are
+// stored in the mirrored position above the diagonal (row-major inside the block).
+__device__ __forceinline__ float* t_block(PrepLds& L, int i, int j) {
+    return i == j ? &L.AT[16 * i][16 * i] : &L.AT[16 * j][16 * i];
+}
+
+__global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) {
     __shared__ PrepLds L;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
@@ -151,147 +174,166 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, SeqMap sm) {
 
     if (threadIdx.x == 0) L.unsafe = 0;
 
-    // ---- load this lane's token (16w + lr) and its 32 channels 32*ks + 8*lg + i
+    // ---- this lane: token r = 16w + lr, channels 32*ks + 8*lg + i (the matrix-core operand
+    //      layout); rows past the chunk end load a clamped row and are zeroed
     const int r = 16 * w + lr;
     const bool valid = r < Lc;
-    const int64_t rowk = ((t0 + r) * H + h) * (int64_t)DK;
-    float kf[4][8], qf[4][8], gl[4][8];
+    const int64_t rowk = ((t0 + (valid ? r : Lc - 1)) * H + h) * (int64_t)DK;
+    uint4 kv[4], qv[4];
+    float4 gv[8];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int c0 = 32 * ks + 8 * lg;
-        if (valid) {
-            const uint4 kv = *reinterpret_cast<const uint4*>(k + rowk + c0);
-            const uint4 qv = *reinterpret_cast<const uint4*>(q + rowk + c0);
-            const float4 g0 = *reinterpret_cast<const float4*>(a.g + rowk + c0);
-            const float4 g1 = *reinterpret_cast<const float4*>(a.g + rowk + c0 + 4);
-            const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        kv[ks] = *reinterpret_cast<const uint4*>(k + rowk + c0);
+        qv[ks] = *reinterpret_cast<const uint4*>(q + rowk + c0);
+        gv[2 * ks] = *reinterpret_cast<const float4*>(a.g + rowk + c0);
+        gv[2 * ks + 1] = *reinterpret_cast<const float4*>(a.g + rowk + c0 + 4);
+    }
+    // g as floats (zero past the chunk end); k, q stay packed bf16 until used
+    float gl[4][8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kf[ks][2 * i] = bf(kw[i] & 0xFFFF);
-                kf[ks][2 * i + 1] = bf(kw[i] >> 16);
-                qf[ks][2 * i] = bf(qw[i] & 0xFFFF);
-                qf[ks][2 * i + 1] = bf(qw[i] >> 16);
-            }
-            gl[ks][0] = g0.x; gl[ks][1] = g0.y; gl[ks][2] = g0.z; gl[ks][3] = g0.w;
-            gl[ks][4] = g1.x; gl[ks][5] = g1.y; gl[ks][6] = g1.z; gl[ks][7] = g1.w;
-        } else {
+    for (int ks = 0; ks < 4; ++ks) {
+        const float4 g0 = gv[2 * ks], g1 = gv[2 * ks + 1];
+        gl[ks][0] = g0.x; gl[ks][1] = g0.y; gl[ks][2] = g0.z; gl[ks][3] = g0.w;
+        gl[ks][4] = g1.x; gl[ks][5] = g1.y; gl[ks][6] = g1.z; gl[ks][7] = g1.w;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kf[ks][i] = qf[ks][i] = gl[ks][i] = 0.f;
-        }
+        for (int i = 0; i < 8; ++i) gl[ks][i] = valid ? gl[ks][i] : 0.f;
     }
 
-    // ---- within-block inclusive cumulative sum of g over the 16 tokens (lanes lr)
+    // ---- within-block inclusive cumulative sum of g over the 16 tokens (16-lane rows)
 #pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
+    for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) gl[ks][i] += dpp_row_shr(gl[ks][i], d);
+    if (lr == 15 || lr == 7) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float y = __shfl_up(gl[ks][i], d, 16);
-                if (lr >= d) gl[ks][i] += y;
+                const int ch = 32 * ks + 8 * lg + i;
+                if (lr == 15) L.tot[w][ch] = gl[ks][i];
+                else L.gmid[w][ch] = gl[ks][i];
             }
-    }
-    if (lr == 15) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) L.tot[w][32 * ks + 8 * lg + i] = gl[ks][i];
-    }
-    if (lr == 7) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) L.gmid[w][32 * ks + 8 * lg + i] = gl[ks][i];
     }
     __syncthreads();
 
-    // ---- factors and operand tiles
+    // ---- per-channel factor tables (threads 0..127: one channel each)
+    if (threadIdx.x < DK) {
+        const int ch = threadIdx.x;
+        const float d0 = L.tot[0][ch], d1 = L.tot[1][ch], d2 = L.tot[2][ch], d3 = L.tot[3][ch];
+        const float Pb[4] = {0.f, d0, d0 + d1, d0 + d1 + d2};
+        const float Db[4] = {d0, d1, d2, d3};
+        const float Ct = d0 + d1 + d2 + d3;
+        bool bad = false;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float gm = L.gmid[b][ch];
+            L.eP[b][ch] = fast_exp(Pb[b]);
+            L.etail[b][ch] = fast_exp(Ct - Pb[b] - Db[b]);
+            L.emr[b][ch] = fast_exp(-gm);
+            L.emc[b][ch] = fast_exp(gm - Db[b]);
+            // diagonal-block factors are bounded by exp(-gm) (rows) and exp(gm - D_b) (columns);
+            // both must stay below e^10 to fit fp16
+            bad |= (-gm > 10.f) || (gm - Db[b] > 10.f);
+        }
+        L.Z[0][ch] = fast_exp(d1);
+        L.Z[1][ch] = fast_exp(d2);
+        L.Z[2][ch] = fast_exp(d1 + d2);
+        if (bad) L.unsafe = 1;  // benign race: every writer stores 1
+    }
+    __syncthreads();
+
+    // ---- operand tiles for this lane's token and 32 channels
     half8 KR[4], QR[4], KRd[4], QRd[4], KCd[4];
-    bool unsafe = false;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         half8 kp, qp, kc;
+        const uint32_t kw[4] = {kv[ks].x, kv[ks].y, kv[ks].z, kv[ks].w};
+        const uint32_t qw[4] = {qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int ch = 32 * ks + 8 * lg + i;
-            float P = 0.f, Ctot = 0.f;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float t = L.tot[b][ch];
-                if (b < w) P += t;
-                Ctot += t;
-            }
-            const float Dw = L.tot[w][ch];
             const float gloc = gl[ks][i];
-            const float gm = L.gmid[w][ch];
-            const float eloc = fast_exp(gloc);                    // exp(G_r - P_w)
-            const float ecol = fast_exp(Dw - gloc);               // exp(P_{w+1} - G_r)
-            const float eP = fast_exp(P);                         // exp(P_w)
-            const float etail = fast_exp(Ctot - P - Dw);          // exp(G_{L-1} - P_{w+1})
-            const float dr = gloc - gm, dc = gm - gloc;           // diagonal-block exponents
-            unsafe |= (dr > 10.f) || (dc > 10.f);
-            const float erd = fast_exp(dr), ecd = fast_exp(dc);
-            const float kk = kf[ks][i], qq = qf[ks][i];
-            kp[i] = (_Float16)(kk * eloc * eP);
-            qp[i] = (_Float16)(qq * eloc * eP);
-            L.kdT[ch][r] = (_Float16)(kk * ecol * etail);
+            const uint32_t kb16 = (i & 1) ? (kw[i >> 1] >> 16) : (kw[i >> 1] & 0xFFFF);
+            const uint32_t qb16 = (i & 1) ? (qw[i >> 1] >> 16) : (qw[i >> 1] & 0xFFFF);
+            const float kk = valid ? bf(kb16) : 0.f, qq = valid ? bf(qb16) : 0.f;
+            const float eloc = fast_exp(gloc);              // exp(G_r - P_w)          <= 1
+            const float ecol = fast_exp(L.tot[w][ch] - gloc);  // exp(P_{w+1} - G_r)   <= 1
+            const float ep = L.eP[w][ch];
+            kp[i] = (_Float16)(kk * eloc * ep);
+            qp[i] = (_Float16)(qq * eloc * ep);
+            L.kdT[ch][r] = (_Float16)(kk * ecol * L.etail[w][ch]);
             KR[ks][i] = (_Float16)(kk * eloc);
             QR[ks][i] = (_Float16)(qq * eloc);
             kc[i] = (_Float16)(kk * ecol);
+            const float erd = eloc * L.emr[w][ch], ecd = ecol * L.emc[w][ch];
             KRd[ks][i] = (_Float16)(kk * erd);
             QRd[ks][i] = (_Float16)(qq * erd);
             KCd[ks][i] = (_Float16)(kk * ecd);
         }
         *reinterpret_cast<half8*>(rec + kOffKp + (w * 4 + ks) * kTile + lane * 16) = kp;
         *reinterpret_cast<half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16) = qp;
-        if (w < 3) *reinterpret_cast<half8*>(&L.kc[w][ks][lane][0]) = kc;
+        if (w < 3) *reinterpret_cast<half8*>(&L.u.kc[w][ks][lane][0]) = kc;
+        // keep the per-channel table reads of one k-step from being hoisted above the previous
+        // one (bounds register pressure)
+        asm volatile("" ::: "memory");
     }
-    if (unsafe) L.unsafe = 1;  // benign race: every writer stores 1
-    __syncthreads();
 
-    // ---- gated Gram matrices, row block w (tiles (w, j) for j <= w)
+    // ---- gated Gram matrices of row block w: first the diagonal tile (w, w) from this lane's
+    //      own operands, then (after the column operands of the other blocks are visible) the
+    //      tiles (w, j < w)
     float brow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int rr = 16 * w + 4 * lg + i;
-        brow[i] = rr < Lc ? bf(beta[(t0 + rr) * H + h]) : 0.f;
+        const float bv = bf(beta[(t0 + (rr < Lc ? rr : Lc - 1)) * H + h]);
+        brow[i] = rr < Lc ? bv : 0.f;
     }
-    for (int j = 0; j < 4; ++j) {
+    {
         floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
-        if (j < w) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                half8 bcol = *reinterpret_cast<const half8*>(&L.kc[j][ks][lane][0]);
-                if (j + 1 < w) {  // scale by exp(P_w - P_{j+1}), the decay of blocks j+1 .. w-1
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int ch = 32 * ks + 8 * lg + i;
-                        float z = 0.f;
-                        for (int b = j + 1; b < w; ++b) z += L.tot[b][ch];
-                        bcol[i] = (_Float16)((float)bcol[i] * fast_exp(z));
-                    }
-                }
-                accA = mfma16x16x32(KR[ks], bcol, accA);
-                accM = mfma16x16x32(QR[ks], bcol, accM);
-            }
-        } else if (j == w) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                accA = mfma16x16x32(KRd[ks], KCd[ks], accA);
-                accM = mfma16x16x32(QRd[ks], KCd[ks], accM);
-            }
+        for (int ks = 0; ks < 4; ++ks) {
+            accA = mfma16x16x32(KRd[ks], KCd[ks], accA);
+            accM = mfma16x16x32(QRd[ks], KCd[ks], accM);
         }
         // accumulator: column s = lr of block j, rows 4*lg + i of block w
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const int rr = 16 * w + 4 * lg + i, ss = 16 * w + lr;
+            L.AT[rr][ss] = (ss < rr) ? brow[i] * accA[i] : 0.f;
+            L.M[rr][ss] = (_Float16)((ss <= rr) ? accM[i] : 0.f);
+        }
+        for (int j = w + 1; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) L.M[16 * w + 4 * lg + i][16 * j + lr] = (_Float16)0.f;
+    }
+    __syncthreads();
+    for (int j = 0; j < w; ++j) {
+        floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+        const int zi = (w - j == 2) ? (w == 2 ? 0 : 1) : 2;  // Z table of pair (w, j) when j + 1 < w
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            half8 bcol = *reinterpret_cast<const half8*>(&L.u.kc[j][ks][lane][0]);
+            if (j + 1 < w) {  // scale by exp(P_w - P_{j+1}), the decay of blocks j+1 .. w-1
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bcol[i] = (_Float16)((float)bcol[i] * L.Z[zi][32 * ks + 8 * lg + i]);
+            }
+            accA = mfma16x16x32(KR[ks], bcol, accA);
+            accM = mfma16x16x32(QR[ks], bcol, accM);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
             const int rr = 16 * w + 4 * lg + i, ss = 16 * j + lr;
-            L.A[rr][ss] = (ss < rr) ? brow[i] * accA[i] : 0.f;
-            L.M[rr][ss] = (ss <= rr) ? accM[i] : 0.f;
+            L.AT[rr][ss] = brow[i] * accA[i];
+            L.M[rr][ss] = (_Float16)accM[i];
         }
     }
     __syncthreads();
 
-    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (lane = column)
+    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (lane = column);
+    //      T_ww overwrites A_ww (no longer needed)
     if (lane < 16) {
         const int j = lane, o = 16 * w;
         float tc[16];
@@ -299,16 +341,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, SeqMap sm) {
         for (int rr = 0; rr < 16; ++rr) {
             float acc = 0.f;
 #pragma unroll
-            for (int s = 0; s < rr; ++s) acc += L.A[o + rr][o + s] * tc[s];
+            for (int s2 = 0; s2 < rr; ++s2) acc += L.AT[o + rr][o + s2] * tc[s2];
             tc[rr] = rr < j ? 0.f : (rr == j ? 1.f : -acc);
         }
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) L.T[o + rr][o + j] = tc[rr];
-    }
-    // zero the strictly upper blocks of T
-    for (int e = threadIdx.x; e < C * C; e += 256) {
-        const int rr = e / C, ss = e % C;
-        if ((ss >> 4) > (rr >> 4)) L.T[rr][ss] = 0.f;
+        for (int rr = 0; rr < 16; ++rr) L.AT[o + rr][o + j] = tc[rr];
     }
     __syncthreads();
     // off-diagonal blocks: T_ij = -T_ii * (sum_{m=j}^{i-1} A_im T_mj), by distance i - j
@@ -316,15 +353,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, SeqMap sm) {
         const int j = w, i = w + dist;
         if (i < 4) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int m = j; m < i; ++m) acc = mm16(&L.A[16 * i][16 * m], C + 1, &L.T[16 * m][16 * j], C + 1, acc, lane);
+            for (int m = j; m < i; ++m) acc = mm16(&L.AT[16 * i][16 * m], C + 1, t_block(L, m, j), C + 1, acc, lane);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) L.X[w][4 * lg + e][lr] = acc[e];
+            for (int e = 0; e < 4; ++e) L.u.X[w][4 * lg + e][lr] = acc[e];
             __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_wave_barrier();
             floatx4 t = {0.f, 0.f, 0.f, 0.f};
-            t = mm16(&L.T[16 * i][16 * i], C + 1, &L.X[w][0][0], 17, t, lane);
+            t = mm16(t_block(L, i, i), C + 1, &L.u.X[w][0][0], 17, t, lane);
+            float* dst = t_block(L, i, j);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) L.T[16 * i + 4 * lg + e][16 * j + lr] = -t[e];
+            for (int e = 0; e < 4; ++e) dst[(4 * lg + e) * (C + 1) + lr] = -t[e];
         }
         __syncthreads();
     }
@@ -332,14 +370,17 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, SeqMap sm) {
     // ---- write T, M (8 tiles each) and K'^T (16 tiles) as fp16 operand tiles
     for (int t = w; t < 8; t += 4) {
         const int rb = t >> 1, kb = t & 1;
-        half8 tv, mv;
+        half8 tv;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            tv[i] = (_Float16)L.T[16 * rb + lr][32 * kb + 8 * lg + i];
-            mv[i] = (_Float16)L.M[16 * rb + lr][32 * kb + 8 * lg + i];
+            const int col = 32 * kb + 8 * lg + i, cb = col >> 4;
+            float val = 0.f;
+            if (cb <= rb) val = t_block(L, rb, cb)[lr * (C + 1) + (col & 15)];
+            tv[i] = (_Float16)val;
         }
         *reinterpret_cast<half8*>(rec + kOffT + t * kTile + lane * 16) = tv;
-        *reinterpret_cast<half8*>(rec + kOffM + t * kTile + lane * 16) = mv;
+        *reinterpret_cast<half8*>(rec + kOffM + t * kTile + lane * 16) =
+            *reinterpret_cast<const half8*>(&L.M[16 * rb + lr][32 * kb + 8 * lg]);
     }
     for (int t = w; t < 16; t += 4) {
         const int cb = t >> 1, ks = t & 1;
@@ -357,6 +398,47 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, SeqMap sm) {
 // ------------------------------------------------------------------------------------------
 // state kernel: one workgroup (4 waves) per (sequence, head, 16-column value block)
 // ------------------------------------------------------------------------------------------
+// Operands of one chunk as held by one lane of wave w.
+struct ChunkFrags {
+    half8 kp[4], qp[4];   // K+, Q+ rows of token block w, k-steps 0..3
+    half8 kd[2][2];       // K'^T rows of channel blocks 2w, 2w+1, k-steps 0..1
+    half8 tt[2], mm[2];   // T, M rows of token block w, k-steps 0..1
+    floatx4 gam[2];       // gamma for this lane's 4 channels of each owned channel block
+    uint16_t vr[4], br[4];  // raw bf16 v and beta of this lane's 4 tokens (clamped index)
+};
+
+__device__ __forceinline__ void load_chunk(ChunkFrags& f, const unsigned char* rec, const uint16_t* v,
+                                           const uint16_t* beta, int64_t t0, int Lc, int H, int h, int vb, int w,
+                                           int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        f.kp[ks] = *reinterpret_cast<const half8*>(rec + kOffKp + (w * 4 + ks) * kTile + lane * 16);
+        f.qp[ks] = *reinterpret_cast<const half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            f.kd[t][ks] = *reinterpret_cast<const half8*>(rec + kOffKdT + ((2 * w + t) * 2 + ks) * kTile + lane * 16);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        f.tt[kb] = *reinterpret_cast<const half8*>(rec + kOffT + (w * 2 + kb) * kTile + lane * 16);
+        f.mm[kb] = *reinterpret_cast<const half8*>(rec + kOffM + (w * 2 + kb) * kTile + lane * 16);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        f.gam[t] = *reinterpret_cast<const floatx4*>(rec + kOffGamma + (16 * (2 * w + t) + 4 * lg) * 4);
+    // unconditional loads at a clamped token (no branch); masked where used
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * w + 4 * lg + i;
+        const int rc = rr < Lc ? rr : Lc - 1;
+        f.vr[i] = v[((t0 + rc) * H + h) * (int64_t)DV + vb * BV + lr];
+        f.br[i] = beta[(t0 + rc) * H + h];
+    }
+}
+
 __global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
     __shared__ _Float16 S_lds[BV][DK + 8];  // state block as matrix-core B operand: [column][channel]
     __shared__ _Float16 R_lds[BV][C + 8];   // [column][token]
@@ -388,58 +470,39 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
     const uint16_t* v = static_cast<const uint16_t*>(a.v);
     const uint16_t* beta = static_cast<const uint16_t*>(a.beta);
     const int64_t sbase = nh * (int64_t)DK * DV + vb * BV;
+    const unsigned char* ws = static_cast<const unsigned char*>(a.ws);
 
     // fp32 state rows owned by this wave: channel blocks 2w, 2w+1 (accumulator layout)
-    floatx4 Sf[2];
+    floatx4 Sf[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (a.s0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Sf[t][i] = a.s0[sbase + (int64_t)(16 * (2 * w + t) + 4 * lg + i) * DV + lr];
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int cb = 2 * w + t;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ch = 16 * cb + 4 * lg + i;
-            Sf[t][i] = a.s0 ? a.s0[sbase + (int64_t)ch * DV + lr] : 0.f;
-        }
         half4 hv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) hv[i] = (_Float16)Sf[t][i];
-        *reinterpret_cast<half4*>(&S_lds[lr][16 * cb + 4 * lg]) = hv;
+        *reinterpret_cast<half4*>(&S_lds[lr][16 * (2 * w + t) + 4 * lg]) = hv;
+    }
+
+    ChunkFrags nxt;
+    if (nchunks > 0) {
+        const int L0 = (int)((eos - bos) < C ? (eos - bos) : C);
+        load_chunk(nxt, ws + (slot0 * H + h) * (int64_t)kRecord, v, beta, bos, L0, H, h, vb, w, lane);
     }
     __syncthreads();
 
     for (int64_t c = 0; c < nchunks; ++c) {
-        const unsigned char* rec =
-            static_cast<const unsigned char*>(a.ws) + ((slot0 + c) * H + h) * (int64_t)kRecord;
         const int64_t t0 = bos + c * C;
         const int Lc = (int)((eos - t0) < C ? (eos - t0) : C);
-        half8 kp[4], qp[4], kd[2][2], tt[2], mm[2];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            kp[ks] = *reinterpret_cast<const half8*>(rec + kOffKp + (w * 4 + ks) * kTile + lane * 16);
-            qp[ks] = *reinterpret_cast<const half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                kd[t][ks] = *reinterpret_cast<const half8*>(rec + kOffKdT + ((2 * w + t) * 2 + ks) * kTile + lane * 16);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            tt[kb] = *reinterpret_cast<const half8*>(rec + kOffT + (w * 2 + kb) * kTile + lane * 16);
-            mm[kb] = *reinterpret_cast<const half8*>(rec + kOffM + (w * 2 + kb) * kTile + lane * 16);
-        }
-        float gam[2][4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const float4 gv = *reinterpret_cast<const float4*>(rec + kOffGamma + (16 * (2 * w + t) + 4 * lg) * 4);
-            gam[t][0] = gv.x; gam[t][1] = gv.y; gam[t][2] = gv.z; gam[t][3] = gv.w;
-        }
-        float vv[4], bb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 16 * w + 4 * lg + i;
-            const bool ok = rr < Lc;
-            vv[i] = ok ? bf(v[((t0 + rr) * H + h) * (int64_t)DV + vb * BV + lr]) : 0.f;
-            bb[i] = ok ? bf(beta[(t0 + rr) * H + h]) : 0.f;
+        const ChunkFrags cur = nxt;
+        if (c + 1 < nchunks) {  // prefetch the next chunk's operands (uniform branch)
+            const int64_t t1 = t0 + C;
+            const int L1 = (int)((eos - t1) < C ? (eos - t1) : C);
+            load_chunk(nxt, ws + ((slot0 + c + 1) * H + h) * (int64_t)kRecord, v, beta, t1, L1, H, h, vb, w, lane);
         }
 
         // X = K+ S0, Y = Q+ S0 for this wave's 16 tokens
@@ -447,21 +510,25 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const half8 sb = *reinterpret_cast<const half8*>(&S_lds[lr][32 * ks + 8 * lg]);
-            X = mfma16x16x32(kp[ks], sb, X);
-            Y = mfma16x16x32(qp[ks], sb, Y);
+            X = mfma16x16x32(cur.kp[ks], sb, X);
+            Y = mfma16x16x32(cur.qp[ks], sb, Y);
         }
         half4 rh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rh[i] = (_Float16)(bb[i] * (vv[i] - X[i]));
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = 16 * w + 4 * lg + i < Lc;
+            const float vv = ok ? bf(cur.vr[i]) : 0.f, bb = ok ? bf(cur.br[i]) : 0.f;
+            rh[i] = (_Float16)(bb * (vv - X[i]));
+        }
         *reinterpret_cast<half4*>(&R_lds[lr][16 * w + 4 * lg]) = rh;
         __syncthreads();
 
-        // D = T R (rows of this wave's token block)
+        // D = T R for this wave's token block (T is zero above its block diagonal)
         floatx4 Dacc = {0.f, 0.f, 0.f, 0.f};
-        const int nkb = w >= 2 ? 2 : 1;
-        for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
             const half8 rb = *reinterpret_cast<const half8*>(&R_lds[lr][32 * kb + 8 * lg]);
-            Dacc = mfma16x16x32(tt[kb], rb, Dacc);
+            Dacc = mfma16x16x32(cur.tt[kb], rb, Dacc);
         }
         half4 dh;
 #pragma unroll
@@ -474,7 +541,8 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) db[kb] = *reinterpret_cast<const half8*>(&D_lds[lr][32 * kb + 8 * lg]);
         floatx4 O = Y;
-        for (int kb = 0; kb < nkb; ++kb) O = mfma16x16x32(mm[kb], db[kb], O);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) O = mfma16x16x32(cur.mm[kb], db[kb], O);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rr = 16 * w + 4 * lg + i;
@@ -484,11 +552,9 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
         // S1 = Diag(gamma) S0 + K'^T D for this wave's 32 channels
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            floatx4 acc;
+            floatx4 acc = cur.gam[t] * Sf[t];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = gam[t][i] * Sf[t][i];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) acc = mfma16x16x32(kd[t][kb], db[kb], acc);
+            for (int kb = 0; kb < 2; ++kb) acc = mfma16x16x32(cur.kd[t][kb], db[kb], acc);
             Sf[t] = acc;
             half4 hv;
 #pragma unroll
@@ -502,10 +568,8 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ch = 16 * (2 * w + t) + 4 * lg + i;
-                a.sT[sbase + (int64_t)ch * DV + lr] = Sf[t][i];
-            }
+            for (int i = 0; i < 4; ++i)
+                a.sT[sbase + (int64_t)(16 * (2 * w + t) + 4 * lg + i) * DV + lr] = Sf[t][i];
     }
 }
 
@@ -537,13 +601,19 @@ hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
     if (a.N * a.H == 0) return hipSuccess;
     const SeqMap sm = make_map(a);
     const int64_t slots = num_slots(a.N, a.T_fixed, a.T_total, a.cu == nullptr);
+    const bool timed = timing_on();
     if (slots > 0 && a.T_total > 0) {
+        if (timed) timed_begin(kKernelPrep, s);
         hipLaunchKernelGGL(prep_kernel, dim3((unsigned)slots, (unsigned)a.H), dim3(256), 0, s, a, sm);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (timed) timed_end(s);
     }
+    if (timed) timed_begin(kKernelState, s);
     hipLaunchKernelGGL(state_kernel, dim3((unsigned)(a.N * a.H * NVB)), dim3(256), 0, s, a, sm);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (timed) timed_end(s);
+    return e;
 }
 
 }  // namespace kda

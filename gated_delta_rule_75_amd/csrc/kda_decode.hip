@@ -123,6 +123,8 @@ template <int DK, int DV>
 hipError_t launch_shape(const DecodeArgs& a, hipStream_t s) {
     using Sh = DecodeShape<DK, DV>;
     const dim3 grid(static_cast<unsigned>(a.N * a.H));
+    const bool timed = timing_on();
+    if (timed) timed_begin(kKernelDecode, s);
     if (a.bf16) {
         hipLaunchKernelGGL((decode_kernel<DK, DV, uint16_t>), grid, dim3(Sh::kThreads), 0, s,
                            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
@@ -134,7 +136,9 @@ hipError_t launch_shape(const DecodeArgs& a, hipStream_t s) {
                            static_cast<const float*>(a.v), a.g, static_cast<const float*>(a.beta), a.s_in,
                            a.s_out, a.o);
     }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (timed) timed_end(s);
+    return e;
 }
 
 }  // namespace

@@ -7,6 +7,13 @@
 
 namespace kda {
 
+// Per-kernel event timing (diagnostics).  When timing is on for the calling
+// thread, launchers bracket each kernel with timed_begin/timed_end.
+enum KernelId { kKernelPrep = 1, kKernelState = 2, kKernelChunkF32 = 3, kKernelDecode = 4 };
+bool timing_on();
+void timed_begin(int kernel_id, hipStream_t s);
+void timed_end(hipStream_t s);
+
 // Sequences of a prefill/append call.  Either `cu` (device int32 [N+1]) is set,
 // or every sequence has `T_fixed` tokens and sequence n starts at n * T_fixed.
 struct PrefillArgs {

@@ -134,6 +134,27 @@ const char* kda_last_error(void);
 /* Library version string. */
 const char* kda_version(void);
 
+/*
+ * Diagnostics: per-kernel timing with HIP events (the library's own tracing).
+ * kda_timing_begin() starts recording, for calls made on the calling thread,
+ * a HIP event immediately before and after every kernel the library launches,
+ * on that call's stream.  kda_timing_end() stops recording, waits for the
+ * recorded events, and writes up to max_records (kernel id, milliseconds)
+ * pairs in launch order into kernel_ids / ms (either may be NULL to only
+ * count).  Returns the number of kernels recorded, or a negative kda_status
+ * (KDA_ERR_HIP if an event failed).  Event objects are created on first use and
+ * reused; no device memory is allocated.  Kernel ids are kda_kernel values.
+ */
+typedef enum {
+    KDA_KERNEL_PREP = 1,      /* chunk-parallel prep of the matrix-core prefill */
+    KDA_KERNEL_STATE = 2,     /* sequential state pass of the matrix-core prefill */
+    KDA_KERNEL_CHUNK_F32 = 3, /* fp32 chunked prefill */
+    KDA_KERNEL_DECODE = 4     /* decode step */
+} kda_kernel;
+
+int kda_timing_begin(void);
+int kda_timing_end(int32_t* kernel_ids, float* ms, int32_t max_records);
+
 #ifdef __cplusplus
 }
 #endif
