@@ -68,11 +68,12 @@ def _lib():
 
 
 def default_threads() -> int:
+    """Host threads the oracle uses: the CPUs this process may run on, at most 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, n)
+    return max(1, min(16, n))
 
 
 def _f64(x):

@@ -31,4 +31,5 @@ def assert_close(x, y, tol, cu=None, what=""):
     e = slice_rel_err(x, y, cu)
     worst = float(e.max()) if e.size else 0.0
     assert worst <= tol, f"{what}: max per-slice error {worst:.3e} > {tol:.1e} at {np.unravel_index(e.argmax(), e.shape)}"
+    print(f"  {what}: max per-slice error {worst:.3e} (tol {tol:.0e})", flush=True)
     return worst
