@@ -49,13 +49,14 @@ constexpr int NVB = DV / BV;
 
 // chunk record in the workspace (bytes); tiles are 64 lanes x 16 bytes
 constexpr int kTile = 1024;
-constexpr int kOffKp = 0;                 // 16 tiles (token block tb, k-step ks): tb*4+ks
+constexpr int kOffW = 0;                  // 16 tiles (token block tb, k-step ks): tb*4+ks
 constexpr int kOffQp = 16 * kTile;        // 16 tiles
 constexpr int kOffKdT = 32 * kTile;       // 16 tiles (channel block cb, k-step ks): cb*2+ks
 constexpr int kOffT = 48 * kTile;         // 8 tiles (row block rb, k-step kb): rb*2+kb
 constexpr int kOffM = 56 * kTile;         // 8 tiles
 constexpr int kOffGamma = 64 * kTile;     // 128 floats
 constexpr int kRecord = 64 * kTile + 512; // 66048 bytes (multiple of 256)
+constexpr int kWarmAhead = 6;             // chunks of L2 warm-up ahead of the state pass
 
 __device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -128,12 +129,16 @@ struct PrepLds {
     float emr[4][DK];     // exp(-gmid_b): diagonal-block row factor = exp(gloc) * emr
     float emc[4][DK];     // exp(gmid_b - D_b): diagonal-block column factor = exp(D_b - gloc) * emc
     float Z[3][DK];       // decay between blocks: pairs (2,0), (3,1): exp(D_1), exp(D_2); (3,0): exp(D_1 + D_2)
-    _Float16 kdT[DK][C + 8];       // K'^T (transposed through LDS)
+    union {
+        _Float16 kdT[DK][C + 8];   // K'^T (transposed through LDS)
+        _Float16 W[C][DK + 8];     // W = T Diag(beta) K+, fp16, after K'^T has been written out
+    } o;
     _Float16 M[C][C + 8];          // M, fp16
     float AT[C][C + 1];            // A below the block diagonal; T on and above it (see inverse)
     union {
         _Float16 kc[3][4][64][8];  // off-diagonal column operands of blocks 0..2, fragment order
         float X[4][16][17];        // per-wave scratch of the inverse
+        _Float16 bk[C][DK + 8];    // Diag(beta) K+ as [token][channel], operand of W
     } u;
     int unsafe;
 };
@@ -156,7 +161,8 @@ __device__ __forceinline__ float* t_block(PrepLds& L, int i, int j) {
 
 __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) {
     __shared__ PrepLds L;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave index, wave-uniform (readfirstlane lets the compiler keep it in a scalar register)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int H = a.H;
     const int h = blockIdx.y;
@@ -246,10 +252,13 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
     __syncthreads();
 
     // ---- operand tiles for this lane's token and 32 channels
-    half8 KR[4], QR[4], KRd[4], QRd[4], KCd[4];
+    // beta of this lane's token (0 past the chunk end) for Diag(beta) K+
+    const float brow_r = valid ? bf(beta[(t0 + (valid ? r : Lc - 1)) * H + h]) : 0.f;
+    half8 KR[4], QR[4], BKp[4];
+    floatx4 diagA = {0.f, 0.f, 0.f, 0.f}, diagM = {0.f, 0.f, 0.f, 0.f};  // tile (w, w)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        half8 kp, qp, kc;
+        half8 kp, qp, kc, krd, qrd, kcd;
         const uint32_t kw[4] = {kv[ks].x, kv[ks].y, kv[ks].z, kv[ks].w};
         const uint32_t qw[4] = {qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w};
 #pragma unroll
@@ -262,18 +271,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
             const float eloc = fast_exp(gloc);              // exp(G_r - P_w)          <= 1
             const float ecol = fast_exp(L.tot[w][ch] - gloc);  // exp(P_{w+1} - G_r)   <= 1
             const float ep = L.eP[w][ch];
-            kp[i] = (_Float16)(kk * eloc * ep);
+            kp[i] = (_Float16)(kk * eloc * ep * brow_r);
             qp[i] = (_Float16)(qq * eloc * ep);
-            L.kdT[ch][r] = (_Float16)(kk * ecol * L.etail[w][ch]);
+            L.o.kdT[ch][r] = (_Float16)(kk * ecol * L.etail[w][ch]);
             KR[ks][i] = (_Float16)(kk * eloc);
             QR[ks][i] = (_Float16)(qq * eloc);
             kc[i] = (_Float16)(kk * ecol);
             const float erd = eloc * L.emr[w][ch], ecd = ecol * L.emc[w][ch];
-            KRd[ks][i] = (_Float16)(kk * erd);
-            QRd[ks][i] = (_Float16)(qq * erd);
-            KCd[ks][i] = (_Float16)(kk * ecd);
+            krd[i] = (_Float16)(kk * erd);
+            qrd[i] = (_Float16)(qq * erd);
+            kcd[i] = (_Float16)(kk * ecd);
         }
-        *reinterpret_cast<half8*>(rec + kOffKp + (w * 4 + ks) * kTile + lane * 16) = kp;
+        // diagonal Gram tile (w, w): this lane's operands are both the row and the column
+        // fragments, so it accumulates k-step by k-step with nothing exchanged
+        diagA = mfma16x16x32(krd, kcd, diagA);
+        diagM = mfma16x16x32(qrd, kcd, diagM);
+        BKp[ks] = kp;  // Diag(beta) K+, consumed by W after T is known
         *reinterpret_cast<half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16) = qp;
         if (w < 3) *reinterpret_cast<half8*>(&L.u.kc[w][ks][lane][0]) = kc;
         // keep the per-channel table reads of one k-step from being hoisted above the previous
@@ -292,12 +305,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
         brow[i] = rr < Lc ? bv : 0.f;
     }
     {
-        floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            accA = mfma16x16x32(KRd[ks], KCd[ks], accA);
-            accM = mfma16x16x32(QRd[ks], KCd[ks], accM);
-        }
+        const floatx4 accA = diagA, accM = diagM;
         // accumulator: column s = lr of block j, rows 4*lg + i of block w
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -384,9 +392,44 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
     }
     for (int t = w; t < 16; t += 4) {
         const int cb = t >> 1, ks = t & 1;
-        const half8 kd = *reinterpret_cast<const half8*>(&L.kdT[16 * cb + lr][32 * ks + 8 * lg]);
+        const half8 kd = *reinterpret_cast<const half8*>(&L.o.kdT[16 * cb + lr][32 * ks + 8 * lg]);
         *reinterpret_cast<half8*>(rec + kOffKdT + t * kTile + lane * 16) = kd;
     }
+    __syncthreads();  // K'^T read out of the union; the inverse scratch is dead
+
+    // ---- W = T Diag(beta) K+ (64 x 128): rows of token block w, all 8 channel blocks
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        *reinterpret_cast<half8*>(&L.u.bk[r][32 * ks + 8 * lg]) = BKp[ks];
+    __syncthreads();
+    {
+        half8 ta[2];  // T rows of block w as matrix-core A operand, k-steps 0..1 (zero above the diagonal)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int col = 32 * kb + 8 * lg + i, cb = col >> 4;
+                ta[kb][i] = (_Float16)(cb <= w ? t_block(L, w, cb)[lr * (C + 1) + (col & 15)] : 0.f);
+            }
+        for (int cb = 0; cb < 8; ++cb) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                half8 bb;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bb[i] = L.u.bk[32 * kb + 8 * lg + i][16 * cb + lr];
+                acc = mfma16x16x32(ta[kb], bb, acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) L.o.W[16 * w + 4 * lg + i][16 * cb + lr] = (_Float16)acc[i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        *reinterpret_cast<half8*>(rec + kOffW + (w * 4 + ks) * kTile + lane * 16) =
+            *reinterpret_cast<const half8*>(&L.o.W[16 * w + lr][32 * ks + 8 * lg]);
+
     if (w == 0) {
         float* gam = reinterpret_cast<float*>(rec + kOffGamma);
         const float poison = L.unsafe ? __builtin_nanf("") : 0.f;
@@ -396,54 +439,241 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
 }
 
 // ------------------------------------------------------------------------------------------
-// state kernel: one workgroup (4 waves) per (sequence, head, 16-column value block)
+// state kernel: one workgroup per (sequence, head, 16-column value block)
 // ------------------------------------------------------------------------------------------
-// Operands of one chunk as held by one lane of wave w.
+// Per chunk, with S0 the entering state block (128 x 16) and U = T Diag(beta) V:
+//     D  = U - W S0                 (the corrections; W = T Diag(beta) K+ from the prep kernel)
+//     O  = Q+ S0 + M D
+//     S1 = Diag(gamma) S0 + K'^T D
+// Only W S0 -> D -> K'^T D -> S1 is on the sequential path; U and Q+ S0 do not depend on the
+// state.  Compute wave w (0..3) owns token block w (D, O) and key-channel blocks 2w, 2w+1 of
+// the state (update).  Two LDS exchanges per chunk: D (all tokens, for M D and K'^T D) and S1
+// (all channels, for the next chunk's products).  beta*V of the next chunk is staged in LDS,
+// in the matrix-core B layout, in the same pass.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor for `bytes` bytes at `base`.  Both are wave-uniform here; reading them
+// through readfirstlane tells the compiler so (a descriptor it cannot prove uniform is
+// wrapped in a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void* up = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(up, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Operands of one chunk as held by one lane of compute wave w.
 struct ChunkFrags {
-    half8 kp[4], qp[4];   // K+, Q+ rows of token block w, k-steps 0..3
+    half8 wt[4], qp[4];   // W, Q+ rows of token block w, k-steps 0..3
     half8 kd[2][2];       // K'^T rows of channel blocks 2w, 2w+1, k-steps 0..1
-    half8 tt[2], mm[2];   // T, M rows of token block w, k-steps 0..1
-    floatx4 gam[2];       // gamma for this lane's 4 channels of each owned channel block
-    uint16_t vr[4], br[4];  // raw bf16 v and beta of this lane's 4 tokens (clamped index)
+    half8 tt[2], mm[2];   // T, M rows of token block w, k-steps 0..1 (k-step 1 is zero for w < 2)
 };
 
-__device__ __forceinline__ void load_chunk(ChunkFrags& f, const unsigned char* rec, const uint16_t* v,
-                                           const uint16_t* beta, int64_t t0, int Lc, int H, int h, int vb, int w,
-                                           int lane) {
-    const int lr = lane & 15, lg = lane >> 4;
+__device__ __forceinline__ half8 as_half8(u32x4 x) { return __builtin_bit_cast(half8, x); }
+
+// The operand loads of one chunk in four groups.  Each wave-wide load costs the CU's address
+// unit about as much whatever its width, and a wave stalls at issue when that unit is busy, so
+// the groups are issued at four points spread over the previous chunk's compute rather than
+// back to back.
+__device__ __forceinline__ void load_group(ChunkFrags& f, __amdgpu_buffer_rsrc_t rr, int g, int w, int lane) {
+    const int lo = lane * 16;
+    if (g == 0) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        f.kp[ks] = *reinterpret_cast<const half8*>(rec + kOffKp + (w * 4 + ks) * kTile + lane * 16);
-        f.qp[ks] = *reinterpret_cast<const half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16);
-    }
+        for (int ks = 0; ks < 4; ++ks)
+            f.wt[ks] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffW + (w * 4 + ks) * kTile, 0));
+    } else if (g == 1) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int ks = 0; ks < 4; ++ks)
+            f.qp[ks] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffQp + (w * 4 + ks) * kTile, 0));
+    } else if (g == 2) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            f.kd[t][ks] = *reinterpret_cast<const half8*>(rec + kOffKdT + ((2 * w + t) * 2 + ks) * kTile + lane * 16);
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        f.tt[kb] = *reinterpret_cast<const half8*>(rec + kOffT + (w * 2 + kb) * kTile + lane * 16);
-        f.mm[kb] = *reinterpret_cast<const half8*>(rec + kOffM + (w * 2 + kb) * kTile + lane * 16);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-        f.gam[t] = *reinterpret_cast<const floatx4*>(rec + kOffGamma + (16 * (2 * w + t) + 4 * lg) * 4);
-    // unconditional loads at a clamped token (no branch); masked where used
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * w + 4 * lg + i;
-        const int rc = rr < Lc ? rr : Lc - 1;
-        f.vr[i] = v[((t0 + rc) * H + h) * (int64_t)DV + vb * BV + lr];
-        f.br[i] = beta[(t0 + rc) * H + h];
+            for (int ks = 0; ks < 2; ++ks)
+                f.kd[t][ks] = as_half8(
+                    __builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffKdT + ((2 * w + t) * 2 + ks) * kTile, 0));
+    } else {
+        f.tt[0] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffT + (w * 2) * kTile, 0));
+        f.mm[0] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffM + (w * 2) * kTile, 0));
+        if (w >= 2) {  // rows of token blocks 0, 1 have no entries in tokens 32..63
+            f.tt[1] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffT + (w * 2 + 1) * kTile, 0));
+            f.mm[1] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffM + (w * 2 + 1) * kTile, 0));
+        }
     }
 }
 
-__global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
-    __shared__ _Float16 S_lds[BV][DK + 8];  // state block as matrix-core B operand: [column][channel]
-    __shared__ _Float16 R_lds[BV][C + 8];   // [column][token]
-    __shared__ _Float16 D_lds[BV][C + 8];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void load_chunk(ChunkFrags& f, const unsigned char* rec, int w, int lane) {
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, kRecord);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) load_group(f, rr, g, w, lane);
+}
+
+// Warm L2 with the chunk record `rec` ahead of its use: each (sequence, head) has NVB state
+// workgroups reading the same record, so workgroup vb touches every NVB-th 128-byte line of
+// it, one line per lane, with 4-byte direct-to-LDS loads into a dummy slot (no registers are
+// written and nothing waits on them).
+constexpr int kLinesPerRecord = (kRecord + 127) / 128;
+
+__device__ __forceinline__ void warm_l2(const unsigned char* rec, int vb, int lane,
+                                        __attribute__((address_space(3))) void* dummy) {
+    for (int base = 0; base * NVB < kLinesPerRecord; base += 64) {
+        int line = vb + NVB * (base + lane);
+        if (line >= kLinesPerRecord) line = kLinesPerRecord - 1;
+        __builtin_amdgcn_global_load_lds(rec + (size_t)line * 128, dummy, 4, 0, 0);
+    }
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations (lgkmcnt)
+// but not for outstanding global loads, so operand prefetches and L2 warm-ups stay in flight
+// across it (a full __syncthreads() fence would drain them).  The empty asm statements keep
+// the compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // gfx9 encoding: vmcnt/expcnt at max, lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+struct StateLds {
+    alignas(16) _Float16 S[BV][DK + 8];      // state block as B operand: [column][channel]
+    alignas(16) _Float16 D[BV][C + 8];       // corrections as B operand: [column][token]
+    alignas(16) _Float16 BVs[2][BV][C + 8];  // beta*V as B operand, double-buffered by chunk parity
+    alignas(16) float gam[2][DK];            // gamma, double-buffered by chunk parity
+    alignas(16) float Ost[4][16][20];        // per-wave output tile, transposed to token rows
+    alignas(16) float warm_dummy[64];        // sink of the L2 warm-up loads (never read)
+};
+
+// v, beta and gamma of one chunk as loaded by the staging wave: lane l covers token
+// 32*j + l/2 (j = 0, 1), value columns 8*(l&1) .. +7 of this workgroup's block, and gamma
+// channels 2l, 2l+1.  Descriptors end at the chunk's last token, so later tokens read 0.
+struct StageRegs {
+    u32x4 v[2];
+    uint32_t b[2];
+    uint32_t g[2];
+};
+
+__device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* v, const uint16_t* beta,
+                                           const unsigned char* rec, int64_t t0, int Lc, int H, int h, int vb,
+                                           int lane) {
+    const int64_t rowv = (int64_t)H * DV;
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(v + (t0 * H + h) * (int64_t)DV + vb * BV, (uint32_t)(((Lc - 1) * rowv + BV) * 2));
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(beta + t0 * H + h, (uint32_t)(((Lc - 1) * H + 1) * 2));
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(rec + kOffGamma, DK * 4);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int tok = 32 * j + (lane >> 1);
+        r.v[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)((tok * rowv + 8 * (lane & 1)) * 2), 0, 0);
+        r.b[j] = __builtin_amdgcn_raw_buffer_load_b16(brs, tok * H * 2, 0, 0);
+    }
+    r.g[0] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8, 0, 0);
+    r.g[1] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8 + 4, 0, 0);
+}
+
+__device__ __forceinline__ void stage_store(StateLds& L, int buf, const StageRegs& r, int lane) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int tok = 32 * j + (lane >> 1);
+        const float bt = bf((uint16_t)r.b[j]);
+        const uint32_t words[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t bits = (uint16_t)((e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFF));
+            L.BVs[buf][8 * (lane & 1) + e][tok] = (_Float16)(bt * bf(bits));
+        }
+    }
+    L.gam[buf][2 * lane] = __uint_as_float(r.g[0]);
+    L.gam[buf][2 * lane + 1] = __uint_as_float(r.g[1]);
+}
+
+// Output rows of one chunk: the accumulator tile (lane = column, 4 rows) goes through LDS so
+// that each lane stores 4 consecutive columns of one token row (one 16-byte store per lane);
+// the descriptor ends at the chunk's last token.
+__device__ __forceinline__ void store_o(StateLds& L, floatx4 O, float* obase, int Lc, int H, int w, int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L.Ost[w][4 * lg + i][lr] = O[i];
+    const floatx4 row = *reinterpret_cast<const floatx4*>(&L.Ost[w][lane >> 2][4 * (lane & 3)]);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(obase, (uint32_t)(((Lc - 1) * (int64_t)H * DV + BV) * 4));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, row), ors,
+                                           (int)((((16 * w + (lane >> 2)) * (int64_t)H * DV) + 4 * (lane & 3)) * 4),
+                                           0, 0);
+}
+
+// One chunk: operands `cur` (the next chunk's are already requested).  Returns this wave's
+// output rows; the caller stores them after issuing the following prefetch (loads and stores
+// share one in-order counter, so an early store would delay every later operand wait).
+__device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cur, ChunkFrags& nxt,
+                                               const unsigned char* nrec, bool has_next, int buf, floatx4 (&Sf)[2],
+                                               int w, int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+    const __amdgpu_buffer_rsrc_t nr = make_rsrc(nrec, kRecord);  // a valid record even when !has_next
+    if (has_next) load_group(nxt, nr, 0, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    half8 sb[4], bv[2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) sb[ks] = *reinterpret_cast<const half8*>(&L.S[lr][32 * ks + 8 * lg]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) bv[kb] = *reinterpret_cast<const half8*>(&L.BVs[buf][lr][32 * kb + 8 * lg]);
+    // sequential path: X = W S0
+    floatx4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f}, U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) X = mfma16x16x32(cur.wt[ks], sb[ks], X);
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_next) load_group(nxt, nr, 1, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    // state-independent: U = T beta V, Y = Q+ S0
+    U = mfma16x16x32(cur.tt[0], bv[0], U);
+    if (w >= 2) U = mfma16x16x32(cur.tt[1], bv[1], U);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Y = mfma16x16x32(cur.qp[ks], sb[ks], Y);
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_next) load_group(nxt, nr, 2, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    half4 dh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dh[i] = (_Float16)(U[i] - X[i]);
+    *reinterpret_cast<half4*>(&L.D[lr][16 * w + 4 * lg]) = dh;
+    lds_barrier();
+
+    if (has_next) load_group(nxt, nr, 3, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    half8 db[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) db[kb] = *reinterpret_cast<const half8*>(&L.D[lr][32 * kb + 8 * lg]);
+    // sequential path: S1 = Diag(gamma) S0 + K'^T D for this wave's 32 channels
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const floatx4 gm = *reinterpret_cast<const floatx4*>(&L.gam[buf][16 * (2 * w + t) + 4 * lg]);
+        floatx4 acc = gm * Sf[t];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) acc = mfma16x16x32(cur.kd[t][kb], db[kb], acc);
+        Sf[t] = acc;
+        half4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = (_Float16)acc[i];
+        *reinterpret_cast<half4*>(&L.S[lr][16 * (2 * w + t) + 4 * lg]) = hv;
+    }
+    // O = Q+ S0 + M D
+    floatx4 O = Y;
+    O = mfma16x16x32(cur.mm[0], db[0], O);
+    if (w >= 2) O = mfma16x16x32(cur.mm[1], db[1], O);
+    lds_barrier();
+    return O;
+}
+
+// Waves 0..3 compute.  Wave 4 only warms L2 ahead of them; wave 5 stages beta*V and gamma of
+// the next chunk in LDS.  Outstanding memory operations are counted per wave in issue order,
+// so the warm-up's long-latency loads and the staging loads stay out of the compute waves'
+// counters, and the per-CU address unit sees one wide load where each compute wave would
+// have issued several narrow ones.
+constexpr int kStateThreads = 384;
+
+__global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, SeqMap sm) {
+    __shared__ StateLds L;
+    // wave index, wave-uniform (readfirstlane lets the compiler keep it in a scalar register)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int H = a.H;
 
@@ -471,6 +701,51 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
     const uint16_t* beta = static_cast<const uint16_t*>(a.beta);
     const int64_t sbase = nh * (int64_t)DK * DV + vb * BV;
     const unsigned char* ws = static_cast<const unsigned char*>(a.ws);
+    auto rec_of = [&](int64_t c) { return ws + ((slot0 + c) * H + h) * (int64_t)kRecord; };
+    auto len_of = [&](int64_t c) {
+        const int64_t t = eos - (bos + c * C);
+        return (int)(t < C ? t : C);
+    };
+
+    if (w == 4) {
+        // warm-up wave: touch chunks 1..kWarmAhead now, then one chunk per iteration, and take
+        // part in the compute waves' barriers (one before the loop, two per chunk)
+        auto* dummy = reinterpret_cast<__attribute__((address_space(3))) void*>(
+            reinterpret_cast<uintptr_t>(&L.warm_dummy[0]));
+        for (int64_t c = 1; c <= kWarmAhead && c < nchunks; ++c) warm_l2(rec_of(c), vb, lane, dummy);
+        lds_barrier();
+        for (int64_t c = 0; c < nchunks; ++c) {
+            if (c + 1 + kWarmAhead < nchunks) warm_l2(rec_of(c + 1 + kWarmAhead), vb, lane, dummy);
+            lds_barrier();
+            lds_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS write may outlive the workgroup
+        return;
+    }
+    if (w == 5) {
+        // staging wave: chunk c+1's beta*V and gamma go to LDS between the two barriers of
+        // chunk c (from registers loaded one chunk earlier); loads for chunk c+2 are issued
+        // at the start of chunk c
+        StageRegs ra, rb;
+        if (nchunks > 0) {
+            stage_load(ra, v, beta, rec_of(0), bos, len_of(0), H, h, vb, lane);
+            stage_store(L, 0, ra, lane);
+        }
+        if (nchunks > 1) stage_load(rb, v, beta, rec_of(1), bos + C, len_of(1), H, h, vb, lane);
+        lds_barrier();
+        for (int64_t c = 0; c < nchunks; c += 2) {
+            if (c + 2 < nchunks) stage_load(ra, v, beta, rec_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h, vb, lane);
+            lds_barrier();
+            if (c + 1 < nchunks) stage_store(L, 1, rb, lane);
+            lds_barrier();
+            if (c + 1 >= nchunks) break;
+            if (c + 3 < nchunks) stage_load(rb, v, beta, rec_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h, vb, lane);
+            lds_barrier();
+            if (c + 2 < nchunks) stage_store(L, 0, ra, lane);
+            lds_barrier();
+        }
+        return;
+    }
 
     // fp32 state rows owned by this wave: channel blocks 2w, 2w+1 (accumulator layout)
     floatx4 Sf[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -485,84 +760,32 @@ __global__ __launch_bounds__(256) void state_kernel(PrefillArgs a, SeqMap sm) {
         half4 hv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) hv[i] = (_Float16)Sf[t][i];
-        *reinterpret_cast<half4*>(&S_lds[lr][16 * (2 * w + t) + 4 * lg]) = hv;
+        *reinterpret_cast<half4*>(&L.S[lr][16 * (2 * w + t) + 4 * lg]) = hv;
     }
 
+    // Simple (not unrolled) loop: the copy cur = nxt at the top is the only place that waits on
+    // the operand loads, which were issued a whole chunk earlier; the prefetch of the next chunk
+    // and the previous chunk's output store follow it, so the chunk's compute overlaps both.
+    // (With two register sets alternating in an unrolled loop, the compiler's wait insertion
+    // became conservative at the back-edge and made each chunk wait for its own prefetch.)
     ChunkFrags nxt;
-    if (nchunks > 0) {
-        const int L0 = (int)((eos - bos) < C ? (eos - bos) : C);
-        load_chunk(nxt, ws + (slot0 * H + h) * (int64_t)kRecord, v, beta, bos, L0, H, h, vb, w, lane);
-    }
-    __syncthreads();
+    if (nchunks > 0) load_chunk(nxt, rec_of(0), w, lane);
+    lds_barrier();
 
+    float* obase0 = a.o + (bos * H + h) * (int64_t)DV + vb * BV;
+    const int64_t ostep = (int64_t)C * H * DV;
+    floatx4 Oprev = {0.f, 0.f, 0.f, 0.f};
     for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t t0 = bos + c * C;
-        const int Lc = (int)((eos - t0) < C ? (eos - t0) : C);
+        // every load issued during the previous chunk (this chunk's operands) and the previous
+        // output store are complete here; stating it explicitly keeps the compiler's own wait
+        // placement exact inside the chunk (it cannot track loads carried around the loop)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0), expcnt/lgkmcnt at max
         const ChunkFrags cur = nxt;
-        if (c + 1 < nchunks) {  // prefetch the next chunk's operands (uniform branch)
-            const int64_t t1 = t0 + C;
-            const int L1 = (int)((eos - t1) < C ? (eos - t1) : C);
-            load_chunk(nxt, ws + ((slot0 + c + 1) * H + h) * (int64_t)kRecord, v, beta, t1, L1, H, h, vb, w, lane);
-        }
-
-        // X = K+ S0, Y = Q+ S0 for this wave's 16 tokens
-        floatx4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const half8 sb = *reinterpret_cast<const half8*>(&S_lds[lr][32 * ks + 8 * lg]);
-            X = mfma16x16x32(cur.kp[ks], sb, X);
-            Y = mfma16x16x32(cur.qp[ks], sb, Y);
-        }
-        half4 rh;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = 16 * w + 4 * lg + i < Lc;
-            const float vv = ok ? bf(cur.vr[i]) : 0.f, bb = ok ? bf(cur.br[i]) : 0.f;
-            rh[i] = (_Float16)(bb * (vv - X[i]));
-        }
-        *reinterpret_cast<half4*>(&R_lds[lr][16 * w + 4 * lg]) = rh;
-        __syncthreads();
-
-        // D = T R for this wave's token block (T is zero above its block diagonal)
-        floatx4 Dacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const half8 rb = *reinterpret_cast<const half8*>(&R_lds[lr][32 * kb + 8 * lg]);
-            Dacc = mfma16x16x32(cur.tt[kb], rb, Dacc);
-        }
-        half4 dh;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dh[i] = (_Float16)Dacc[i];
-        *reinterpret_cast<half4*>(&D_lds[lr][16 * w + 4 * lg]) = dh;
-        __syncthreads();
-
-        // O = Q+ S0 + M D
-        half8 db[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) db[kb] = *reinterpret_cast<const half8*>(&D_lds[lr][32 * kb + 8 * lg]);
-        floatx4 O = Y;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) O = mfma16x16x32(cur.mm[kb], db[kb], O);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 16 * w + 4 * lg + i;
-            if (rr < Lc) a.o[((t0 + rr) * H + h) * (int64_t)DV + vb * BV + lr] = O[i];
-        }
-
-        // S1 = Diag(gamma) S0 + K'^T D for this wave's 32 channels
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            floatx4 acc = cur.gam[t] * Sf[t];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) acc = mfma16x16x32(cur.kd[t][kb], db[kb], acc);
-            Sf[t] = acc;
-            half4 hv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = (_Float16)acc[i];
-            *reinterpret_cast<half4*>(&S_lds[lr][16 * (2 * w + t) + 4 * lg]) = hv;
-        }
-        __syncthreads();
+        if (c > 0) store_o(L, Oprev, obase0 + (c - 1) * ostep, len_of(c - 1), H, w, lane);
+        const bool has_next = c + 1 < nchunks;
+        Oprev = state_chunk(L, cur, nxt, rec_of(has_next ? c + 1 : c), has_next, (int)(c & 1), Sf, w, lane);
     }
+    if (nchunks > 0) store_o(L, Oprev, obase0 + (nchunks - 1) * ostep, len_of(nchunks - 1), H, w, lane);
 
     if (a.sT) {
 #pragma unroll
@@ -610,7 +833,7 @@ hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
         if (timed) timed_end(s);
     }
     if (timed) timed_begin(kKernelState, s);
-    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(a.N * a.H * NVB)), dim3(256), 0, s, a, sm);
+    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(a.N * a.H * NVB)), dim3(kStateThreads), 0, s, a, sm);
     hipError_t e = hipGetLastError();
     if (timed) timed_end(s);
     return e;
