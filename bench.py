@@ -33,6 +33,69 @@ PREFILL_FLOP_PER_TOKEN_HEAD = 139264                                    # chunke
 DECODE_BYTES_PER_SEQ_HEAD = 65536 + 65536 + 768 + 512 + 2 + 512         # 132866
 
 
+# HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), scaled by the factors a plain device copy of known size reads for the same counters.
+# Each entry holds the SHA-256 of the kernel source it was measured on; once that source changes
+# the figure no longer describes the kernel and is reported as null.
+# Figures and commands: profiles/hbm_counter_calibration_copy_1GiB.md, profiles/*_T65536_*.md,
+# profiles/decode_N256_*.md.
+COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+_KIB = 1024
+_MFMA_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_mfma.hip"
+_MFMA_SHA = "c665a3bcbf11dd32dfcecd4458e0c8f34b88e95b4debd945aa8e9104ca095629"
+_DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
+_DECODE_SHA = "a23a1dbe696fa71e6128ad9dfa7db5d468c3f0c5b105e8e02607886153214617"
+
+
+def _counted(fetch_kib, write_kib):
+    return round(fetch_kib * _KIB * COUNTER_SCALE["FETCH_SIZE"] + write_kib * _KIB * COUNTER_SCALE["WRITE_SIZE"])
+
+
+# kernel name -> where and on what it was measured, and HBM bytes per launch
+MEASURED_TRAFFIC = {
+    "kda_prep": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
+                 "bytes": _counted(1119160.2, 2113536.0)},
+    "kda_state": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
+                  "bytes": _counted(2703576.2, 1102367.0)},
+    "kda_decode": {"source": _DECODE_SRC, "sha256": _DECODE_SHA, "workload": "decode N=256 H=32",
+                   "bytes": _counted(267370.2, 528811.8)},
+}
+
+
+def source_sha256(rel):
+    import hashlib
+
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_of(kernel, workload=None):
+    """Counter-derived HBM bytes per launch of `kernel`, or None if not measured on this source
+    and workload."""
+    m = MEASURED_TRAFFIC.get(kernel)
+    if not m or (workload is not None and m["workload"] != workload) or source_sha256(m["source"]) != m["sha256"]:
+        return None
+    return m["bytes"]
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB: reads and writes exactly 2^30 bytes per launch."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    log(f"[copy] {n} B read + {n} B written in {dt * 1e3:.3f} ms ({2 * n / dt / 1e9:.1f} GB/s)")
+    print(json.dumps({"copy_bytes": n, "ms": dt * 1e3, "GBps": 2 * n / dt / 1e9}), flush=True)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -49,6 +112,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (the HBM-counter calibration kernel) and exit")
     return ap.parse_args()
 
 
@@ -68,6 +133,12 @@ def slice_err(x, y):
     d = np.abs(x - y).max(axis=(0, 2))
     m = np.abs(y).max(axis=(0, 2))
     return float((d / np.where(m > 0, m, 1)).max())
+
+
+def pass_traffic(workload):
+    """HBM bytes of one prefill pass (both kernels) from the counters, or None."""
+    parts = [traffic_of("kda_prep", workload), traffic_of("kda_state", workload)]
+    return None if any(p is None for p in parts) else sum(parts)
 
 
 def bench_prefill(args, res):
@@ -115,7 +186,7 @@ def bench_prefill(args, res):
     for name, alg in (("kda_prep", PREP_BYTES_PER_TOKEN_HEAD), ("kda_state", STATE_BYTES_PER_TOKEN_HEAD)):
         if name in avg:
             kernels.append({"kernel": name, "launches": len(per[name]), "avg_ms": round(avg[name], 4),
-                            "algorithmic_bytes": alg * th,
+                            "algorithmic_bytes": alg * th, "traffic": traffic_of(name, f"prefill T={T} H={H}"),
                             "achieved_GBps": round(alg * th / (avg[name] * 1e-3) / 1e9, 1)})
     tflops = PREFILL_FLOP_PER_TOKEN_HEAD * th / (path_ms * 1e-3) / 1e12
     res["value"] = T * args.steps / elapsed
@@ -123,7 +194,7 @@ def bench_prefill(args, res):
     res["roofline"] = {
         "bound": "hbm", "kernel": "kda_prep+kda_state (one prefill pass)",
         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": pass_traffic(f"prefill T={T} H={H}"),
         "algorithmic_bytes_per_launch": PREFILL_BYTES_PER_TOKEN_HEAD * th,
         "avg_pass_ms": round(path_ms, 4),
         "mfma_algorithmic_tflops": round(tflops, 1),
@@ -225,7 +296,7 @@ def bench_decode(args, res):
                      "kernel_avg_ms": round(avg, 4)}
     res["roofline_decode"] = {"bound": "hbm", "kernel": "kda_decode", "achieved": round(gbps_kernel, 1),
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps_kernel / HBM_PEAK_GBPS, 4),
-                              "traffic": None, "algorithmic_bytes_per_launch": bytes_step}
+                              "traffic": traffic_of("kda_decode", f"decode N={N} H={H}"), "algorithmic_bytes_per_launch": bytes_step}
     log(f"[decode] {steps / elapsed:.1f} steps/s, {gbps_wall:.1f} GB/s wall, kernel avg {avg * 1e3:.1f} us "
         f"({gbps_kernel:.1f} GB/s)")
 
@@ -269,6 +340,9 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     res = {
         "metric": "KDA prefill tokens/s (d=128, T=64K) + decode steps/s & HBM GB/s at batch 256",
         "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
