@@ -49,6 +49,8 @@ def _run_prefill(w, B, T, with_state):
     ("bf16", 128, 64, 2, 333, True),
     ("bf16", 128, 64, 1, 1, True),      # a single token
     ("bf16", 128, 64, 1, 0, True),      # empty: state passes through
+    ("bf16", 128, 64, 1, 4097, True),   # 65 chunks, the last one token long
+    ("bf16", 128, 64, 2, 8292, True),   # two long sequences, ragged tail
 ])
 def test_prefill_matches_oracle(dtype, d, chunk, B, T, with_state):
     print(f"prefill dtype={dtype} d={d} chunk={chunk} B={B} T={T} state={with_state}", flush=True)
@@ -57,6 +59,25 @@ def test_prefill_matches_oracle(dtype, d, chunk, B, T, with_state):
     if T > 0:
         assert_close(o, oref, TOL[dtype], cu, "o")
     assert_close(s, sref, TOL[dtype], None, "S_T")
+
+
+def test_prefill_in_place_state_and_no_final_state():
+    """In-place state (state_out is state_in) and a call without a final state."""
+    w = _w("bf16", H=2, d=128, chunk=64, seed=41, s0_std=0.02)
+    B, T = 1, 64 * 64 + 64 * 3 + 5
+    print(f"prefill in place B={B} T={T}", flush=True)
+    st, wide = make_inputs(w, B * T)
+    s0 = synth.gen_state(w, B)
+    q, k, v, g, b = upload(w, st, (B, T))
+    S = dev(s0, "f32")
+    o1, s1 = kda.prefill_chunked(q, k, v, g, b, S, state_out=S)
+    o2, s2 = kda.prefill_chunked(q, k, v, g, b, dev(s0, "f32"), final_state=False)
+    torch.cuda.synchronize()
+    assert s1.data_ptr() == S.data_ptr() and s2 is None
+    oref, sref = oracle.recurrence(*wide, np.array([0, T]), s0)
+    assert_close(host(o1).reshape(T, w.H, w.dv), oref, TOL["bf16"], None, "o (in place)")
+    assert_close(host(S), sref, TOL["bf16"], None, "S_T (in place)")
+    assert torch.equal(o1, o2), "outputs must not depend on whether the final state is kept"
 
 
 def test_tiny_workload_exact_shape():
