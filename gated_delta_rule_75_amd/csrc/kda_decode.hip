@@ -10,11 +10,13 @@
 //     o = p + (k . q) delta,  S' = alpha * S + k delta^T,
 // so every state element is read once and written once.
 //
-// Work decomposition: one workgroup per (sequence, head).  A thread owns 4
-// consecutive value columns (one 16-byte vector) of RPT rows; a wave covers
-// whole consecutive rows, so each load/store instruction moves contiguous
-// memory.  The column reductions over key rows go through registers, then a
-// small LDS table.
+// Work decomposition: one workgroup of up to 1024 threads per (sequence, head).  A thread
+// owns 4 consecutive value columns (one 16-byte vector) of RPT rows, and a wave covers whole
+// rows, so every load and store instruction moves contiguous memory.  Small per-thread
+// batches (RPT = 4 at d = 128) keep many independent streams in flight, which is what a
+// read-once/write-once HBM stream needs (measured on MI355X at N = 256, H = 32, d = 128:
+// 1024 threads x 4 rows beat 256 x 16, 512 x 8 and column-sliced workgroups).  The column
+// reductions over key rows go through wave shuffles, then a small LDS table.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -25,97 +27,105 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 template <int DK, int DV>
 struct DecodeShape {
-    static constexpr int kColThreads = DV / 4;                       // threads per row
-    static constexpr int kThreads = (kColThreads * DK) < 256 ? kColThreads * DK : 256;
-    static constexpr int kRowGroups = kThreads / kColThreads;
+    static constexpr int kColThreads = DV / 4;                    // threads per row
+    static constexpr int kRowGroups = DK < 1024 / kColThreads ? DK : 1024 / kColThreads;
+    static constexpr int kThreads = kColThreads * kRowGroups;
+    static constexpr int kWaves = kThreads / 64;
     static constexpr int kRowsPerThread = DK / kRowGroups;
-    static_assert(DV % 4 == 0, "value width must be a multiple of 4");
+    static_assert(DV % 4 == 0 && kThreads % 64 == 0, "shape");
     static_assert(DK % kRowGroups == 0, "rows must split evenly");
+    static_assert(kThreads >= DK, "one thread per key row stages alpha, k, q");
 };
 
 template <int DK, int DV, typename TI>
-__global__ __launch_bounds__(256) void decode_kernel(
+__global__ __launch_bounds__(1024) void decode_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v, const float* __restrict__ g,
     const TI* __restrict__ beta, const float* s_in, float* s_out, float* __restrict__ o) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int CT = Sh::kColThreads, RG = Sh::kRowGroups, RPT = Sh::kRowsPerThread;
+    constexpr int NW = Sh::kWaves;
     const int64_t nh = blockIdx.x;  // sequence * H + head
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c4 = tid % CT;  // owns columns 4*c4 .. 4*c4+3
     const int rg = tid / CT;  // owns rows rg, rg + RG, ...
 
-    __shared__ float s_ak[DK], s_aq[DK], s_k[DK], s_a[DK];
-    __shared__ float s_u[RG][DV], s_p[RG][DV];
-    __shared__ float s_kq;
+    __shared__ floatx4 s_red[NW][2][CT];  // per wave: partial u and p of each column group
+    __shared__ float s_kq[NW];
+    __shared__ float s_a[DK], s_k[DK], s_q[DK];
 
-    const floatx4* Sin = reinterpret_cast<const floatx4*>(s_in + nh * (int64_t)DK * DV);
-    floatx4* Sout = reinterpret_cast<floatx4*>(s_out + nh * (int64_t)DK * DV);
+    const float* Sin = s_in + nh * (int64_t)DK * DV + 4 * c4;
+    float* Sout = s_out + nh * (int64_t)DK * DV + 4 * c4;
 
-    // issue the state loads first: they are the bulk of the traffic
+    // the state loads first: they are the bulk of the traffic
     floatx4 st[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&Sin[(rg + i * RG) * CT + c4]);
-
-    for (int i = tid; i < DK; i += Sh::kThreads) {
-        const float a = expf(g[nh * DK + i]);
-        const float kk = ld_in(k, nh * DK + i);
-        const float qq = ld_in(q, nh * DK + i);
-        s_a[i] = a;
-        s_k[i] = kk;
-        s_ak[i] = a * kk;
-        s_aq[i] = a * qq;
-    }
-    if (tid < 64) {  // k . q, one wave
-        float acc = 0.f;
-        for (int i = tid; i < DK; i += 64) acc += ld_in(k, nh * DK + i) * ld_in(q, nh * DK + i);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        if (tid == 0) s_kq = acc;
+    for (int i = 0; i < RPT; ++i)
+        st[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sin + (int64_t)(rg + i * RG) * DV));
+    // alpha, k, q of every key row, one row per thread, shared through LDS
+    if (tid < DK) {
+        s_a[tid] = expf(g[nh * DK + tid]);
+        s_k[tid] = ld_in(k, nh * DK + tid);
+        s_q[tid] = ld_in(q, nh * DK + tid);
     }
     __syncthreads();
-
-    float u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
+    float a[RPT], kk[RPT], u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + i * RG;
-        const float ak = s_ak[r], aq = s_aq[r];
+        a[i] = s_a[r];
+        kk[i] = s_k[r];
+        const float qq = s_q[r];
+        const float ak = a[i] * kk[i], aq = a[i] * qq;
+        kq += kk[i] * qq;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             u[j] += ak * st[i][j];
             p[j] += aq * st[i][j];
         }
     }
+    // reduce over the row groups of this wave (lanes with the same column group) ...
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        s_u[rg][4 * c4 + j] = u[j];
-        s_p[rg][4 * c4 + j] = p[j];
+    for (int off = CT; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u[j] += __shfl_xor(u[j], off, 64);
+            p[j] += __shfl_xor(p[j], off, 64);
+        }
+        kq += __shfl_xor(kq, off, 64);
+    }
+    // ... then over the waves
+    if (lane < CT) {
+        s_red[wave][0][lane] = floatx4{u[0], u[1], u[2], u[3]};
+        s_red[wave][1][lane] = floatx4{p[0], p[1], p[2], p[3]};
+        if (lane == 0) s_kq[wave] = kq;
     }
     __syncthreads();
+    floatx4 uu = s_red[0][0][c4], pp = s_red[0][1][c4];
+    float kqt = s_kq[0];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) {
+        uu += s_red[wv][0][c4];
+        pp += s_red[wv][1][c4];
+        kqt += s_kq[wv];
+    }
 
     float d[4];
     const float b = ld_in(beta, nh);
-    const float kq = s_kq;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = 4 * c4 + j;
-        float uu = 0.f, pp = 0.f;
+    for (int j = 0; j < 4; ++j) d[j] = b * (ld_in(v, nh * DV + 4 * c4 + j) - uu[j]);
+    if (rg == 0) {
+        floatx4 ov;
 #pragma unroll
-        for (int r = 0; r < RG; ++r) {
-            uu += s_u[r][col];
-            pp += s_p[r][col];
-        }
-        d[j] = b * (ld_in(v, nh * DV + col) - uu);
-        if (rg == 0) o[nh * DV + col] = pp + kq * d[j];
+        for (int j = 0; j < 4; ++j) ov[j] = pp[j] + kqt * d[j];
+        *reinterpret_cast<floatx4*>(o + nh * DV + 4 * c4) = ov;
     }
 
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const int r = rg + i * RG;
-        const float a = s_a[r], kk = s_k[r];
         floatx4 ns;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ns[j] = a * st[i][j] + kk * d[j];
-        __builtin_nontemporal_store(ns, &Sout[r * CT + c4]);
+        for (int j = 0; j < 4; ++j) ns[j] = a[i] * st[i][j] + kk[i] * d[j];
+        __builtin_nontemporal_store(ns, reinterpret_cast<floatx4*>(Sout + (int64_t)(rg + i * RG) * DV));
     }
 }
 
