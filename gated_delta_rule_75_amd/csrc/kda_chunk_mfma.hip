@@ -138,7 +138,7 @@ struct PrepLds {
     union {
         _Float16 kc[3][4][64][8];  // off-diagonal column operands of blocks 0..2, fragment order
         float X[4][16][17];        // per-wave scratch of the inverse
-        _Float16 bk[C][DK + 8];    // Diag(beta) K+ as [token][channel], operand of W
+        _Float16 bkT[DK][C + 8];   // Diag(beta) K+ as [channel][token]: B operand of W
     } u;
     int unsafe;
 };
@@ -187,13 +187,18 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
     const int64_t rowk = ((t0 + (valid ? r : Lc - 1)) * H + h) * (int64_t)DK;
     uint4 kv[4], qv[4];
     float4 gv[8];
+    // g first: the decay scan needs it before anything else
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int c0 = 32 * ks + 8 * lg;
+        gv[2 * ks] = *reinterpret_cast<const float4*>(a.g + rowk + c0);
+        gv[2 * ks + 1] = *reinterpret_cast<const float4*>(a.g + rowk + c0 + 4);
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int c0 = 32 * ks + 8 * lg;
         kv[ks] = *reinterpret_cast<const uint4*>(k + rowk + c0);
         qv[ks] = *reinterpret_cast<const uint4*>(q + rowk + c0);
-        gv[2 * ks] = *reinterpret_cast<const float4*>(a.g + rowk + c0);
-        gv[2 * ks + 1] = *reinterpret_cast<const float4*>(a.g + rowk + c0 + 4);
     }
     // g as floats (zero past the chunk end); k, q stay packed bf16 until used
     float gl[4][8];
@@ -397,10 +402,13 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
     }
     __syncthreads();  // K'^T read out of the union; the inverse scratch is dead
 
-    // ---- W = T Diag(beta) K+ (64 x 128): rows of token block w, all 8 channel blocks
+    // ---- W = T Diag(beta) K+ (64 x 128): rows of token block w, all 8 channel blocks.  The
+    //      right-hand operand is staged transposed ([channel][token]) so that each matrix-core
+    //      B fragment (8 consecutive tokens of one channel) is one 16-byte read.
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-        *reinterpret_cast<half8*>(&L.u.bk[r][32 * ks + 8 * lg]) = BKp[ks];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) L.u.bkT[32 * ks + 8 * lg + i][r] = BKp[ks][i];
     __syncthreads();
     {
         half8 ta[2];  // T rows of block w as matrix-core A operand, k-steps 0..1 (zero above the diagonal)
@@ -414,12 +422,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
         for (int cb = 0; cb < 8; ++cb) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                half8 bb;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) bb[i] = L.u.bk[32 * kb + 8 * lg + i][16 * cb + lr];
-                acc = mfma16x16x32(ta[kb], bb, acc);
-            }
+            for (int kb = 0; kb < 2; ++kb)
+                acc = mfma16x16x32(ta[kb], *reinterpret_cast<const half8*>(&L.u.bkT[16 * cb + lr][32 * kb + 8 * lg]),
+                                   acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) L.o.W[16 * w + 4 * lg + i][16 * cb + lr] = (_Float16)acc[i];
         }
