@@ -10,6 +10,8 @@ Per sequence and head, with state S in R^{d_k x d_v} and alpha = exp(g) per key 
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -88,6 +90,18 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _gate(g, shape_channel, shape_head):
+    """Gate kind from the shape of g: one log-decay per key channel or one per head."""
+    if tuple(g.shape) == tuple(shape_head):
+        return _lib.KDA_GATE_HEAD
+    _check(g, "g", torch.float32, shape_channel)
+    return _lib.KDA_GATE_CHANNEL
+
+
+def _options(gate, every=0, snapshots=None, snapshot_cu=None):
+    return ctypes.byref(_lib.Options(gate, every, _ptr(snapshots), _ptr(snapshot_cu)))
+
+
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None
@@ -97,12 +111,15 @@ def _workspace(nbytes, device, workspace):
 
 
 def prefill_chunked(q, k, v, g, beta, state=None, *, chunk=64, out=None, state_out=None, final_state=True,
-                    workspace=None):
+                    workspace=None, snapshot_every=0, snapshots=None):
     """Chunked prefill of B equal-length sequences.
 
-    q, k [B,T,H,dk], v [B,T,H,dv] (float32 or bfloat16), g [B,T,H,dk] float32 (log alpha),
+    q, k [B,T,H,dk], v [B,T,H,dv] (float32 or bfloat16), g float32 log alpha, either
+    [B,T,H,dk] (one decay per key channel, KDA) or [B,T,H] (one per head, Gated DeltaNet),
     beta [B,T,H] (same dtype as q), state [B,H,dk,dv] float32 or None.
-    Returns (o [B,T,H,dv] float32, S_T [B,H,dk,dv] float32 or None)."""
+    Returns (o [B,T,H,dv] float32, S_T [B,H,dk,dv] float32 or None), plus the state snapshots
+    [B, T // (snapshot_every * chunk), H, dk, dv] when snapshot_every > 0 (the state after
+    every snapshot_every chunks)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -112,9 +129,15 @@ def prefill_chunked(q, k, v, g, beta, state=None, *, chunk=64, out=None, state_o
     _check(q, "q", dt, (B, T, H, dk), dev)
     _check(k, "k", dt, (B, T, H, dk), dev)
     _check(v, "v", dt, (B, T, H, dv), dev)
-    _check(g, "g", torch.float32, (B, T, H, dk), dev)
+    gate = _gate(g, (B, T, H, dk), (B, T, H))
+    _check(g, "g", torch.float32, None, dev)
     _check(beta, "beta", dt, (B, T, H), dev)
     _check(state, "state", torch.float32, (B, H, dk, dv), dev)
+    if snapshot_every > 0:
+        shape = (B, T // (snapshot_every * chunk), H, dk, dv)
+        if snapshots is None:
+            snapshots = torch.empty(shape, dtype=torch.float32, device=dev)
+        _check(snapshots, "snapshots", torch.float32, shape, dev)
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     _check(out, "out", torch.float32, (B, T, H, dv), dev)
@@ -124,18 +147,21 @@ def prefill_chunked(q, k, v, g, beta, state=None, *, chunk=64, out=None, state_o
     ws_bytes = workspace_size(_lib.KDA_OP_PREFILL, B, T, H, dk, dv, dt, chunk)
     ws = _workspace(ws_bytes, dev, workspace)
     L = _lib.load()
-    _lib.check(L.kda_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
-                                     _ptr(state_out), B, T, H, dk, dv, _DT[dt], chunk, _ptr(ws), ws_bytes,
-                                     _stream(dev)))
-    return out, state_out
+    _lib.check(L.kda_prefill_chunked_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
+                                        _ptr(state_out), B, T, H, dk, dv, _DT[dt], chunk, _ptr(ws), ws_bytes,
+                                        _options(gate, snapshot_every, snapshots), _stream(dev)))
+    return (out, state_out, snapshots) if snapshot_every > 0 else (out, state_out)
 
 
 def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=None, state_out=None,
-                   final_state=True, workspace=None):
+                   final_state=True, workspace=None, snapshot_every=0):
     """Append-prefill of N packed segments (token-major [T_total, H, d]) on carried states.
 
-    cu_seqlens: int32 GPU tensor [N+1] (0, ..., T_total).  state [N,H,dk,dv] float32 or None.
-    Returns (o [T_total,H,dv] float32, S_T [N,H,dk,dv] float32 or None)."""
+    cu_seqlens: int32 GPU tensor [N+1] (0, ..., T_total).  g [T_total,H,dk] or [T_total,H] (one
+    decay per head).  state [N,H,dk,dv] float32 or None.
+    Returns (o [T_total,H,dv] float32, S_T [N,H,dk,dv] float32 or None), plus, when
+    snapshot_every > 0, (snapshots [S,H,dk,dv], snapshot_cu int32 [N+1]): the state after every
+    snapshot_every chunks of each segment, segment n at rows snapshot_cu[n] .. snapshot_cu[n+1]-1."""
     T, H, dk = q.shape
     dv = v.shape[-1]
     N = cu_seqlens.numel() - 1
@@ -146,10 +172,19 @@ def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=No
     _check(q, "q", dt, (T, H, dk), dev)
     _check(k, "k", dt, (T, H, dk), dev)
     _check(v, "v", dt, (T, H, dv), dev)
-    _check(g, "g", torch.float32, (T, H, dk), dev)
+    gate = _gate(g, (T, H, dk), (T, H))
+    _check(g, "g", torch.float32, None, dev)
     _check(beta, "beta", dt, (T, H), dev)
     _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
     _check(state, "state", torch.float32, (N, H, dk, dv), dev)
+    snapshots = snapshot_cu = None
+    if snapshot_every > 0:
+        # per-segment snapshot counts from the segment lengths (a host copy of cu_seqlens)
+        counts = torch.diff(cu_seqlens.to("cpu", torch.int64)) // (snapshot_every * chunk)
+        snapshot_cu = torch.zeros(N + 1, dtype=torch.int32)
+        snapshot_cu[1:] = torch.cumsum(counts, 0)
+        snapshot_cu = snapshot_cu.to(dev)
+        snapshots = torch.empty((int(counts.sum()), H, dk, dv), dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
     _check(out, "out", torch.float32, (T, H, dv), dev)
@@ -159,14 +194,18 @@ def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=No
     ws_bytes = workspace_size(_lib.KDA_OP_APPEND, N, T, H, dk, dv, dt, chunk)
     ws = _workspace(ws_bytes, dev, workspace)
     L = _lib.load()
-    _lib.check(L.kda_append_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
-                                    _ptr(state), _ptr(out), _ptr(state_out), H, dk, dv, _DT[dt], chunk, _ptr(ws),
-                                    ws_bytes, _stream(dev)))
+    _lib.check(L.kda_append_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+                                       _ptr(state), _ptr(out), _ptr(state_out), H, dk, dv, _DT[dt], chunk,
+                                       _ptr(ws), ws_bytes, _options(gate, snapshot_every, snapshots, snapshot_cu),
+                                       _stream(dev)))
+    if snapshot_every > 0:
+        return out, state_out, snapshots, snapshot_cu
     return out, state_out
 
 
 def decode_step(q, k, v, g, beta, state, *, out=None, state_out=None):
-    """One decode step for N sequences: q, k, g [N,H,dk], v [N,H,dv], beta [N,H], state [N,H,dk,dv].
+    """One decode step for N sequences: q, k [N,H,dk], g [N,H,dk] or [N,H] (one decay per head),
+    v [N,H,dv], beta [N,H], state [N,H,dk,dv].
 
     The state is updated in place unless ``state_out`` is given.  Returns o [N,H,dv] float32."""
     N, H, dk = q.shape
@@ -178,7 +217,8 @@ def decode_step(q, k, v, g, beta, state, *, out=None, state_out=None):
     _check(q, "q", dt, (N, H, dk), dev)
     _check(k, "k", dt, (N, H, dk), dev)
     _check(v, "v", dt, (N, H, dv), dev)
-    _check(g, "g", torch.float32, (N, H, dk), dev)
+    gate = _gate(g, (N, H, dk), (N, H))
+    _check(g, "g", torch.float32, None, dev)
     _check(beta, "beta", dt, (N, H), dev)
     _check(state, "state", torch.float32, (N, H, dk, dv), dev)
     if state_out is None:
@@ -188,6 +228,7 @@ def decode_step(q, k, v, g, beta, state, *, out=None, state_out=None):
         out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     _check(out, "out", torch.float32, (N, H, dv), dev)
     L = _lib.load()
-    _lib.check(L.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(state_out),
-                                 _ptr(out), N, H, dk, dv, _DT[dt], _stream(dev)))
+    _lib.check(L.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                    _ptr(state_out), _ptr(out), N, H, dk, dv, _DT[dt], _options(gate),
+                                    _stream(dev)))
     return out

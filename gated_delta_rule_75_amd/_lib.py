@@ -17,14 +17,21 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_MISALIGNED = 0, -1, -2
 KDA_ERR_ALIAS, KDA_ERR_WORKSPACE, KDA_ERR_HIP = -4, -5, -6
 KDA_F32, KDA_BF16 = 0, 1
 KDA_OP_PREFILL, KDA_OP_APPEND, KDA_OP_DECODE = 0, 1, 2
+KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_prefill_chunked", "kda_append_prefill", "kda_decode_step", "kda_workspace_size",
-           "kda_is_supported", "kda_status_string", "kda_last_error", "kda_version", "kda_timing_begin",
-           "kda_timing_end")
+EXPORTS = ("kda_prefill_chunked", "kda_append_prefill", "kda_decode_step", "kda_prefill_chunked_ex",
+           "kda_append_prefill_ex", "kda_decode_step_ex", "kda_workspace_size", "kda_is_supported",
+           "kda_status_string", "kda_last_error", "kda_version", "kda_timing_begin", "kda_timing_end")
 KERNEL_NAMES = {1: "kda_prep", 2: "kda_state", 3: "kda_chunk_f32", 4: "kda_decode"}
 
 _LIB = None
+
+
+class Options(ctypes.Structure):
+    """struct kda_options"""
+    _fields_ = [("gate", ctypes.c_int32), ("snapshot_every", ctypes.c_int32), ("snapshots", ctypes.c_void_p),
+                ("snapshot_cu", ctypes.c_void_p)]
 
 
 class KdaError(RuntimeError):
@@ -48,6 +55,13 @@ def load():
                                      vp]
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    op = ctypes.POINTER(Options)
+    L.kda_prefill_chunked_ex.restype = ctypes.c_int
+    L.kda_prefill_chunked_ex.argtypes = L.kda_prefill_chunked.argtypes[:-1] + [op, vp]
+    L.kda_append_prefill_ex.restype = ctypes.c_int
+    L.kda_append_prefill_ex.argtypes = L.kda_append_prefill.argtypes[:-1] + [op, vp]
+    L.kda_decode_step_ex.restype = ctypes.c_int
+    L.kda_decode_step_ex.argtypes = L.kda_decode_step.argtypes[:-1] + [op, vp]
     L.kda_workspace_size.restype = sz
     L.kda_workspace_size.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32]
     L.kda_is_supported.restype = ctypes.c_int

@@ -136,17 +136,48 @@ int run_prefill(const kda::PrefillArgs& a, int32_t dtype, hipStream_t s, const c
 // Alignment: q, k and g are read with 16-byte vector loads by the prefill kernels
 // (qkg_align = 16); every other tensor only needs its element alignment.
 int validate_common(const void* q, const void* k, const void* v, const float* g, const void* beta, int64_t tokens,
-                    int32_t H, int32_t dk, int32_t dv, int32_t dtype, size_t qkg_align) {
+                    int32_t H, int32_t dk, int32_t dv, int32_t dtype, size_t qkg_align, bool gate_head) {
     if (H <= 0 || dk <= 0 || dv <= 0) return fail(KDA_ERR_INVALID_ARG, "H, d_k, d_v must be positive");
     if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "dtype must be KDA_F32 or KDA_BF16");
     if (tokens > 0 && (!q || !k || !v || !g || !beta))
         return fail(KDA_ERR_INVALID_ARG, "q, k, v, g and beta are required");
     const size_t esz = dtype == KDA_BF16 ? 2 : 4;
     const size_t qa = qkg_align > esz ? qkg_align : esz;
-    if (!aligned_to(q, qa) || !aligned_to(k, qa) || !aligned_to(g, qkg_align > 4 ? qkg_align : 4))
-        return fail(KDA_ERR_MISALIGNED, "q, k and g must be %zu-byte aligned", qa);
+    if (!aligned_to(q, qa) || !aligned_to(k, qa) || !aligned_to(g, gate_head || qkg_align < 4 ? 4 : qkg_align))
+        return fail(KDA_ERR_MISALIGNED, "q and k must be %zu-byte aligned, g %zu-byte aligned", qa,
+                    gate_head || qkg_align < 4 ? (size_t)4 : qkg_align);
     if (!aligned_to(v, esz) || !aligned_to(beta, esz))
         return fail(KDA_ERR_MISALIGNED, "v and beta must be aligned to their element size");
+    return KDA_OK;
+}
+
+// Options of the extended calls (NULL: defaults).
+struct Opts {
+    bool gate_head = false;
+    int every = 0;
+    float* snaps = nullptr;
+    const int32_t* snap_cu = nullptr;
+};
+
+int read_options(const kda_options* o, int op, const char* name, Opts& out) {
+    out = Opts{};
+    if (!o) return KDA_OK;
+    if (o->gate != KDA_GATE_CHANNEL && o->gate != KDA_GATE_HEAD)
+        return fail(KDA_ERR_INVALID_ARG, "%s: options.gate must be KDA_GATE_CHANNEL or KDA_GATE_HEAD", name);
+    if (o->snapshot_every < 0) return fail(KDA_ERR_INVALID_ARG, "%s: options.snapshot_every must be >= 0", name);
+    if (op == KDA_OP_DECODE && (o->snapshot_every || o->snapshots || o->snapshot_cu))
+        return fail(KDA_ERR_INVALID_ARG, "%s: a decode step takes no snapshots", name);
+    if (o->snapshot_every > 0) {
+        if (!o->snapshots) return fail(KDA_ERR_INVALID_ARG, "%s: options.snapshots is required", name);
+        if (op == KDA_OP_APPEND && !o->snapshot_cu)
+            return fail(KDA_ERR_INVALID_ARG, "%s: options.snapshot_cu is required", name);
+        if (!aligned_to(o->snapshots, 4) || !aligned_to(o->snapshot_cu, 4))
+            return fail(KDA_ERR_MISALIGNED, "%s: snapshots and snapshot_cu must be 4-byte aligned", name);
+    }
+    out.gate_head = o->gate == KDA_GATE_HEAD;
+    out.every = o->snapshot_every;
+    out.snaps = o->snapshot_every > 0 ? o->snapshots : nullptr;
+    out.snap_cu = o->snapshot_every > 0 ? o->snapshot_cu : nullptr;
     return KDA_OK;
 }
 
@@ -213,13 +244,15 @@ size_t kda_workspace_size(int32_t op, int64_t B_or_N, int64_t T, int32_t H, int3
     return ws_size(op, B_or_N, T, H, d_k, d_v, dtype, chunk);
 }
 
-int kda_prefill_chunked(const void* q, const void* k, const void* v, const float* g, const void* beta,
-                        const float* state_in, float* out, float* state_out, int64_t B, int64_t T, int32_t H,
-                        int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk, void* workspace,
-                        size_t workspace_bytes, void* hip_stream) {
+int kda_prefill_chunked_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                           const float* state_in, float* out, float* state_out, int64_t B, int64_t T, int32_t H,
+                           int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk, void* workspace,
+                           size_t workspace_bytes, const kda_options* options, void* hip_stream) {
     static const char* name = "kda_prefill_chunked";
+    Opts op;
+    if (int rc = read_options(options, KDA_OP_PREFILL, name, op)) return rc;
     if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARG, "%s: B and T must be >= 0", name);
-    if (int rc = validate_common(q, k, v, g, beta, B * T, H, d_k, d_v, dtype, 16)) return rc;
+    if (int rc = validate_common(q, k, v, g, beta, B * T, H, d_k, d_v, dtype, 16, op.gate_head)) return rc;
     if (!prefill_path(dtype, d_k, d_v, chunk))
         return fail(KDA_ERR_UNSUPPORTED, "%s: dtype=%d d_k=%d d_v=%d chunk=%d not implemented", name, dtype, d_k, d_v,
                     chunk);
@@ -231,12 +264,15 @@ int kda_prefill_chunked(const void* q, const void* k, const void* v, const float
     const size_t sbytes = (size_t)B * H * d_k * d_v * 4;
     const Span sin{state_in, state_in ? sbytes : 0}, sout{state_out, state_out ? sbytes : 0};
     const Span o{out, tokens * H * d_v * 4};
+    const int64_t snap_per_seq = op.every > 0 ? T / ((int64_t)op.every * chunk) : 0;
+    const Span snp{op.snaps, (size_t)(B * snap_per_seq) * H * d_k * d_v * 4};
     const Span ins[] = {{q, tokens * H * d_k * esz}, {k, tokens * H * d_k * esz}, {v, tokens * H * d_v * esz},
-                        {g, tokens * H * d_k * 4},   {beta, tokens * H * esz},    sin};
+                        {g, tokens * H * (op.gate_head ? 1 : d_k) * 4}, {beta, tokens * H * esz}, sin};
     for (const Span& in : ins)
-        if (overlap(o, in) || (overlap(sout, in) && in.p != state_in))
-            return fail(KDA_ERR_ALIAS, "%s: out/state_out overlap an input", name);
-    if (overlap(o, sout)) return fail(KDA_ERR_ALIAS, "%s: out overlaps state_out", name);
+        if (overlap(o, in) || (overlap(sout, in) && in.p != state_in) || overlap(snp, in))
+            return fail(KDA_ERR_ALIAS, "%s: out/state_out/snapshots overlap an input", name);
+    if (overlap(o, sout) || overlap(snp, o) || overlap(snp, sout))
+        return fail(KDA_ERR_ALIAS, "%s: out, state_out and snapshots overlap", name);
     if (overlap(sin, sout) && state_in != state_out)
         return fail(KDA_ERR_ALIAS, "%s: state_out partially overlaps state_in", name);
     const size_t need = ws_size(KDA_OP_PREFILL, B, T, H, d_k, d_v, dtype, chunk);
@@ -249,17 +285,29 @@ int kda_prefill_chunked(const void* q, const void* k, const void* v, const float
     a.cu = nullptr; a.N = B; a.T_fixed = T; a.T_total = B * T;
     a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.bf16 = dtype == KDA_BF16;
     a.ws = workspace; a.ws_bytes = workspace_bytes;
+    a.gate_head = op.gate_head; a.snap = snap_per_seq > 0 ? op.snaps : nullptr; a.snap_every = op.every;
+    a.snap_cu = nullptr; a.snap_per_seq = snap_per_seq;
     return run_prefill(a, dtype, static_cast<hipStream_t>(hip_stream), name);
 }
 
-int kda_append_prefill(const void* q, const void* k, const void* v, const float* g, const void* beta,
-                       const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in, float* out,
-                       float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
-                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+int kda_prefill_chunked(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                        const float* state_in, float* out, float* state_out, int64_t B, int64_t T, int32_t H,
+                        int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk, void* workspace,
+                        size_t workspace_bytes, void* hip_stream) {
+    return kda_prefill_chunked_ex(q, k, v, g, beta, state_in, out, state_out, B, T, H, d_k, d_v, dtype, chunk,
+                                  workspace, workspace_bytes, nullptr, hip_stream);
+}
+
+int kda_append_prefill_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                          const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in, float* out,
+                          float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                          void* workspace, size_t workspace_bytes, const kda_options* options, void* hip_stream) {
     static const char* name = "kda_append_prefill";
+    Opts op;
+    if (int rc = read_options(options, KDA_OP_APPEND, name, op)) return rc;
     if (N < 0 || T_total < 0) return fail(KDA_ERR_INVALID_ARG, "%s: N and T_total must be >= 0", name);
     if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens is required", name);
-    if (int rc = validate_common(q, k, v, g, beta, T_total, H, d_k, d_v, dtype, 16)) return rc;
+    if (int rc = validate_common(q, k, v, g, beta, T_total, H, d_k, d_v, dtype, 16, op.gate_head)) return rc;
     if (!prefill_path(dtype, d_k, d_v, chunk))
         return fail(KDA_ERR_UNSUPPORTED, "%s: dtype=%d d_k=%d d_v=%d chunk=%d not implemented", name, dtype, d_k, d_v,
                     chunk);
@@ -271,13 +319,16 @@ int kda_append_prefill(const void* q, const void* k, const void* v, const float*
     const size_t sbytes = (size_t)N * H * d_k * d_v * 4;
     const Span sin{state_in, state_in ? sbytes : 0}, sout{state_out, state_out ? sbytes : 0};
     const Span o{out, tokens * H * d_v * 4};
+    // the snapshot rows are on the device (snapshot_cu); only the first row is checked here
+    const Span snp{op.snaps, (size_t)H * d_k * d_v * 4};
     const Span ins[] = {{q, tokens * H * d_k * esz}, {k, tokens * H * d_k * esz}, {v, tokens * H * d_v * esz},
-                        {g, tokens * H * d_k * 4},   {beta, tokens * H * esz},    {cu_seqlens, (size_t)(N + 1) * 4},
-                        sin};
+                        {g, tokens * H * (op.gate_head ? 1 : d_k) * 4}, {beta, tokens * H * esz},
+                        {cu_seqlens, (size_t)(N + 1) * 4}, {op.snap_cu, op.snap_cu ? (size_t)(N + 1) * 4 : 0}, sin};
     for (const Span& in : ins)
-        if (overlap(o, in) || (overlap(sout, in) && in.p != state_in))
-            return fail(KDA_ERR_ALIAS, "%s: out/state_out overlap an input", name);
-    if (overlap(o, sout)) return fail(KDA_ERR_ALIAS, "%s: out overlaps state_out", name);
+        if (overlap(o, in) || (overlap(sout, in) && in.p != state_in) || overlap(snp, in))
+            return fail(KDA_ERR_ALIAS, "%s: out/state_out/snapshots overlap an input", name);
+    if (overlap(o, sout) || overlap(snp, o) || overlap(snp, sout))
+        return fail(KDA_ERR_ALIAS, "%s: out, state_out and snapshots overlap", name);
     if (overlap(sin, sout) && state_in != state_out)
         return fail(KDA_ERR_ALIAS, "%s: state_out partially overlaps state_in", name);
     const size_t need = ws_size(KDA_OP_APPEND, N, T_total, H, d_k, d_v, dtype, chunk);
@@ -290,15 +341,27 @@ int kda_append_prefill(const void* q, const void* k, const void* v, const float*
     a.cu = cu_seqlens; a.N = N; a.T_fixed = 0; a.T_total = T_total;
     a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.bf16 = dtype == KDA_BF16;
     a.ws = workspace; a.ws_bytes = workspace_bytes;
+    a.gate_head = op.gate_head; a.snap = op.snaps; a.snap_every = op.every; a.snap_cu = op.snap_cu;
+    a.snap_per_seq = 0;
     return run_prefill(a, dtype, static_cast<hipStream_t>(hip_stream), name);
 }
 
-int kda_decode_step(const void* q, const void* k, const void* v, const float* g, const void* beta,
-                    const float* state_in, float* state_out, float* out, int32_t N, int32_t H, int32_t d_k,
-                    int32_t d_v, int32_t dtype, void* hip_stream) {
+int kda_append_prefill(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                       const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in, float* out,
+                       float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return kda_append_prefill_ex(q, k, v, g, beta, cu_seqlens, N, T_total, state_in, out, state_out, H, d_k, d_v,
+                                 dtype, chunk, workspace, workspace_bytes, nullptr, hip_stream);
+}
+
+int kda_decode_step_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                       const float* state_in, float* state_out, float* out, int32_t N, int32_t H, int32_t d_k,
+                       int32_t d_v, int32_t dtype, const kda_options* options, void* hip_stream) {
     static const char* name = "kda_decode_step";
+    Opts op;
+    if (int rc = read_options(options, KDA_OP_DECODE, name, op)) return rc;
     if (N < 0) return fail(KDA_ERR_INVALID_ARG, "%s: N must be >= 0", name);
-    if (int rc = validate_common(q, k, v, g, beta, N, H, d_k, d_v, dtype, 1)) return rc;
+    if (int rc = validate_common(q, k, v, g, beta, N, H, d_k, d_v, dtype, 1, op.gate_head)) return rc;
     if (!kda::decode_supported(d_k, d_v))
         return fail(KDA_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d not implemented", name, d_k, d_v);
     if (N > 0 && (!state_in || !state_out || !out))
@@ -309,7 +372,7 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* g,
     const size_t sbytes = (size_t)N * H * d_k * d_v * 4;
     const Span sin{state_in, sbytes}, sout{state_out, sbytes}, o{out, (size_t)N * H * d_v * 4};
     const Span ins[] = {{q, (size_t)N * H * d_k * esz}, {k, (size_t)N * H * d_k * esz}, {v, (size_t)N * H * d_v * esz},
-                        {g, (size_t)N * H * d_k * 4},   {beta, (size_t)N * H * esz},    sin};
+                        {g, (size_t)N * H * (op.gate_head ? 1 : d_k) * 4}, {beta, (size_t)N * H * esz}, sin};
     for (const Span& in : ins)
         if (overlap(o, in) || (overlap(sout, in) && in.p != state_in))
             return fail(KDA_ERR_ALIAS, "%s: out/state_out overlap an input", name);
@@ -320,9 +383,16 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* g,
     kda::DecodeArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s_in = state_in; a.s_out = state_out; a.o = out;
-    a.N = N; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16;
+    a.N = N; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16; a.gate_head = op.gate_head;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     return check_hip(kda::launch_decode(a, s), s, name);
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                    const float* state_in, float* state_out, float* out, int32_t N, int32_t H, int32_t d_k,
+                    int32_t d_v, int32_t dtype, void* hip_stream) {
+    return kda_decode_step_ex(q, k, v, g, beta, state_in, state_out, out, N, H, d_k, d_v, dtype, nullptr,
+                              hip_stream);
 }
 
 }  // extern "C"

@@ -19,7 +19,8 @@
 // are used as given and every product is fp32 FMA on the vector ALUs.
 //
 // One workgroup per (sequence, head, block of 16 value columns); value columns
-// never interact, so blocks of them are independent chains.
+// never interact, so blocks of them are independent chains.  With one forget gate
+// per head (Gated DeltaNet) every key channel takes the same log-decay.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(PrefillArgs a) {
         for (int i = tid; i < DK; i += kThreads) {
             float acc = 0.f;
             for (int r = 0; r < C; ++r) {
-                if (r < L) acc += a.g[((t0 + r) * H + h) * (int64_t)DK + i];
+                if (r < L) acc += a.gate_head ? a.g[(t0 + r) * H + h] : a.g[((t0 + r) * H + h) * (int64_t)DK + i];
                 sG[r * DK + i] = acc;
             }
         }
@@ -165,6 +166,12 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(PrefillArgs a) {
             float acc = expf(gl) * sS[e];
             for (int s = 0; s < L; ++s) acc += sk[s * DK + c] * expf(gl - sG[s * DK + c]) * sD[s * kBV + j];
             sS[e] = acc;
+            // state snapshot after every snap_every full chunks (this thread's own elements)
+            const int64_t chunks_done = (t0 - bos) / C + 1;
+            if (a.snap && L == C && chunks_done % a.snap_every == 0) {
+                const int64_t row = (a.snap_cu ? (int64_t)a.snap_cu[n] : n * a.snap_per_seq) + chunks_done / a.snap_every - 1;
+                a.snap[((row * H + h) * DK + c) * (int64_t)DV + vb * kBV + j] = acc;
+            }
         }
     }
     __syncthreads();

@@ -187,12 +187,19 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
     const int64_t rowk = ((t0 + (valid ? r : Lc - 1)) * H + h) * (int64_t)DK;
     uint4 kv[4], qv[4];
     float4 gv[8];
-    // g first: the decay scan needs it before anything else
+    // g first: the decay scan needs it before anything else (with one gate per head, the
+    // token's single log-decay on every channel)
+    if (a.gate_head) {
+        const float gs = a.g[(t0 + (valid ? r : Lc - 1)) * H + h];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int c0 = 32 * ks + 8 * lg;
-        gv[2 * ks] = *reinterpret_cast<const float4*>(a.g + rowk + c0);
-        gv[2 * ks + 1] = *reinterpret_cast<const float4*>(a.g + rowk + c0 + 4);
+        for (int j = 0; j < 8; ++j) gv[j] = make_float4(gs, gs, gs, gs);
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int c0 = 32 * ks + 8 * lg;
+            gv[2 * ks] = *reinterpret_cast<const float4*>(a.g + rowk + c0);
+            gv[2 * ks + 1] = *reinterpret_cast<const float4*>(a.g + rowk + c0 + 4);
+        }
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -789,6 +796,15 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
         if (c > 0) store_o(L, Oprev, obase0 + (c - 1) * ostep, len_of(c - 1), H, w, lane);
         const bool has_next = c + 1 < nchunks;
         Oprev = state_chunk(L, cur, nxt, rec_of(has_next ? c + 1 : c), has_next, (int)(c & 1), Sf, w, lane);
+        // state snapshot after every snap_every full chunks
+        if (a.snap && (c + 1) % a.snap_every == 0 && len_of(c) == C) {
+            const int64_t row = (a.snap_cu ? (int64_t)a.snap_cu[n] : n * a.snap_per_seq) + (c + 1) / a.snap_every - 1;
+            float* dst = a.snap + (row * H + h) * (int64_t)DK * DV + vb * BV;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * (2 * w + t) + 4 * lg + i) * DV + lr] = Sf[t][i];
+        }
     }
     if (nchunks > 0) store_o(L, Oprev, obase0 + (nchunks - 1) * ostep, len_of(nchunks - 1), H, w, lane);
 

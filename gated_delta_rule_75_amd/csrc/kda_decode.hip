@@ -10,6 +10,8 @@
 //     o = p + (k . q) delta,  S' = alpha * S + k delta^T,
 // so every state element is read once and written once.
 //
+// With one forget gate per head (Gated DeltaNet) alpha is the same for every key row.
+//
 // Work decomposition: one workgroup of up to 1024 threads per (sequence, head).  A thread
 // owns 4 consecutive value columns (one 16-byte vector) of RPT rows, and a wave covers whole
 // rows, so every load and store instruction moves contiguous memory.  Small per-thread
@@ -40,7 +42,7 @@ struct DecodeShape {
 template <int DK, int DV, typename TI>
 __global__ __launch_bounds__(1024) void decode_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v, const float* __restrict__ g,
-    const TI* __restrict__ beta, const float* s_in, float* s_out, float* __restrict__ o) {
+    const TI* __restrict__ beta, const float* s_in, float* s_out, float* __restrict__ o, int gate_head) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int CT = Sh::kColThreads, RG = Sh::kRowGroups, RPT = Sh::kRowsPerThread;
     constexpr int NW = Sh::kWaves;
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(
         st[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sin + (int64_t)(rg + i * RG) * DV));
     // alpha, k, q of every key row, one row per thread, shared through LDS
     if (tid < DK) {
-        s_a[tid] = expf(g[nh * DK + tid]);
+        s_a[tid] = expf(gate_head ? g[nh] : g[nh * DK + tid]);  // one decay per head, or per key channel
         s_k[tid] = ld_in(k, nh * DK + tid);
         s_q[tid] = ld_in(q, nh * DK + tid);
     }
@@ -139,12 +141,12 @@ hipError_t launch_shape(const DecodeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((decode_kernel<DK, DV, uint16_t>), grid, dim3(Sh::kThreads), 0, s,
                            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                            static_cast<const uint16_t*>(a.v), a.g, static_cast<const uint16_t*>(a.beta), a.s_in,
-                           a.s_out, a.o);
+                           a.s_out, a.o, a.gate_head);
     } else {
         hipLaunchKernelGGL((decode_kernel<DK, DV, float>), grid, dim3(Sh::kThreads), 0, s,
                            static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                            static_cast<const float*>(a.v), a.g, static_cast<const float*>(a.beta), a.s_in,
-                           a.s_out, a.o);
+                           a.s_out, a.o, a.gate_head);
     }
     hipError_t e = hipGetLastError();
     if (timed) timed_end(s);

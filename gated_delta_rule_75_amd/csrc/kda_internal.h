@@ -33,6 +33,11 @@ struct PrefillArgs {
     int bf16;  // storage type of q, k, v, beta
     void* ws;
     size_t ws_bytes;
+    int gate_head;          // g is [T_total, H] (one decay per token and head) instead of [T_total, H, dk]
+    float* snap;            // state snapshots, or nullptr
+    int snap_every;         // chunks between snapshots
+    const int32_t* snap_cu; // varlen: first snapshot row of each sequence (device)
+    int64_t snap_per_seq;   // fixed length: snapshots per sequence
 };
 
 struct DecodeArgs {
@@ -47,6 +52,7 @@ struct DecodeArgs {
     int64_t N;
     int H, dk, dv;
     int bf16;
+    int gate_head;  // g is [N, H] (one decay per sequence and head) instead of [N, H, dk]
 };
 
 // generic fp32-arithmetic chunked kernel (any supported shape, either storage type)

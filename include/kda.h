@@ -116,6 +116,60 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* g,
                     const float* state_in, float* state_out, float* out, int32_t N, int32_t H,
                     int32_t d_k, int32_t d_v, int32_t dtype, void* hip_stream);
 
+/*
+ * Extended calls: the same operations with options.
+ *
+ * Gate kind ("Kimi K3, explained", "How Kimi Delta Attention works, step by
+ * step" and the comparison with Gated DeltaNet, whose forget gate is one
+ * scalar per head and token rather than one value per key channel):
+ *   KDA_GATE_CHANNEL  g has one log-decay per key channel: [..., H, d_k]
+ *                     (KDA; the plain calls always use this).
+ *   KDA_GATE_HEAD     g has one log-decay per token and head: [..., H], and
+ *                     alpha_t = exp(g_t) multiplies every key channel (Gated
+ *                     DeltaNet; g = 0 gives the plain delta rule).
+ *
+ * State snapshots ("Kimi K3 changed the memory math for agentic AI": keeping
+ * the fixed-size state at checkpoints of a long context so that a session can
+ * resume from one).  With snapshot_every = E > 0 (prefill and append only),
+ * the state after every E * chunk tokens of a sequence is written, counted
+ * from the start of the call's tokens for that sequence: snapshot m (m = 0,
+ * 1, ...) is the state after the first (m + 1) * E * chunk tokens, for every
+ * such count that does not exceed the sequence's length.  The final state
+ * still goes to state_out.
+ *   prefill: snapshots [B, T / (E * chunk), H, d_k, d_v] float (integer division)
+ *   append:  snapshots [snapshot_cu[N], H, d_k, d_v] float, sequence n at rows
+ *            snapshot_cu[n] .. snapshot_cu[n+1]-1; snapshot_cu is a DEVICE
+ *            int32 [N + 1] with snapshot_cu[0] = 0 and snapshot_cu[n+1] -
+ *            snapshot_cu[n] = (cu_seqlens[n+1] - cu_seqlens[n]) / (E * chunk)
+ *            (a caller contract, not checked on the device).
+ * snapshots must be 4-byte aligned and overlap no other argument.  A NULL
+ * options pointer means { KDA_GATE_CHANNEL, 0, NULL, NULL }.
+ */
+typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1 } kda_gate;
+
+typedef struct kda_options {
+    int32_t gate;               /* kda_gate */
+    int32_t snapshot_every;     /* chunks between state snapshots; 0 = none (must be 0 for decode) */
+    float* snapshots;           /* see above; NULL when snapshot_every = 0 */
+    const int32_t* snapshot_cu; /* append only; NULL otherwise */
+} kda_options;
+
+int kda_prefill_chunked_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                           const float* state_in, float* out, float* state_out, int64_t B, int64_t T,
+                           int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                           void* workspace, size_t workspace_bytes, const kda_options* options,
+                           void* hip_stream);
+
+int kda_append_prefill_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                          const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in,
+                          float* out, float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                          int32_t chunk, void* workspace, size_t workspace_bytes, const kda_options* options,
+                          void* hip_stream);
+
+int kda_decode_step_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                       const float* state_in, float* state_out, float* out, int32_t N, int32_t H,
+                       int32_t d_k, int32_t d_v, int32_t dtype, const kda_options* options, void* hip_stream);
+
 /* Workspace bytes an op needs (B_or_N sequences, T tokens per sequence for
  * KDA_OP_PREFILL or T_total for KDA_OP_APPEND).  0 for KDA_OP_DECODE.
  * Returns (size_t)-1 for an unsupported or invalid combination. */

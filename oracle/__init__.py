@@ -58,6 +58,8 @@ def _lib():
         L.kda_oracle_recurrence.restype = ctypes.c_int
         L.kda_oracle_recurrence.argtypes = [dp, dp, dp, dp, dp, ip, i64, dp, dp, dp, i64, i64, i64, i64,
                                             ctypes.c_int]
+        L.kda_oracle_recurrence_snap.restype = ctypes.c_int
+        L.kda_oracle_recurrence_snap.argtypes = L.kda_oracle_recurrence.argtypes + [i64, ip, dp]
         L.kda_oracle_chunked.restype = ctypes.c_int
         L.kda_oracle_chunked.argtypes = [dp, dp, dp, dp, dp, ip, i64, dp, dp, dp, i64, i64, i64, i64,
                                          ctypes.c_int]
@@ -88,6 +90,10 @@ def _prep(q, k, v, g, beta, cu, s0):
     q, k, v, g, beta, s0 = map(_f64, (q, k, v, g, beta, s0))
     T, H, dk = q.shape
     dv = v.shape[2]
+    if g.shape == (T, H):
+        # one log-decay per token and head (Gated DeltaNet): Diag(alpha_t) = alpha_t * I, the
+        # same decay on every key channel
+        g = np.ascontiguousarray(np.broadcast_to(g[:, :, None], (T, H, dk)))
     if k.shape != (T, H, dk) or g.shape != (T, H, dk) or v.shape[:2] != (T, H) or beta.shape != (T, H):
         raise ValueError("shape mismatch: q,k,g [T,H,dk], v [T,H,dv], beta [T,H]")
     cu = np.asarray([0, T] if cu is None else cu, dtype=np.int64)
@@ -99,18 +105,26 @@ def _prep(q, k, v, g, beta, cu, s0):
     return q, k, v, g, beta, np.ascontiguousarray(cu), s0, T, H, dk, dv, N
 
 
-def recurrence(q, k, v, g, beta, cu=None, s0=None, *, threads=None, vcols=0):
+def recurrence(q, k, v, g, beta, cu=None, s0=None, *, threads=None, vcols=0, snapshot_every=0):
     """Token-by-token fp64 recurrence.  Inputs [T,H,d] (packed sequences per ``cu``),
-    g = log(alpha) [T,H,dk], beta [T,H], s0 [N,H,dk,dv] or None.  Returns (o, sT)."""
+    g = log(alpha) [T,H,dk] (one decay per key channel) or [T,H] (one per head), beta [T,H],
+    s0 [N,H,dk,dv] or None.  Returns (o, sT), plus the state snapshots [S,H,dk,dv] when
+    snapshot_every > 0: the state after every snapshot_every tokens of each sequence, in
+    sequence order."""
     q, k, v, g, beta, cu, s0, T, H, dk, dv, N = _prep(q, k, v, g, beta, cu, s0)
     o = np.zeros((T, H, dv), np.float64)
     sT = np.zeros((N, H, dk, dv), np.float64)
-    rc = _lib().kda_oracle_recurrence(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu.ctypes.data, N,
-                                      _ptr(s0), o.ctypes.data, sT.ctypes.data, H, dk, dv, int(vcols),
-                                      threads or default_threads())
+    snap_cu = np.zeros(N + 1, np.int64)
+    if snapshot_every > 0:
+        snap_cu[1:] = np.cumsum(np.diff(cu) // snapshot_every)
+    snaps = np.zeros((int(snap_cu[-1]), H, dk, dv), np.float64)
+    rc = _lib().kda_oracle_recurrence_snap(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu.ctypes.data, N,
+                                           _ptr(s0), o.ctypes.data, sT.ctypes.data, H, dk, dv, int(vcols),
+                                           threads or default_threads(), int(snapshot_every), snap_cu.ctypes.data,
+                                           snaps.ctypes.data)
     if rc != 0:
         raise RuntimeError(f"kda_oracle_recurrence failed ({rc})")
-    return o, sT
+    return (o, sT, snaps) if snapshot_every > 0 else (o, sT)
 
 
 def chunked(q, k, v, g, beta, cu=None, s0=None, *, chunk=16, threads=None):

@@ -38,6 +38,9 @@ typedef struct {
     const double *q, *k, *v, *g, *beta, *s0;
     const int64_t* cu;
     double *o, *sT;
+    int64_t snap_every;      /* tokens between state snapshots (0: none) */
+    const int64_t* snap_cu;  /* first snapshot row of each sequence */
+    double* snaps;           /* [snap_cu[N], H, dk, dv] */
     int64_t N, H, dk, dv, chunk;
     int64_t vcols; /* value columns per work unit */
     int64_t nunits;
@@ -87,6 +90,13 @@ static void recurrence_unit(ctx_t* c, int64_t n, int64_t h, int64_t j0, int64_t 
             double o = 0;
             for (int64_t i = 0; i < dk; ++i) o += qt[i] * S[i * w + j];
             c->o[(t * H + h) * dv + j0 + j] = o;
+        }
+        /* snapshot: the state after every snap_every tokens of the sequence */
+        const int64_t done = t - c->cu[n] + 1;
+        if (c->snaps && done % c->snap_every == 0) {
+            double* dst = c->snaps + ((c->snap_cu[n] + done / c->snap_every - 1) * H + h) * dk * dv;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < w; ++j) dst[i * dv + j0 + j] = S[i * w + j];
         }
     }
     if (c->sT)
@@ -239,17 +249,33 @@ static int check(const int64_t* cu, int64_t N, int64_t H, int64_t dk, int64_t dv
  * be NULL.  vcols > 0 splits value columns into work units of that width for
  * threading (0 = whole rows).  Returns 0, -1 on a bad argument, -2 on OOM.
  */
-int kda_oracle_recurrence(const double* q, const double* k, const double* v, const double* g,
-                          const double* beta, const int64_t* cu, int64_t N, const double* s0, double* o,
-                          double* sT, int64_t H, int64_t dk, int64_t dv, int64_t vcols, int nthreads) {
+/*
+ * O1 with state snapshots: snaps receives the state after every snap_every
+ * tokens of each sequence (snapshot m of sequence n, the state after its first
+ * (m + 1) * snap_every tokens, at row snap_cu[n] + m); snap_every = 0 or
+ * snaps = NULL: no snapshots.
+ */
+int kda_oracle_recurrence_snap(const double* q, const double* k, const double* v, const double* g,
+                               const double* beta, const int64_t* cu, int64_t N, const double* s0, double* o,
+                               double* sT, int64_t H, int64_t dk, int64_t dv, int64_t vcols, int nthreads,
+                               int64_t snap_every, const int64_t* snap_cu, double* snaps) {
     if (check(cu, N, H, dk, dv) || (cu[N] > 0 && (!q || !k || !v || !g || !beta || !o))) return -1;
+    if (snap_every < 0 || (snap_every > 0 && snaps && !snap_cu)) return -1;
     ctx_t c;
     memset(&c, 0, sizeof(c));
     c.q = q; c.k = k; c.v = v; c.g = g; c.beta = beta; c.s0 = s0; c.cu = cu; c.o = o; c.sT = sT;
+    c.snap_every = snap_every; c.snap_cu = snap_cu; c.snaps = snap_every > 0 ? snaps : NULL;
     c.N = N; c.H = H; c.dk = dk; c.dv = dv;
     c.vcols = vcols > 0 && vcols < dv ? vcols : dv;
     c.nunits = N * H * ((dv + c.vcols - 1) / c.vcols);
     return run(&c, recurrence_worker, nthreads);
+}
+
+int kda_oracle_recurrence(const double* q, const double* k, const double* v, const double* g,
+                          const double* beta, const int64_t* cu, int64_t N, const double* s0, double* o,
+                          double* sT, int64_t H, int64_t dk, int64_t dv, int64_t vcols, int nthreads) {
+    return kda_oracle_recurrence_snap(q, k, v, g, beta, cu, N, s0, o, sT, H, dk, dv, vcols, nthreads, 0, NULL,
+                                      NULL);
 }
 
 /* Chunked fp64 algebra (check of the chunked form only).  chunk >= 1. */

@@ -90,3 +90,52 @@ def test_injected_launch_failure_reports_hip_error(monkeypatch):
     ptrs = [base + i * (1 << 30) for i in range(8)]
     rc = L.kda_decode_step(*ptrs[:5], ptrs[5], ptrs[5], ptrs[6], 1, 1, 16, 16, 0, None)
     assert rc == _l.KDA_ERR_HIP and b"injected" in L.kda_last_error()
+
+
+def test_extended_call_options_are_validated():
+    """Options of the extended calls: gate kind, snapshot spacing and buffers (host-side checks,
+    nothing is launched)."""
+    import ctypes
+
+    _l, L = _lib()
+    base = 1 << 40
+    p = [base + i * (1 << 30) for i in range(12)]  # valid, non-overlapping fake buffers
+
+    def opts(gate=0, every=0, snaps=None, snap_cu=None):
+        return ctypes.byref(_l.Options(gate, every, snaps, snap_cu))
+
+    def prefill(o):
+        return L.kda_prefill_chunked_ex(p[0], p[1], p[2], p[3], p[4], None, p[5], None, 1, 64, 2, 16, 16, 0, 16,
+                                        None, 0, o, None)
+
+    def append(o):
+        return L.kda_append_prefill_ex(p[0], p[1], p[2], p[3], p[4], p[6], 1, 64, None, p[5], None, 2, 16, 16, 0,
+                                       16, None, 0, o, None)
+
+    def decode(o):
+        return L.kda_decode_step_ex(p[0], p[1], p[2], p[3], p[4], p[7], p[7], p[5], 1, 1, 16, 16, 0, o, None)
+
+    assert prefill(opts(gate=2)) == _l.KDA_ERR_INVALID_ARG and b"gate" in L.kda_last_error()
+    assert prefill(opts(every=-1)) == _l.KDA_ERR_INVALID_ARG
+    assert prefill(opts(every=1)) == _l.KDA_ERR_INVALID_ARG and b"snapshots" in L.kda_last_error()
+    assert prefill(opts(every=1, snaps=p[8] + 2)) == _l.KDA_ERR_MISALIGNED
+    assert prefill(opts(every=1, snaps=p[0])) == _l.KDA_ERR_ALIAS  # snapshots on top of q
+    assert append(opts(every=1, snaps=p[8])) == _l.KDA_ERR_INVALID_ARG and b"snapshot_cu" in L.kda_last_error()
+    assert append(opts(every=1, snaps=p[6], snap_cu=p[9])) == _l.KDA_ERR_ALIAS  # snapshots on cu_seqlens
+    assert decode(opts(every=1, snaps=p[8])) == _l.KDA_ERR_INVALID_ARG and b"snapshot" in L.kda_last_error()
+    # per-head gate: g is [T, H] (4-byte alignment suffices), channel gate: 16 bytes for prefill
+    assert L.kda_prefill_chunked_ex(p[0], p[1], p[2], p[3] + 4, p[4], None, p[5], None, 1, 64, 2, 16, 16, 0, 16,
+                                    None, 0, opts(gate=0), None) == _l.KDA_ERR_MISALIGNED
+
+
+def test_python_options_marshalling():
+    """The binding's option struct matches struct kda_options field for field."""
+    import ctypes
+
+    import gated_delta_rule_75_amd as kda
+    from gated_delta_rule_75_amd import _lib as _l
+
+    o = _l.Options(_l.KDA_GATE_HEAD, 3, 0x1000, 0x2000)
+    assert (o.gate, o.snapshot_every, o.snapshots, o.snapshot_cu) == (1, 3, 0x1000, 0x2000)
+    assert ctypes.sizeof(o) == 24  # int32, int32, pointer, pointer
+    assert kda._options(_l.KDA_GATE_CHANNEL) is not None

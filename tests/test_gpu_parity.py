@@ -214,3 +214,71 @@ def test_strong_decay_is_flagged_not_wrong():
     o, s = kda.prefill_chunked(q, k, v, g, b)
     torch.cuda.synchronize()
     assert torch.isnan(s).all()
+
+
+# ---------------------------------------------------------------------------------------------
+# Gated DeltaNet gate (one log-decay per token and head) and state snapshots
+# ---------------------------------------------------------------------------------------------
+def _head_gate(st, wide):
+    """The same inputs with one gate per head: the first channel's log-decay of each token."""
+    q, k, v, g, b = st
+    gh = np.ascontiguousarray(g[..., 0])
+    return (q, k, v, gh, b), (wide[0], wide[1], wide[2], gh.astype(np.float64), wide[4])
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("f32", 32, 32), ("f32", 16, 16), ("bf16", 64, 32)])
+def test_head_gate_prefill_and_decode_match_oracle(dtype, d, chunk):
+    print(f"head gate dtype={dtype} d={d} chunk={chunk}", flush=True)
+    w = _w(dtype, H=3, d=d, chunk=chunk, seed=31, s0_std=0.02)
+    B, T = 2, 333
+    st, wide = _head_gate(*make_inputs(w, B * T))
+    s0 = synth.gen_state(w, B)
+    q, k, v, g, b = upload(w, st, (B, T))
+    assert g.shape == (B, T, 3)
+    o, sT = kda.prefill_chunked(q, k, v, g, b, dev(s0, "f32"), chunk=chunk)
+    # one decode step continuing from the prefill's final state, also with a per-head gate
+    st2, wide2 = _head_gate(*make_inputs(w, B, offset_tokens=B * T))
+    q2, k2, v2, g2, b2 = upload(w, st2)
+    S = sT.clone()
+    o2 = kda.decode_step(q2, k2, v2, g2, b2, S)
+    torch.cuda.synchronize()
+    cu = np.arange(B + 1) * T
+    oref, sref = oracle.recurrence(*wide, cu, s0)
+    assert_close(host(o).reshape(B * T, 3, d), oref, TOL[dtype], cu, "o")
+    assert_close(host(sT), sref, TOL[dtype], None, "S_T")
+    oref2, sref2 = oracle.recurrence(*wide2, np.arange(B + 1), sref)
+    assert_close(host(o2), oref2, TOL[dtype], np.arange(B + 1), "decode o")
+    assert_close(host(S), sref2, TOL[dtype], None, "decode S")
+
+
+@pytest.mark.parametrize("dtype,d,chunk,every", [("bf16", 128, 64, 3), ("f32", 32, 32, 2), ("bf16", 64, 16, 5)])
+def test_snapshots_match_oracle(dtype, d, chunk, every):
+    """Prefill (B=2, ragged tail) and append (segments shorter than one snapshot interval, empty
+    ones and a long one) with state snapshots every `every` chunks."""
+    print(f"snapshots dtype={dtype} d={d} chunk={chunk} every={every}", flush=True)
+    w = _w(dtype, H=2, d=d, chunk=chunk, seed=37, s0_std=0.02)
+    E = every * chunk
+    # prefill
+    B, T = 2, 1000
+    st, wide = make_inputs(w, B * T)
+    s0 = synth.gen_state(w, B)
+    q, k, v, g, b = upload(w, st, (B, T))
+    o, sT, snaps = kda.prefill_chunked(q, k, v, g, b, dev(s0, "f32"), chunk=chunk, snapshot_every=every)
+    # append
+    lens = [E * 3 + 17, 5, 0, E, E * 2 - 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    Ta = int(cu[-1])
+    sta, widea = make_inputs(w, Ta, offset_tokens=B * T)
+    s0a = synth.gen_state(w, len(lens))
+    qa, ka, va, ga, ba = upload(w, sta)
+    oa, sTa, snapsa, snap_cu = kda.append_prefill(qa, ka, va, ga, ba, torch.from_numpy(cu).cuda(), dev(s0a, "f32"),
+                                                  chunk=chunk, snapshot_every=every)
+    torch.cuda.synchronize()
+    assert snaps.shape[:2] == (B, T // E)
+    _, _, sref = oracle.recurrence(*wide, np.arange(B + 1) * T, s0, snapshot_every=E)
+    assert_close(host(snaps).reshape(-1, 2, d, d), sref, TOL[dtype], None, "prefill snapshots")
+    _, sTref, srefa = oracle.recurrence(*widea, cu, s0a, snapshot_every=E)
+    assert list(snap_cu.cpu().numpy()) == list(np.concatenate([[0], np.cumsum([n // E for n in lens])]))
+    assert snapsa.shape[0] == srefa.shape[0] == 3 + 0 + 0 + 1 + 1
+    assert_close(host(snapsa), srefa, TOL[dtype], None, "append snapshots")
+    assert_close(host(sTa), sTref, TOL[dtype], None, "append S_T")

@@ -293,3 +293,63 @@ def test_matches_both_orientations_of_the_equation():
         P = P @ np.diag(np.exp(g[t])) @ (np.eye(dk) - b[t] * np.outer(k[t], k[t])) + b[t] * np.outer(v[t], k[t])
         np.testing.assert_allclose(P @ q[t], o[t], atol=1e-12)
     np.testing.assert_allclose(P.T, S, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# Gated DeltaNet: one forget gate per head and token ("Kimi K3, explained", the comparison of
+# KDA with Gated DeltaNet: a scalar decay instead of one per key channel)
+# ---------------------------------------------------------------------------------------------
+def test_head_gate_decay_only_closed_form():
+    """beta = 0 with a per-head gate: the whole state shrinks by exp(sum of g) (every channel
+    alike, unlike the per-channel case above)."""
+    rng = np.random.default_rng(21)
+    T, H, dk, dv = 12, 3, 8, 6
+    g = np.log(rng.uniform(0.3, 1.0, (T, H)))
+    S0 = rng.standard_normal((1, H, dk, dv))
+    _, S = oracle.recurrence(rng.standard_normal((T, H, dk)), _rand_unit(rng, T * H, dk).reshape(T, H, dk),
+                             rng.standard_normal((T, H, dv)), g, np.zeros((T, H)), None, S0, threads=1)
+    np.testing.assert_allclose(S[0], np.exp(g.sum(0))[:, None, None] * S0[0], rtol=1e-13, atol=0)
+
+
+def test_head_gate_overwrite_under_any_decay():
+    """beta = 1, unit key: whatever the scalar decay and the prior state, reading the key right
+    after the write returns the written value ("The math", the overwrite special case)."""
+    rng = np.random.default_rng(22)
+    T, H, dk, dv = 9, 2, 8, 5
+    k = _rand_unit(rng, T * H, dk).reshape(T, H, dk)
+    v = rng.standard_normal((T, H, dv))
+    o, _ = oracle.recurrence(k, k, v, np.log(rng.uniform(0.05, 1.0, (T, H))), np.ones((T, H)), None,
+                             rng.standard_normal((1, H, dk, dv)), threads=1)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# State snapshots ("Kimi K3 changed the memory math for agentic AI": checkpoints of the
+# fixed-size state along a long context): snapshot m of a sequence is the state after its
+# first (m + 1) * E tokens, i.e. the final state of a run over just those tokens.
+# ---------------------------------------------------------------------------------------------
+def test_snapshots_are_final_states_of_prefixes():
+    rng = np.random.default_rng(23)
+    H, dk, dv, E = 2, 8, 6, 7
+    lens = [30, 5, 0, 21, 14]  # with a sequence shorter than E and an empty one
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q = rng.standard_normal((T, H, dk))
+    k = _rand_unit(rng, T * H, dk).reshape(T, H, dk)
+    v = rng.standard_normal((T, H, dv))
+    g = np.log(rng.uniform(0.5, 1.0, (T, H, dk)))
+    b = rng.uniform(0, 1, (T, H))
+    s0 = rng.standard_normal((len(lens), H, dk, dv))
+    _, sT, snaps = oracle.recurrence(q, k, v, g, b, cu, s0, threads=2, snapshot_every=E)
+    assert snaps.shape[0] == sum(n // E for n in lens)
+    row = 0
+    for n, L in enumerate(lens):
+        for m in range(L // E):
+            sl = slice(cu[n], cu[n] + (m + 1) * E)
+            _, ref = oracle.recurrence(q[sl], k[sl], v[sl], g[sl], b[sl], None, s0[n:n + 1], threads=1)
+            np.testing.assert_allclose(snaps[row], ref[0], rtol=0, atol=0)
+            row += 1
+    # a snapshot exactly at the end of a sequence equals its final state (sequences 3 and 4:
+    # rows 4..6 and 7..8)
+    np.testing.assert_allclose(snaps[6], sT[3], rtol=0, atol=0)
+    np.testing.assert_allclose(snaps[8], sT[4], rtol=0, atol=0)
