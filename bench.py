@@ -215,7 +215,43 @@ def bench_prefill(args, res):
     log(f"[prefill] {res['value'] / 1e6:.2f} M tokens/s, {res['ms_per_step']:.3f} ms/step, pass {path_ms:.3f} ms "
         f"(events), kernel time per pass {{{kp}}}")
 
+    # the next rows on the same inputs: one gate per head (Gated DeltaNet: the first channel's
+    # log-decay of each token) and state snapshots every 16 chunks
+    tgh = tg[..., 0].contiguous()
+    snaps = torch.empty((1, T // (16 * 64), H, dk, dv), dtype=torch.float32, device=dev)
+
+    def timed_passes(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+
+    ms_head = timed_passes(lambda: kda.prefill_chunked(tq, tk, tv, tgh, tb, None, out=out, state_out=sT,
+                                                       workspace=ws))
+    ms_snap = timed_passes(lambda: kda.prefill_chunked(tq, tk, tv, tg, tb, None, out=out, state_out=sT,
+                                                       workspace=ws, snapshot_every=16, snapshots=snaps))
+    head_bytes = (PREFILL_BYTES_PER_TOKEN_HEAD - 512 + 4) * th  # g is one fp32 per token-head
+    res["next_rows"] = {
+        "head_gate_prefill": {"workload": f"as the headline, g [T,H] (one log-decay per token and head)",
+                              "ms_per_pass": round(ms_head, 4), "tokens_per_s": round(T / (ms_head * 1e-3), 1),
+                              "roofline": {"bound": "hbm", "achieved": round(head_bytes / (ms_head * 1e-3) / 1e9, 1),
+                                           "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                           "frac": round(head_bytes / (ms_head * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                           "algorithmic_bytes_per_launch": head_bytes}},
+        "snapshots_every_16_chunks": {"snapshots": int(snaps.shape[1]), "ms_per_pass": round(ms_snap, 4),
+                                      "overhead_vs_headline": round(ms_snap / path_ms - 1, 4)},
+    }
+    log(f"[prefill] per-head gate {ms_head:.3f} ms/pass; with {snaps.shape[1]} snapshots {ms_snap:.3f} ms/pass")
+    del snaps, tgh
+
     # parity of the timed output on a token sample (all heads) + CPU baseline from the same oracle run
+    step()
+    torch.cuda.synchronize()
     wide_all = (q, k, v, g, b)
     return out, sT, wide_all
 

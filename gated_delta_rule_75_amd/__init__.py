@@ -98,8 +98,10 @@ def _gate(g, shape_channel, shape_head):
     return _lib.KDA_GATE_CHANNEL
 
 
-def _options(gate, every=0, snapshots=None, snapshot_cu=None):
-    return ctypes.byref(_lib.Options(gate, every, _ptr(snapshots), _ptr(snapshot_cu)))
+def _options(gate, every=0, snapshots=None, snapshot_cu=None, gate_scale=None):
+    """kda_options; gate_scale given = fused prologue (raw q, k, beta logits, raw gate inputs)."""
+    return ctypes.byref(_lib.Options(gate, every, _ptr(snapshots), _ptr(snapshot_cu), int(gate_scale is not None),
+                                     float(gate_scale or 0.0)))
 
 
 def _workspace(nbytes, device, workspace):
@@ -111,7 +113,7 @@ def _workspace(nbytes, device, workspace):
 
 
 def prefill_chunked(q, k, v, g, beta, state=None, *, chunk=64, out=None, state_out=None, final_state=True,
-                    workspace=None, snapshot_every=0, snapshots=None):
+                    workspace=None, snapshot_every=0, snapshots=None, prologue_gate_scale=None):
     """Chunked prefill of B equal-length sequences.
 
     q, k [B,T,H,dk], v [B,T,H,dv] (float32 or bfloat16), g float32 log alpha, either
@@ -119,7 +121,10 @@ def prefill_chunked(q, k, v, g, beta, state=None, *, chunk=64, out=None, state_o
     beta [B,T,H] (same dtype as q), state [B,H,dk,dv] float32 or None.
     Returns (o [B,T,H,dv] float32, S_T [B,H,dk,dv] float32 or None), plus the state snapshots
     [B, T // (snapshot_every * chunk), H, dk, dv] when snapshot_every > 0 (the state after
-    every snapshot_every chunks)."""
+    every snapshot_every chunks).
+
+    prologue_gate_scale = s (not None): fused input prologue; q, k are raw (normalised inside),
+    beta holds logits and g the raw gate inputs a (g = -s * softplus(a))."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -149,12 +154,13 @@ def prefill_chunked(q, k, v, g, beta, state=None, *, chunk=64, out=None, state_o
     L = _lib.load()
     _lib.check(L.kda_prefill_chunked_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
                                         _ptr(state_out), B, T, H, dk, dv, _DT[dt], chunk, _ptr(ws), ws_bytes,
-                                        _options(gate, snapshot_every, snapshots), _stream(dev)))
+                                        _options(gate, snapshot_every, snapshots, None, prologue_gate_scale),
+                                        _stream(dev)))
     return (out, state_out, snapshots) if snapshot_every > 0 else (out, state_out)
 
 
 def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=None, state_out=None,
-                   final_state=True, workspace=None, snapshot_every=0):
+                   final_state=True, workspace=None, snapshot_every=0, prologue_gate_scale=None):
     """Append-prefill of N packed segments (token-major [T_total, H, d]) on carried states.
 
     cu_seqlens: int32 GPU tensor [N+1] (0, ..., T_total).  g [T_total,H,dk] or [T_total,H] (one
@@ -196,14 +202,15 @@ def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=No
     L = _lib.load()
     _lib.check(L.kda_append_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
                                        _ptr(state), _ptr(out), _ptr(state_out), H, dk, dv, _DT[dt], chunk,
-                                       _ptr(ws), ws_bytes, _options(gate, snapshot_every, snapshots, snapshot_cu),
+                                       _ptr(ws), ws_bytes,
+                                       _options(gate, snapshot_every, snapshots, snapshot_cu, prologue_gate_scale),
                                        _stream(dev)))
     if snapshot_every > 0:
         return out, state_out, snapshots, snapshot_cu
     return out, state_out
 
 
-def decode_step(q, k, v, g, beta, state, *, out=None, state_out=None):
+def decode_step(q, k, v, g, beta, state, *, out=None, state_out=None, prologue_gate_scale=None):
     """One decode step for N sequences: q, k [N,H,dk], g [N,H,dk] or [N,H] (one decay per head),
     v [N,H,dv], beta [N,H], state [N,H,dk,dv].
 
@@ -229,6 +236,7 @@ def decode_step(q, k, v, g, beta, state, *, out=None, state_out=None):
     _check(out, "out", torch.float32, (N, H, dv), dev)
     L = _lib.load()
     _lib.check(L.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                    _ptr(state_out), _ptr(out), N, H, dk, dv, _DT[dt], _options(gate),
+                                    _ptr(state_out), _ptr(out), N, H, dk, dv, _DT[dt],
+                                    _options(gate, gate_scale=prologue_gate_scale),
                                     _stream(dev)))
     return out

@@ -31,7 +31,7 @@ _LIB = None
 class Options(ctypes.Structure):
     """struct kda_options"""
     _fields_ = [("gate", ctypes.c_int32), ("snapshot_every", ctypes.c_int32), ("snapshots", ctypes.c_void_p),
-                ("snapshot_cu", ctypes.c_void_p)]
+                ("snapshot_cu", ctypes.c_void_p), ("prologue", ctypes.c_int32), ("gate_scale", ctypes.c_float)]
 
 
 class KdaError(RuntimeError):

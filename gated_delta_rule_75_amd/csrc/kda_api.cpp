@@ -157,6 +157,8 @@ struct Opts {
     int every = 0;
     float* snaps = nullptr;
     const int32_t* snap_cu = nullptr;
+    bool prologue = false;
+    float gate_scale = 0.f;
 };
 
 int read_options(const kda_options* o, int op, const char* name, Opts& out) {
@@ -174,6 +176,12 @@ int read_options(const kda_options* o, int op, const char* name, Opts& out) {
         if (!aligned_to(o->snapshots, 4) || !aligned_to(o->snapshot_cu, 4))
             return fail(KDA_ERR_MISALIGNED, "%s: snapshots and snapshot_cu must be 4-byte aligned", name);
     }
+    if (o->prologue != 0 && o->prologue != 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: options.prologue must be 0 or 1", name);
+    if (o->prologue && !(o->gate_scale > 0.f && o->gate_scale < 3.4e38f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: options.gate_scale must be finite and > 0", name);
+    out.prologue = o->prologue == 1;
+    out.gate_scale = o->prologue ? o->gate_scale : 0.f;
     out.gate_head = o->gate == KDA_GATE_HEAD;
     out.every = o->snapshot_every;
     out.snaps = o->snapshot_every > 0 ? o->snapshots : nullptr;
@@ -287,6 +295,7 @@ int kda_prefill_chunked_ex(const void* q, const void* k, const void* v, const fl
     a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.gate_head = op.gate_head; a.snap = snap_per_seq > 0 ? op.snaps : nullptr; a.snap_every = op.every;
     a.snap_cu = nullptr; a.snap_per_seq = snap_per_seq;
+    a.prologue = op.prologue; a.gate_scale = op.gate_scale;
     return run_prefill(a, dtype, static_cast<hipStream_t>(hip_stream), name);
 }
 
@@ -343,6 +352,7 @@ int kda_append_prefill_ex(const void* q, const void* k, const void* v, const flo
     a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.gate_head = op.gate_head; a.snap = op.snaps; a.snap_every = op.every; a.snap_cu = op.snap_cu;
     a.snap_per_seq = 0;
+    a.prologue = op.prologue; a.gate_scale = op.gate_scale;
     return run_prefill(a, dtype, static_cast<hipStream_t>(hip_stream), name);
 }
 
@@ -384,6 +394,7 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const float*
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s_in = state_in; a.s_out = state_out; a.o = out;
     a.N = N; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16; a.gate_head = op.gate_head;
+    a.prologue = op.prologue; a.gate_scale = op.gate_scale;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     return check_hip(kda::launch_decode(a, s), s, name);
 }

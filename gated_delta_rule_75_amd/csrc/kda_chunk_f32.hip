@@ -38,7 +38,8 @@ struct F32Lds {
         + 3 * (size_t)C * kLdc   // A, M, T
         + (size_t)DK * kBV       // S
         + 2 * (size_t)C * kBV    // R, D
-        + C;                     // beta
+        + C                      // beta
+        + 2 * (size_t)C;         // 1/|k|, 1/|q| per row (fused prologue)
     static constexpr size_t kBytes = kFloats * sizeof(float);
 };
 
@@ -58,6 +59,8 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(PrefillArgs a) {
     float* sR = sS + DK * kBV;          // [C][kBV]
     float* sD = sR + C * kBV;           // [C][kBV]
     float* sb = sD + C * kBV;           // [C]
+    float* sik = sb + C;                // [C] 1/|k_r| (fused prologue)
+    float* siq = sik + C;               // [C] 1/|q_r|
 
     const TI* q = static_cast<const TI*>(a.q);
     const TI* k = static_cast<const TI*>(a.k);
@@ -89,12 +92,35 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(PrefillArgs a) {
         for (int i = tid; i < DK; i += kThreads) {
             float acc = 0.f;
             for (int r = 0; r < C; ++r) {
-                if (r < L) acc += a.gate_head ? a.g[(t0 + r) * H + h] : a.g[((t0 + r) * H + h) * (int64_t)DK + i];
+                if (r < L) {
+                    float gv = a.gate_head ? a.g[(t0 + r) * H + h] : a.g[((t0 + r) * H + h) * (int64_t)DK + i];
+                    acc += a.prologue ? gate_from_raw(gv, a.gate_scale) : gv;
+                }
                 sG[r * DK + i] = acc;
             }
         }
-        for (int r = tid; r < C; r += kThreads) sb[r] = r < L ? ld_in(beta, (t0 + r) * H + h) : 0.f;
+        for (int r = tid; r < C; r += kThreads) {
+            const float bt = r < L ? ld_in(beta, (t0 + r) * H + h) : 0.f;
+            sb[r] = r < L && a.prologue ? sigmoid(bt) : bt;
+        }
         __syncthreads();
+        if (a.prologue) {  // fused prologue: unit-length keys and queries
+            for (int r = tid; r < C; r += kThreads) {
+                float ssk = 0.f, ssq = 0.f;
+                for (int c = 0; c < DK; ++c) {
+                    ssk += sk[r * DK + c] * sk[r * DK + c];
+                    ssq += sq[r * DK + c] * sq[r * DK + c];
+                }
+                sik[r] = ssk > 0.f ? rsqrtf(ssk) : 0.f;
+                siq[r] = ssq > 0.f ? rsqrtf(ssq) : 0.f;
+            }
+            __syncthreads();
+            for (int e = tid; e < C * DK; e += kThreads) {
+                sk[e] *= sik[e / DK];
+                sq[e] *= siq[e / DK];
+            }
+            __syncthreads();
+        }
 
         // gated Gram matrices
         for (int e = tid; e < C * C; e += kThreads) {

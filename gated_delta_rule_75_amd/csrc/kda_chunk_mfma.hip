@@ -159,6 +159,9 @@ __device__ __forceinline__ float* t_block(PrepLds& L, int i, int j) {
     return i == j ? &L.AT[16 * i][16 * i] : &L.AT[16 * j][16 * i];
 }
 
+// PRO: fused input prologue (raw q, k, beta logits, raw gate inputs); a template parameter so
+// that the plain kernel carries none of its code.
+template <bool PRO>
 __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) {
     __shared__ PrepLds L;
     // wave index, wave-uniform (readfirstlane lets the compiler keep it in a scalar register)
@@ -190,7 +193,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
     // g first: the decay scan needs it before anything else (with one gate per head, the
     // token's single log-decay on every channel)
     if (a.gate_head) {
-        const float gs = a.g[(t0 + (valid ? r : Lc - 1)) * H + h];
+        float gs = a.g[(t0 + (valid ? r : Lc - 1)) * H + h];
+        if (PRO) gs = gate_from_raw(gs, a.gate_scale);
 #pragma unroll
         for (int j = 0; j < 8; ++j) gv[j] = make_float4(gs, gs, gs, gs);
     } else {
@@ -214,6 +218,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
         const float4 g0 = gv[2 * ks], g1 = gv[2 * ks + 1];
         gl[ks][0] = g0.x; gl[ks][1] = g0.y; gl[ks][2] = g0.z; gl[ks][3] = g0.w;
         gl[ks][4] = g1.x; gl[ks][5] = g1.y; gl[ks][6] = g1.z; gl[ks][7] = g1.w;
+        if (PRO && !a.gate_head) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) gl[ks][i] = gate_from_raw(gl[ks][i], a.gate_scale);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) gl[ks][i] = valid ? gl[ks][i] : 0.f;
     }
@@ -265,7 +273,32 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
 
     // ---- operand tiles for this lane's token and 32 channels
     // beta of this lane's token (0 past the chunk end) for Diag(beta) K+
-    const float brow_r = valid ? bf(beta[(t0 + (valid ? r : Lc - 1)) * H + h]) : 0.f;
+    float brow_r = bf(beta[(t0 + (valid ? r : Lc - 1)) * H + h]);
+    brow_r = valid ? (PRO ? sigmoid(brow_r) : brow_r) : 0.f;
+    // fused prologue: this token's key and query are scaled to unit length (its 128 channels
+    // are spread over the 4 lanes lr, lr + 16, lr + 32, lr + 48)
+    float inv_k = 1.f, inv_q = 1.f;
+    if (PRO) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t kw[4] = {kv[ks].x, kv[ks].y, kv[ks].z, kv[ks].w};
+            const uint32_t qw[4] = {qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float kk = bf((uint16_t)((i & 1) ? (kw[i >> 1] >> 16) : (kw[i >> 1] & 0xFFFF)));
+                const float qq = bf((uint16_t)((i & 1) ? (qw[i >> 1] >> 16) : (qw[i >> 1] & 0xFFFF)));
+                sk += kk * kk;
+                sq += qq * qq;
+            }
+        }
+        sk += __shfl_xor(sk, 16, 64);
+        sq += __shfl_xor(sq, 16, 64);
+        sk += __shfl_xor(sk, 32, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        inv_k = sk > 0.f ? rsqrtf(sk) : 0.f;
+        inv_q = sq > 0.f ? rsqrtf(sq) : 0.f;
+    }
     half8 KR[4], QR[4], BKp[4];
     floatx4 diagA = {0.f, 0.f, 0.f, 0.f}, diagM = {0.f, 0.f, 0.f, 0.f};  // tile (w, w)
 #pragma unroll
@@ -279,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
             const float gloc = gl[ks][i];
             const uint32_t kb16 = (i & 1) ? (kw[i >> 1] >> 16) : (kw[i >> 1] & 0xFFFF);
             const uint32_t qb16 = (i & 1) ? (qw[i >> 1] >> 16) : (qw[i >> 1] & 0xFFFF);
-            const float kk = valid ? bf(kb16) : 0.f, qq = valid ? bf(qb16) : 0.f;
+            const float kk = valid ? bf(kb16) * inv_k : 0.f, qq = valid ? bf(qb16) * inv_q : 0.f;
             const float eloc = fast_exp(gloc);              // exp(G_r - P_w)          <= 1
             const float ecol = fast_exp(L.tot[w][ch] - gloc);  // exp(P_{w+1} - G_r)   <= 1
             const float ep = L.eP[w][ch];
@@ -314,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
     for (int i = 0; i < 4; ++i) {
         const int rr = 16 * w + 4 * lg + i;
         const float bv = bf(beta[(t0 + (rr < Lc ? rr : Lc - 1)) * H + h]);
-        brow[i] = rr < Lc ? bv : 0.f;
+        brow[i] = rr < Lc ? (PRO ? sigmoid(bv) : bv) : 0.f;
     }
     {
         const floatx4 accA = diagA, accM = diagM;
@@ -583,11 +616,11 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* v, cons
     r.g[1] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8 + 4, 0, 0);
 }
 
-__device__ __forceinline__ void stage_store(StateLds& L, int buf, const StageRegs& r, int lane) {
+__device__ __forceinline__ void stage_store(StateLds& L, int buf, const StageRegs& r, int lane, bool beta_logits) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int tok = 32 * j + (lane >> 1);
-        const float bt = bf((uint16_t)r.b[j]);
+        const float bt = beta_logits ? sigmoid(bf((uint16_t)r.b[j])) : bf((uint16_t)r.b[j]);
         const uint32_t words[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -741,19 +774,19 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
         StageRegs ra, rb;
         if (nchunks > 0) {
             stage_load(ra, v, beta, rec_of(0), bos, len_of(0), H, h, vb, lane);
-            stage_store(L, 0, ra, lane);
+            stage_store(L, 0, ra, lane, a.prologue);
         }
         if (nchunks > 1) stage_load(rb, v, beta, rec_of(1), bos + C, len_of(1), H, h, vb, lane);
         lds_barrier();
         for (int64_t c = 0; c < nchunks; c += 2) {
             if (c + 2 < nchunks) stage_load(ra, v, beta, rec_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h, vb, lane);
             lds_barrier();
-            if (c + 1 < nchunks) stage_store(L, 1, rb, lane);
+            if (c + 1 < nchunks) stage_store(L, 1, rb, lane, a.prologue);
             lds_barrier();
             if (c + 1 >= nchunks) break;
             if (c + 3 < nchunks) stage_load(rb, v, beta, rec_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h, vb, lane);
             lds_barrier();
-            if (c + 2 < nchunks) stage_store(L, 0, ra, lane);
+            if (c + 2 < nchunks) stage_store(L, 0, ra, lane, a.prologue);
             lds_barrier();
         }
         return;
@@ -848,7 +881,10 @@ hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
     const bool timed = timing_on();
     if (slots > 0 && a.T_total > 0) {
         if (timed) timed_begin(kKernelPrep, s);
-        hipLaunchKernelGGL(prep_kernel, dim3((unsigned)slots, (unsigned)a.H), dim3(256), 0, s, a, sm);
+        if (a.prologue)
+            hipLaunchKernelGGL(prep_kernel<true>, dim3((unsigned)slots, (unsigned)a.H), dim3(256), 0, s, a, sm);
+        else
+            hipLaunchKernelGGL(prep_kernel<false>, dim3((unsigned)slots, (unsigned)a.H), dim3(256), 0, s, a, sm);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (timed) timed_end(s);

@@ -39,10 +39,11 @@ struct DecodeShape {
     static_assert(kThreads >= DK, "one thread per key row stages alpha, k, q");
 };
 
-template <int DK, int DV, typename TI>
+template <int DK, int DV, typename TI, bool PROLOGUE>
 __global__ __launch_bounds__(1024) void decode_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v, const float* __restrict__ g,
-    const TI* __restrict__ beta, const float* s_in, float* s_out, float* __restrict__ o, int gate_head) {
+    const TI* __restrict__ beta, const float* s_in, float* s_out, float* __restrict__ o, int gate_head,
+    float gate_scale) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int CT = Sh::kColThreads, RG = Sh::kRowGroups, RPT = Sh::kRowsPerThread;
     constexpr int NW = Sh::kWaves;
@@ -54,6 +55,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     __shared__ floatx4 s_red[NW][2][CT];  // per wave: partial u and p of each column group
     __shared__ float s_kq[NW];
     __shared__ float s_a[DK], s_k[DK], s_q[DK];
+    __shared__ float s_nrm[2][DK / 64 > 0 ? DK / 64 : 1];
 
     const float* Sin = s_in + nh * (int64_t)DK * DV + 4 * c4;
     float* Sout = s_out + nh * (int64_t)DK * DV + 4 * c4;
@@ -64,10 +66,39 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     for (int i = 0; i < RPT; ++i)
         st[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sin + (int64_t)(rg + i * RG) * DV));
     // alpha, k, q of every key row, one row per thread, shared through LDS
+    float kt = 0.f, qt = 0.f;
     if (tid < DK) {
-        s_a[tid] = expf(gate_head ? g[nh] : g[nh * DK + tid]);  // one decay per head, or per key channel
-        s_k[tid] = ld_in(k, nh * DK + tid);
-        s_q[tid] = ld_in(q, nh * DK + tid);
+        kt = ld_in(k, nh * DK + tid);
+        qt = ld_in(q, nh * DK + tid);
+    }
+    if (PROLOGUE) {  // fused prologue: unit-length key and query (threads 0 .. DK-1 hold them)
+        float sk = kt * kt, sq = qt * qt;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            sk += __shfl_xor(sk, off, 64);
+            sq += __shfl_xor(sq, off, 64);
+        }
+        if (tid < DK && lane == 0) {
+            s_nrm[0][wave] = sk;
+            s_nrm[1][wave] = sq;
+        }
+        __syncthreads();
+        sk = 0.f;
+        sq = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < (DK + 63) / 64; ++wv) {
+            sk += s_nrm[0][wv];
+            sq += s_nrm[1][wv];
+        }
+        kt *= sk > 0.f ? rsqrtf(sk) : 0.f;
+        qt *= sq > 0.f ? rsqrtf(sq) : 0.f;
+    }
+    if (tid < DK) {
+        float gv = gate_head ? g[nh] : g[nh * DK + tid];  // one decay per head, or per key channel
+        if (PROLOGUE) gv = gate_from_raw(gv, gate_scale);
+        s_a[tid] = expf(gv);
+        s_k[tid] = kt;
+        s_q[tid] = qt;
     }
     __syncthreads();
     float a[RPT], kk[RPT], u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
@@ -112,7 +143,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     }
 
     float d[4];
-    const float b = ld_in(beta, nh);
+    const float b = PROLOGUE ? sigmoid(ld_in(beta, nh)) : ld_in(beta, nh);
 #pragma unroll
     for (int j = 0; j < 4; ++j) d[j] = b * (ld_in(v, nh * DV + 4 * c4 + j) - uu[j]);
     if (rg == 0) {
@@ -131,23 +162,30 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     }
 }
 
+template <int DK, int DV, typename TI>
+void launch_typed(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+    const TI* q = static_cast<const TI*>(a.q);
+    const TI* k = static_cast<const TI*>(a.k);
+    const TI* v = static_cast<const TI*>(a.v);
+    const TI* b = static_cast<const TI*>(a.beta);
+    if (a.prologue)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, TI, true>), grid, block, 0, s, q, k, v, a.g, b, a.s_in, a.s_out,
+                           a.o, a.gate_head, a.gate_scale);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, DV, TI, false>), grid, block, 0, s, q, k, v, a.g, b, a.s_in, a.s_out,
+                           a.o, a.gate_head, a.gate_scale);
+}
+
 template <int DK, int DV>
 hipError_t launch_shape(const DecodeArgs& a, hipStream_t s) {
     using Sh = DecodeShape<DK, DV>;
     const dim3 grid(static_cast<unsigned>(a.N * a.H));
     const bool timed = timing_on();
     if (timed) timed_begin(kKernelDecode, s);
-    if (a.bf16) {
-        hipLaunchKernelGGL((decode_kernel<DK, DV, uint16_t>), grid, dim3(Sh::kThreads), 0, s,
-                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(a.v), a.g, static_cast<const uint16_t*>(a.beta), a.s_in,
-                           a.s_out, a.o, a.gate_head);
-    } else {
-        hipLaunchKernelGGL((decode_kernel<DK, DV, float>), grid, dim3(Sh::kThreads), 0, s,
-                           static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                           static_cast<const float*>(a.v), a.g, static_cast<const float*>(a.beta), a.s_in,
-                           a.s_out, a.o, a.gate_head);
-    }
+    if (a.bf16)
+        launch_typed<DK, DV, uint16_t>(a, grid, dim3(Sh::kThreads), s);
+    else
+        launch_typed<DK, DV, float>(a, grid, dim3(Sh::kThreads), s);
     hipError_t e = hipGetLastError();
     if (timed) timed_end(s);
     return e;

@@ -28,4 +28,16 @@ __device__ __forceinline__ float fast_exp(float x) {
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// Fused input prologue: beta from its logit, g from the raw gate input.  Both use the hardware
+// base-2 exponential and logarithm (about 1e-7 relative error), which keeps them small enough
+// for the register budget of the kernels they are inlined into.
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + fast_exp(-x)); }
+
+__device__ __forceinline__ float gate_from_raw(float a, float scale) {
+    // -scale * softplus(a), softplus(a) = log(1 + e^a) written so that it cannot overflow:
+    // max(a, 0) + log(1 + e^-|a|)
+    const float t = 1.f + fast_exp(-fabsf(a));
+    return -scale * (fmaxf(a, 0.f) + __builtin_amdgcn_logf(t) * 0.6931471805599453f);
+}
+
 }  // namespace kda

@@ -38,6 +38,8 @@ struct PrefillArgs {
     int snap_every;         // chunks between snapshots
     const int32_t* snap_cu; // varlen: first snapshot row of each sequence (device)
     int64_t snap_per_seq;   // fixed length: snapshots per sequence
+    int prologue;           // raw inputs: normalise q, k; beta = sigmoid(beta); g = -gate_scale * softplus(g)
+    float gate_scale;
 };
 
 struct DecodeArgs {
@@ -53,6 +55,8 @@ struct DecodeArgs {
     int H, dk, dv;
     int bf16;
     int gate_head;  // g is [N, H] (one decay per sequence and head) instead of [N, H, dk]
+    int prologue;   // raw inputs, as in PrefillArgs
+    float gate_scale;
 };
 
 // generic fp32-arithmetic chunked kernel (any supported shape, either storage type)

@@ -142,8 +142,21 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* g,
  *            int32 [N + 1] with snapshot_cu[0] = 0 and snapshot_cu[n+1] -
  *            snapshot_cu[n] = (cu_seqlens[n+1] - cu_seqlens[n]) / (E * chunk)
  *            (a caller contract, not checked on the device).
- * snapshots must be 4-byte aligned and overlap no other argument.  A NULL
- * options pointer means { KDA_GATE_CHANNEL, 0, NULL, NULL }.
+ * snapshots must be 4-byte aligned and overlap no other argument.
+ *
+ * Fused input prologue ("Kimi K3, explained", "How Kimi Delta Attention
+ * works, step by step": in the DeltaNet family queries and keys are
+ * L2-normalised; beta is a write strength in (0, 1) and alpha a forget gate in
+ * (0, 1)).  With prologue = 1 the inputs are the raw projections and the
+ * kernels apply, per token and head:
+ *   q <- q / ||q||,  k <- k / ||k||       (a zero vector stays zero)
+ *   beta <- sigmoid(beta)                 (beta holds logits)
+ *   g <- -gate_scale * softplus(g)        (g holds the raw gate input a, per
+ *                                          key channel or per head)
+ * so that no separate elementwise pass (and no extra round trip through
+ * memory) is needed.  gate_scale must be finite and > 0.
+ *
+ * A NULL options pointer means { KDA_GATE_CHANNEL, 0, NULL, NULL, 0, 0 }.
  */
 typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1 } kda_gate;
 
@@ -152,6 +165,8 @@ typedef struct kda_options {
     int32_t snapshot_every;     /* chunks between state snapshots; 0 = none (must be 0 for decode) */
     float* snapshots;           /* see above; NULL when snapshot_every = 0 */
     const int32_t* snapshot_cu; /* append only; NULL otherwise */
+    int32_t prologue;           /* 1: raw q, k, beta logits and gate inputs (see above); 0: as stored */
+    float gate_scale;           /* prologue only: g = -gate_scale * softplus(a) */
 } kda_options;
 
 int kda_prefill_chunked_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,

@@ -127,6 +127,22 @@ def recurrence(q, k, v, g, beta, cu=None, s0=None, *, threads=None, vcols=0, sna
     return (o, sT, snaps) if snapshot_every > 0 else (o, sT)
 
 
+def prologue(q, k, beta_logits, gate_in, gate_scale):
+    """The input prologue of the DeltaNet family ("Kimi K3, explained", "How Kimi Delta Attention
+    works, step by step"), in fp64: queries and keys L2-normalised per token and head (a zero
+    vector stays zero), beta = sigmoid(logit), g = log(alpha) = -gate_scale * softplus(a).
+    Returns (q, k, beta, g)."""
+    q, k, b, a = (np.asarray(x, np.float64) for x in (q, k, beta_logits, gate_in))
+
+    def unit(x):
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+    beta = 1.0 / (1.0 + np.exp(-b))
+    g = -gate_scale * (np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a))))
+    return unit(q), unit(k), beta, g
+
+
 def chunked(q, k, v, g, beta, cu=None, s0=None, *, chunk=16, threads=None):
     """fp64 chunked algebra (the form the GPU path organises its work in)."""
     q, k, v, g, beta, cu, s0, T, H, dk, dv, N = _prep(q, k, v, g, beta, cu, s0)

@@ -162,6 +162,23 @@ def gen_tokens(w: Workload, T: int, *, offset_tokens: int = 0, q_unit: bool | No
     return q, k, v, g, beta
 
 
+def gen_raw_tokens(w: Workload, T: int, *, offset_tokens: int = 0, gate_head: bool = False, threads=None):
+    """Raw projections for the fused input prologue: q, k ~ N(0, 2^2) (not normalised),
+    v ~ N(0, 1), beta logits ~ N(0, 1) (all stored in w.dtype), gate inputs a ~ N(0, 1) fp32,
+    [T, H, dk] or [T, H] with one per head.  Returns (q, k, v, a, beta_logits)."""
+    H, dk, dv, dt = w.H, w.dk, w.dv, w.dtype
+    off_k, off_v, off_h = offset_tokens * H * dk, offset_tokens * H * dv, offset_tokens * H
+    q = fill(K_NORMAL, w.seed, TID_Q, (T, H, dk), dt, offset=off_k, p0=2.0, threads=threads)
+    k = fill(K_NORMAL, w.seed, TID_K, (T, H, dk), dt, offset=off_k, p0=2.0, threads=threads)
+    v = fill(K_NORMAL, w.seed, TID_V, (T, H, dv), dt, offset=off_v, p0=1.0, threads=threads)
+    beta = fill(K_NORMAL, w.seed, TID_BETA, (T, H), dt, offset=off_h, p0=1.0, threads=threads)
+    if gate_head:
+        a = fill(K_NORMAL, w.seed, TID_G, (T, H), "f32", offset=off_h, p0=1.0, threads=threads)
+    else:
+        a = fill(K_NORMAL, w.seed, TID_G, (T, H, dk), "f32", offset=off_k, p0=1.0, threads=threads)
+    return q, k, v, a, beta
+
+
 def gen_state(w: Workload, N: int, threads=None):
     """Carried fp32 state [N, H, dk, dv] ~ N(0, s0_std^2), or None for a zero state."""
     if w.s0_std <= 0:

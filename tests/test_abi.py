@@ -101,8 +101,8 @@ def test_extended_call_options_are_validated():
     base = 1 << 40
     p = [base + i * (1 << 30) for i in range(12)]  # valid, non-overlapping fake buffers
 
-    def opts(gate=0, every=0, snaps=None, snap_cu=None):
-        return ctypes.byref(_l.Options(gate, every, snaps, snap_cu))
+    def opts(gate=0, every=0, snaps=None, snap_cu=None, prologue=0, scale=0.0):
+        return ctypes.byref(_l.Options(gate, every, snaps, snap_cu, prologue, scale))
 
     def prefill(o):
         return L.kda_prefill_chunked_ex(p[0], p[1], p[2], p[3], p[4], None, p[5], None, 1, 64, 2, 16, 16, 0, 16,
@@ -116,6 +116,9 @@ def test_extended_call_options_are_validated():
         return L.kda_decode_step_ex(p[0], p[1], p[2], p[3], p[4], p[7], p[7], p[5], 1, 1, 16, 16, 0, o, None)
 
     assert prefill(opts(gate=2)) == _l.KDA_ERR_INVALID_ARG and b"gate" in L.kda_last_error()
+    assert prefill(opts(prologue=2)) == _l.KDA_ERR_INVALID_ARG and b"prologue" in L.kda_last_error()
+    assert prefill(opts(prologue=1, scale=0.0)) == _l.KDA_ERR_INVALID_ARG and b"gate_scale" in L.kda_last_error()
+    assert decode(opts(prologue=1, scale=float("inf"))) == _l.KDA_ERR_INVALID_ARG
     assert prefill(opts(every=-1)) == _l.KDA_ERR_INVALID_ARG
     assert prefill(opts(every=1)) == _l.KDA_ERR_INVALID_ARG and b"snapshots" in L.kda_last_error()
     assert prefill(opts(every=1, snaps=p[8] + 2)) == _l.KDA_ERR_MISALIGNED
@@ -135,7 +138,8 @@ def test_python_options_marshalling():
     import gated_delta_rule_75_amd as kda
     from gated_delta_rule_75_amd import _lib as _l
 
-    o = _l.Options(_l.KDA_GATE_HEAD, 3, 0x1000, 0x2000)
-    assert (o.gate, o.snapshot_every, o.snapshots, o.snapshot_cu) == (1, 3, 0x1000, 0x2000)
-    assert ctypes.sizeof(o) == 24  # int32, int32, pointer, pointer
+    o = _l.Options(_l.KDA_GATE_HEAD, 3, 0x1000, 0x2000, 1, 0.5)
+    assert (o.gate, o.snapshot_every, o.snapshots, o.snapshot_cu, o.prologue, o.gate_scale) == (1, 3, 0x1000, 0x2000,
+                                                                                                   1, 0.5)
+    assert ctypes.sizeof(o) == 32  # int32, int32, pointer, pointer, int32, float
     assert kda._options(_l.KDA_GATE_CHANNEL) is not None

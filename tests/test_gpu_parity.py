@@ -282,3 +282,35 @@ def test_snapshots_match_oracle(dtype, d, chunk, every):
     assert snapsa.shape[0] == srefa.shape[0] == 3 + 0 + 0 + 1 + 1
     assert_close(host(snapsa), srefa, TOL[dtype], None, "append snapshots")
     assert_close(host(sTa), sTref, TOL[dtype], None, "append S_T")
+
+
+# ---------------------------------------------------------------------------------------------
+# Fused input prologue: raw q, k (normalised in the kernels), beta logits, raw gate inputs
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d,chunk,gate_head", [("bf16", 128, 64, False), ("bf16", 128, 64, True),
+                                                      ("f32", 32, 32, False), ("f32", 16, 16, True)])
+def test_fused_prologue_matches_oracle(dtype, d, chunk, gate_head):
+    print(f"prologue dtype={dtype} d={d} chunk={chunk} gate_head={gate_head}", flush=True)
+    w = _w(dtype, H=3, d=d, chunk=chunk, seed=43, s0_std=0.02)
+    scale = 0.1
+    B, T = 2, 333
+    q, k, v, a, b = synth.gen_raw_tokens(w, B * T + B, gate_head=gate_head)
+    s0 = synth.gen_state(w, B)
+    wide = [synth.to_f64(x, dtype) for x in (q, k, v)] + [a.astype(np.float64), synth.to_f64(b, dtype)]
+    qn, kn, beta, g = oracle.prologue(wide[0], wide[1], wide[4], wide[3], scale)
+    tq, tk, tv, tb = (dev(x, dtype) for x in (q, k, v, b))
+    ta = dev(a, "f32")
+    n = B * T
+    bt = lambda t: t[:n].reshape(B, T, *t.shape[1:])  # noqa: E731
+    o, sT = kda.prefill_chunked(bt(tq), bt(tk), bt(tv), bt(ta), bt(tb), dev(s0, "f32"), chunk=chunk,
+                                prologue_gate_scale=scale)
+    S = sT.clone()
+    o2 = kda.decode_step(tq[n:], tk[n:], tv[n:], ta[n:], tb[n:], S, prologue_gate_scale=scale)
+    torch.cuda.synchronize()
+    cu = np.arange(B + 1) * T
+    oref, sref = oracle.recurrence(qn[:n], kn[:n], wide[2][:n], g[:n], beta[:n], cu, s0)
+    assert_close(host(o).reshape(n, 3, d), oref, TOL[dtype], cu, "o")
+    assert_close(host(sT), sref, TOL[dtype], None, "S_T")
+    oref2, sref2 = oracle.recurrence(qn[n:], kn[n:], wide[2][n:], g[n:], beta[n:], np.arange(B + 1), sref)
+    assert_close(host(o2), oref2, TOL[dtype], np.arange(B + 1), "decode o")
+    assert_close(host(S), sref2, TOL[dtype], None, "decode S")

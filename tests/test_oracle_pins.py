@@ -353,3 +353,24 @@ def test_snapshots_are_final_states_of_prefixes():
     # rows 4..6 and 7..8)
     np.testing.assert_allclose(snaps[6], sT[3], rtol=0, atol=0)
     np.testing.assert_allclose(snaps[8], sT[4], rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------------------------------------
+# Fused input prologue ("Kimi K3, explained", "How Kimi Delta Attention works, step by step":
+# normalised queries and keys, beta and alpha in (0, 1))
+# ---------------------------------------------------------------------------------------------
+def test_prologue_closed_forms():
+    rng = np.random.default_rng(24)
+    q, k = rng.standard_normal((2, 5, 3, 16)) * 7.0
+    k[0, 0] = 0.0  # a zero key stays zero
+    qn, kn, beta, g = oracle.prologue(q, k, np.array([0.0, 40.0, -40.0, 3.0]), np.array([0.0, 50.0, -50.0, 1.0]),
+                                      0.1)
+    np.testing.assert_allclose(np.linalg.norm(qn, axis=-1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(np.linalg.norm(kn[1:], axis=-1), 1.0, rtol=1e-14)
+    assert np.all(kn[0, 0] == 0.0)
+    np.testing.assert_allclose(kn * np.linalg.norm(k, axis=-1, keepdims=True), k, rtol=1e-14, atol=0)
+    # sigmoid: 1/2 at 0, saturating at +-40; 3 -> e^3 / (1 + e^3)
+    np.testing.assert_allclose(beta, [0.5, 1.0, np.exp(-40.0), np.exp(3.0) / (1 + np.exp(3.0))], rtol=1e-14)
+    # softplus: ln 2 at 0, x for large x, e^x for very negative x, log(1 + e) at 1
+    np.testing.assert_allclose(g, [-0.1 * np.log(2.0), -5.0, -0.1 * np.exp(-50.0), -0.1 * np.log1p(np.e)],
+                               rtol=1e-14)
