@@ -11,7 +11,8 @@ step by step" and "The math"), per sequence and head, with the state S in R^{d_k
     S_t     = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
     o_t     = S_t^T q_t                                   (read after the write)
 
-``recurrence`` is the definition stepped token by token (the oracle proper); ``chunked``
+``recurrence`` is the definition stepped token by token (the oracle proper); ``backward`` is
+its reverse-mode derivative (the same token steps taken backwards); ``chunked``
 is the chunked algebra in fp64 (used only to pin that the chunked form reaches the same
 result); ``linear_attention`` is the page's contrast rule S <- S + k v^T.
 
@@ -63,6 +64,9 @@ def _lib():
         L.kda_oracle_chunked.restype = ctypes.c_int
         L.kda_oracle_chunked.argtypes = [dp, dp, dp, dp, dp, ip, i64, dp, dp, dp, i64, i64, i64, i64,
                                          ctypes.c_int]
+        L.kda_oracle_backward.restype = ctypes.c_int
+        L.kda_oracle_backward.argtypes = [dp, dp, dp, dp, dp, ip, i64, dp, dp, dp, dp, dp, dp, dp, dp, dp, i64, i64,
+                                          i64, ctypes.c_int]
         L.kda_oracle_linear_attention.restype = ctypes.c_int
         L.kda_oracle_linear_attention.argtypes = [dp, dp, dp, i64, i64, i64, dp, dp, dp]
         _LIB = L
@@ -125,6 +129,29 @@ def recurrence(q, k, v, g, beta, cu=None, s0=None, *, threads=None, vcols=0, sna
     if rc != 0:
         raise RuntimeError(f"kda_oracle_recurrence failed ({rc})")
     return (o, sT, snaps) if snapshot_every > 0 else (o, sT)
+
+
+def backward(q, k, v, g, beta, cu=None, s0=None, *, d_o, d_sT=None, threads=None):
+    """Reverse-mode derivative of ``recurrence`` in fp64.  ``d_o`` [T,H,dv] is dL/do and ``d_sT``
+    [N,H,dk,dv] (or None: zero) is dL/dS_T.  Returns (dq, dk, dv, dg, dbeta, ds0): dL/d of each
+    input, with dg = dL/d(log alpha) in g's own shape ([T,H,dk], or [T,H] for one decay per head,
+    the sum over key channels) and ds0 = dL/dS_0 [N,H,dk,dv] (returned also when s0 is None)."""
+    head_gate = np.ndim(g) == 2
+    q, k, v, g, beta, cu, s0, T, H, dk, dv, N = _prep(q, k, v, g, beta, cu, s0)
+    d_o, d_sT = _f64(d_o), _f64(d_sT)
+    if d_o.shape != (T, H, dv) or (d_sT is not None and d_sT.shape != (N, H, dk, dv)):
+        raise ValueError("d_o must be [T,H,dv] and d_sT [N,H,dk,dv]")
+    dq, dk_, dg = (np.zeros((T, H, dk), np.float64) for _ in range(3))
+    dv_ = np.zeros((T, H, dv), np.float64)
+    db = np.zeros((T, H), np.float64)
+    ds0 = np.zeros((N, H, dk, dv), np.float64)
+    rc = _lib().kda_oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu.ctypes.data, N, _ptr(s0),
+                                    _ptr(d_o), _ptr(d_sT), dq.ctypes.data, dk_.ctypes.data, dv_.ctypes.data,
+                                    dg.ctypes.data, db.ctypes.data, ds0.ctypes.data, H, dk, dv,
+                                    threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_backward failed ({rc})")
+    return dq, dk_, dv_, (dg.sum(-1) if head_gate else dg), db, ds0
 
 
 def prologue(q, k, beta_logits, gate_in, gate_scale):

@@ -41,6 +41,9 @@ typedef struct {
     int64_t snap_every;      /* tokens between state snapshots (0: none) */
     const int64_t* snap_cu;  /* first snapshot row of each sequence */
     double* snaps;           /* [snap_cu[N], H, dk, dv] */
+    /* reverse mode (O3): upstream gradients in, input gradients out */
+    const double *dO, *dsT;
+    double *dq, *dk_, *dv_, *dg, *dbeta, *ds0;
     int64_t N, H, dk, dv, chunk;
     int64_t vcols; /* value columns per work unit */
     int64_t nunits;
@@ -206,6 +209,145 @@ done:
     free(S); free(G); free(A); free(M); free(Tm); free(R); free(D); free(Sn);
 }
 
+/*
+ * One token of O1 on a whole state (rows i < dk, columns j < dv), keeping what
+ * the reverse sweep needs: X = Diag(alpha_t) S_{t-1}, u = X^T k_t and
+ * delta = beta_t (v_t - u).  S is advanced to S_t in place.
+ */
+static void step_token(const ctx_t* c, int64_t t, int64_t h, double* S, double* X, double* u, double* delta) {
+    const int64_t H = c->H, dk = c->dk, dv = c->dv;
+    const double* kt = c->k + (t * H + h) * dk;
+    const double* vt = c->v + (t * H + h) * dv;
+    const double* gt = c->g + (t * H + h) * dk;
+    const double bt = c->beta[t * H + h];
+    for (int64_t i = 0; i < dk; ++i) {
+        const double a = exp(gt[i]);
+        for (int64_t j = 0; j < dv; ++j) X[i * dv + j] = a * S[i * dv + j];
+    }
+    for (int64_t j = 0; j < dv; ++j) {
+        double acc = 0;
+        for (int64_t i = 0; i < dk; ++i) acc += kt[i] * X[i * dv + j];
+        u[j] = acc;
+        delta[j] = bt * (vt[j] - acc);
+    }
+    for (int64_t i = 0; i < dk; ++i)
+        for (int64_t j = 0; j < dv; ++j) S[i * dv + j] = X[i * dv + j] + kt[i] * delta[j];
+}
+
+/*
+ * O3 — reverse-mode derivative of O1 for one (sequence n, head h).  Given the
+ * upstream gradients dL/do_t (dO) and dL/dS_T (dsT, NULL = 0), it returns
+ * dL/dq, dL/dk, dL/dv, dL/dg (g = log alpha), dL/dbeta and dL/dS_0.  Written
+ * from the four lines of one token, taken backwards (S the state after the
+ * token, dS its gradient):
+ *   o = S^T q             dq = S do;           dS += q do^T
+ *   S = X + k delta^T     dk += dS delta;      ddelta = dS^T k;   dX = dS
+ *   delta = beta (v - u)  dbeta = ddelta.(v - u); dv = beta ddelta; du = -beta ddelta
+ *   u = X^T k             dk += X du;          dX += k du^T
+ *   X = Diag(alpha) S'    dg_i = sum_j dX_ij X_ij;  dS' = Diag(alpha) dX
+ * The states S_{t-1} come from a forward sweep that keeps the state at the
+ * start of every block of `blk` tokens and re-steps each block when the
+ * reverse sweep reaches it (the same arithmetic, so the same states).
+ */
+static void backward_unit(ctx_t* c, int64_t n, int64_t h) {
+    const int64_t H = c->H, dk = c->dk, dv = c->dv, t0 = c->cu[n], L = c->cu[n + 1] - t0;
+    const int64_t blk = 64, nblk = (L + blk - 1) / blk, sz = dk * dv;
+    double* ck = (double*)malloc(sizeof(double) * (size_t)((nblk > 0 ? nblk : 1) * sz));
+    double* st = (double*)malloc(sizeof(double) * (size_t)(blk * sz)); /* S_{t-1} of each token of a block */
+    double* S = (double*)calloc((size_t)sz, sizeof(double));
+    double* X = (double*)malloc(sizeof(double) * (size_t)sz);
+    double* dS = (double*)calloc((size_t)sz, sizeof(double));
+    double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* delta = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* dd = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!ck || !st || !S || !X || !dS || !u || !delta || !dd) { c->err = 1; goto done; }
+    if (c->s0) memcpy(S, c->s0 + (n * H + h) * sz, sizeof(double) * (size_t)sz);
+    for (int64_t b = 0; b < nblk; ++b) {
+        memcpy(ck + b * sz, S, sizeof(double) * (size_t)sz);
+        for (int64_t t = t0 + b * blk; t < t0 + L && t < t0 + (b + 1) * blk; ++t) step_token(c, t, h, S, X, u, delta);
+    }
+    if (c->dsT) memcpy(dS, c->dsT + (n * H + h) * sz, sizeof(double) * (size_t)sz);
+    for (int64_t b = nblk - 1; b >= 0; --b) {
+        const int64_t ta = t0 + b * blk, tb = ta + blk < t0 + L ? ta + blk : t0 + L;
+        memcpy(S, ck + b * sz, sizeof(double) * (size_t)sz);
+        for (int64_t t = ta; t < tb; ++t) {
+            memcpy(st + (t - ta) * sz, S, sizeof(double) * (size_t)sz);
+            step_token(c, t, h, S, X, u, delta);
+        }
+        for (int64_t t = tb - 1; t >= ta; --t) {
+            /* recompute this token from S_{t-1}: S becomes S_t, X, u and delta as in the forward */
+            memcpy(S, st + (t - ta) * sz, sizeof(double) * (size_t)sz);
+            step_token(c, t, h, S, X, u, delta);
+            const double* qt = c->q + (t * H + h) * dk;
+            const double* kt = c->k + (t * H + h) * dk;
+            const double* vt = c->v + (t * H + h) * dv;
+            const double* gt = c->g + (t * H + h) * dk;
+            const double* dot = c->dO + (t * H + h) * dv;
+            const double bt = c->beta[t * H + h];
+            double* dqt = c->dq + (t * H + h) * dk;
+            double* dkt = c->dk_ + (t * H + h) * dk;
+            double* dvt = c->dv_ + (t * H + h) * dv;
+            double* dgt = c->dg + (t * H + h) * dk;
+            /* read: o = S_t^T q */
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0;
+                for (int64_t j = 0; j < dv; ++j) {
+                    acc += S[i * dv + j] * dot[j];
+                    dS[i * dv + j] += qt[i] * dot[j];
+                }
+                dqt[i] = acc;
+            }
+            /* write: S_t = X + k delta^T */
+            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0;
+                for (int64_t i = 0; i < dk; ++i) acc += kt[i] * dS[i * dv + j];
+                dd[j] = acc;
+            }
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0;
+                for (int64_t j = 0; j < dv; ++j) acc += dS[i * dv + j] * delta[j];
+                dkt[i] = acc;
+            }
+            /* erase: delta = beta (v - u) */
+            double db = 0;
+            for (int64_t j = 0; j < dv; ++j) {
+                db += dd[j] * (vt[j] - u[j]);
+                dvt[j] = bt * dd[j];
+                dd[j] = -bt * dd[j]; /* now du */
+            }
+            c->dbeta[t * H + h] = db;
+            /* u = X^T k: into dk and into dX (held in dS) */
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0;
+                for (int64_t j = 0; j < dv; ++j) {
+                    acc += X[i * dv + j] * dd[j];
+                    dS[i * dv + j] += kt[i] * dd[j];
+                }
+                dkt[i] += acc;
+            }
+            /* decay: X = Diag(alpha) S_{t-1} */
+            for (int64_t i = 0; i < dk; ++i) {
+                const double a = exp(gt[i]);
+                double acc = 0;
+                for (int64_t j = 0; j < dv; ++j) {
+                    acc += dS[i * dv + j] * X[i * dv + j];
+                    dS[i * dv + j] *= a;
+                }
+                dgt[i] = acc;
+            }
+        }
+    }
+    if (c->ds0) memcpy(c->ds0 + (n * H + h) * sz, dS, sizeof(double) * (size_t)sz);
+done:
+    free(ck); free(st); free(S); free(X); free(dS); free(u); free(delta); free(dd);
+}
+
+static void* backward_worker(void* arg) {
+    ctx_t* c = (ctx_t*)arg;
+    for (int64_t u; (u = take_unit(c)) >= 0;) backward_unit(c, u / c->H, u % c->H);
+    return NULL;
+}
+
 static void* recurrence_worker(void* arg) {
     ctx_t* c = (ctx_t*)arg;
     const int64_t nvb = (c->dv + c->vcols - 1) / c->vcols;
@@ -289,6 +431,28 @@ int kda_oracle_chunked(const double* q, const double* k, const double* v, const 
     c.N = N; c.H = H; c.dk = dk; c.dv = dv; c.chunk = chunk;
     c.nunits = N * H;
     return run(&c, chunked_worker, nthreads);
+}
+
+/*
+ * O3: gradients of the recurrence.  dO [T_total, H, dv] is required; dsT
+ * [N, H, dk, dv] may be NULL (zero).  dq, dk, dg [T_total, H, dk], dv
+ * [T_total, H, dv] and dbeta [T_total, H] are written; ds0 [N, H, dk, dv] may
+ * be NULL.  s0 may be NULL (zero initial state).
+ */
+int kda_oracle_backward(const double* q, const double* k, const double* v, const double* g, const double* beta,
+                        const int64_t* cu, int64_t N, const double* s0, const double* dO, const double* dsT,
+                        double* dq, double* dk, double* dv_out, double* dg, double* dbeta, double* ds0, int64_t H,
+                        int64_t dk_dim, int64_t dv, int nthreads) {
+    if (check(cu, N, H, dk_dim, dv) ||
+        (cu[N] > 0 && (!q || !k || !v || !g || !beta || !dO || !dq || !dk || !dv_out || !dg || !dbeta)))
+        return -1;
+    ctx_t c;
+    memset(&c, 0, sizeof(c));
+    c.q = q; c.k = k; c.v = v; c.g = g; c.beta = beta; c.s0 = s0; c.cu = cu;
+    c.dO = dO; c.dsT = dsT; c.dq = dq; c.dk_ = dk; c.dv_ = dv_out; c.dg = dg; c.dbeta = dbeta; c.ds0 = ds0;
+    c.N = N; c.H = H; c.dk = dk_dim; c.dv = dv;
+    c.nunits = N * H;
+    return run(&c, backward_worker, nthreads);
 }
 
 /*
