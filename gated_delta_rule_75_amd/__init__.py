@@ -17,8 +17,8 @@ import torch
 from . import _lib
 from ._lib import KdaError  # noqa: F401
 
-__all__ = ["prefill_chunked", "append_prefill", "decode_step", "workspace_size", "is_supported", "version",
-           "KdaError", "kernel_timing"]
+__all__ = ["prefill_chunked", "append_prefill", "decode_step", "chunked_backward", "workspace_size", "is_supported",
+           "version", "KdaError", "kernel_timing"]
 
 _DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
 
@@ -208,6 +208,46 @@ def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=No
     if snapshot_every > 0:
         return out, state_out, snapshots, snapshot_cu
     return out, state_out
+
+
+def chunked_backward(q, k, v, g, beta, cu_seqlens, state=None, *, d_out, d_state_out=None, chunk=64,
+                     state_grad=True, workspace=None):
+    """Gradients of ``append_prefill`` (packed segments, token-major [T_total, H, d]).
+
+    d_out [T_total,H,dv] float32 = dL/do; d_state_out [N,H,dk,dv] float32 = dL/dS_T or None (zero).
+    Returns (dq, dk [T_total,H,dk], dv [T_total,H,dv], dg (g's shape), dbeta [T_total,H],
+    dS0 [N,H,dk,dv] or None when state_grad is False), all float32.  A batch of B equal
+    sequences of T tokens is the packed layout [B*T, H, d] with cu_seqlens = 0, T, ..., B*T."""
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    dev = q.device
+    _check(q, "q", dt, (T, H, dk), dev)
+    _check(k, "k", dt, (T, H, dk), dev)
+    _check(v, "v", dt, (T, H, dv), dev)
+    gate = _gate(g, (T, H, dk), (T, H))
+    _check(g, "g", torch.float32, None, dev)
+    _check(beta, "beta", dt, (T, H), dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    _check(state, "state", torch.float32, (N, H, dk, dv), dev)
+    _check(d_out, "d_out", torch.float32, (T, H, dv), dev)
+    _check(d_state_out, "d_state_out", torch.float32, (N, H, dk, dv), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk_, dv_ = torch.empty((T, H, dk), **f32), torch.empty((T, H, dk), **f32), torch.empty((T, H, dv), **f32)
+    dg = torch.empty(tuple(g.shape), **f32)
+    db = torch.empty((T, H), **f32)
+    ds0 = torch.empty((N, H, dk, dv), **f32) if state_grad else None
+    ws_bytes = workspace_size(_lib.KDA_OP_BACKWARD, N, T, H, dk, dv, dt, chunk)
+    ws = _workspace(ws_bytes, dev, workspace)
+    L = _lib.load()
+    _lib.check(L.kda_chunked_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+                                      _ptr(state), _ptr(d_out), _ptr(d_state_out), _ptr(dq), _ptr(dk_), _ptr(dv_),
+                                      _ptr(dg), _ptr(db), _ptr(ds0), H, dk, dv, _DT[dt], chunk, _ptr(ws), ws_bytes,
+                                      _options(gate), _stream(dev)))
+    return dq, dk_, dv_, dg, db, ds0
 
 
 def decode_step(q, k, v, g, beta, state, *, out=None, state_out=None, prologue_gate_scale=None):

@@ -120,6 +120,7 @@ int prefill_path(int32_t dtype, int32_t dk, int32_t dv, int32_t chunk) {
 
 size_t ws_size(int32_t op, int64_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t dtype, int32_t chunk) {
     if (op == KDA_OP_DECODE) return 0;
+    if (op == KDA_OP_BACKWARD) return kda::chunk_bwd_workspace(N, T, H, dk, dv, chunk);
     if (prefill_path(dtype, dk, dv, chunk) != 2) return 0;
     const bool fixed = op == KDA_OP_PREFILL;
     const int64_t T_total = fixed ? N * T : T;
@@ -243,6 +244,7 @@ int kda_is_supported(int32_t op, int32_t dtype, int32_t d_k, int32_t d_v, int32_
     if (!valid_dtype(dtype)) return 0;
     if (op == KDA_OP_DECODE) return kda::decode_supported(d_k, d_v) ? 1 : 0;
     if (op == KDA_OP_PREFILL || op == KDA_OP_APPEND) return prefill_path(dtype, d_k, d_v, chunk) ? 1 : 0;
+    if (op == KDA_OP_BACKWARD) return kda::chunk_bwd_supported(d_k, d_v, chunk) ? 1 : 0;
     return 0;
 }
 
@@ -362,6 +364,67 @@ int kda_append_prefill(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, void* hip_stream) {
     return kda_append_prefill_ex(q, k, v, g, beta, cu_seqlens, N, T_total, state_in, out, state_out, H, d_k, d_v,
                                  dtype, chunk, workspace, workspace_bytes, nullptr, hip_stream);
+}
+
+int kda_chunked_backward(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                         const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in,
+                         const float* d_out, const float* d_state_out, float* dq, float* dk, float* dv,
+                         float* dg, float* dbeta, float* d_state_in, int32_t H, int32_t d_k, int32_t d_v,
+                         int32_t dtype, int32_t chunk, void* workspace, size_t workspace_bytes,
+                         const kda_options* options, void* hip_stream) {
+    static const char* name = "kda_chunked_backward";
+    Opts op;
+    if (int rc = read_options(options, KDA_OP_APPEND, name, op)) return rc;
+    if (op.every || op.prologue)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: snapshots and the fused prologue are not part of the backward", name);
+    if (N < 0 || T_total < 0) return fail(KDA_ERR_INVALID_ARG, "%s: N and T_total must be >= 0", name);
+    if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens is required", name);
+    if (int rc = validate_common(q, k, v, g, beta, T_total, H, d_k, d_v, dtype, 1, op.gate_head)) return rc;
+    if (!kda::chunk_bwd_supported(d_k, d_v, chunk))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d chunk=%d not implemented", name, d_k, d_v, chunk);
+    if (T_total > 0 && (!d_out || !dq || !dk || !dv || !dg || !dbeta))
+        return fail(KDA_ERR_INVALID_ARG, "%s: d_out, dq, dk, dv, dg and dbeta are required", name);
+    const void* fl[] = {state_in, d_out, d_state_out, dq, dk, dv, dg, dbeta, d_state_in};
+    for (const void* p : fl)
+        if (!aligned_to(p, 4)) return fail(KDA_ERR_MISALIGNED, "%s: float buffers must be 4-byte aligned", name);
+    if (!aligned_to(workspace, 256)) return fail(KDA_ERR_MISALIGNED, "%s: workspace must be 256-byte aligned", name);
+    const size_t esz = dtype == KDA_BF16 ? 2 : 4, tokens = (size_t)T_total;
+    const size_t sbytes = (size_t)N * H * d_k * d_v * 4, gk = op.gate_head ? 1 : (size_t)d_k;
+    const Span ins[] = {{q, tokens * H * d_k * esz},
+                        {k, tokens * H * d_k * esz},
+                        {v, tokens * H * d_v * esz},
+                        {g, tokens * H * gk * 4},
+                        {beta, tokens * H * esz},
+                        {cu_seqlens, (size_t)(N + 1) * 4},
+                        {state_in, state_in ? sbytes : 0},
+                        {d_out, tokens * H * d_v * 4},
+                        {d_state_out, d_state_out ? sbytes : 0}};
+    const Span outs[] = {{dq, tokens * H * d_k * 4}, {dk, tokens * H * d_k * 4}, {dv, tokens * H * d_v * 4},
+                         {dg, tokens * H * gk * 4},  {dbeta, tokens * H * 4},    {d_state_in, d_state_in ? sbytes : 0}};
+    const size_t need = ws_size(KDA_OP_BACKWARD, N, T_total, H, d_k, d_v, dtype, chunk);
+    const Span ws{workspace, need};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Span& in : ins)
+            if (overlap(outs[i], in)) return fail(KDA_ERR_ALIAS, "%s: a gradient output overlaps an input", name);
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlap(outs[i], outs[j])) return fail(KDA_ERR_ALIAS, "%s: gradient outputs overlap", name);
+        if (overlap(outs[i], ws)) return fail(KDA_ERR_ALIAS, "%s: a gradient output overlaps the workspace", name);
+    }
+    for (const Span& in : ins)
+        if (overlap(ws, in)) return fail(KDA_ERR_ALIAS, "%s: the workspace overlaps an input", name);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(KDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (injected_launch_failure()) return fail(KDA_ERR_HIP, "%s: injected launch failure (KDA_TEST_FAIL_LAUNCH)", name);
+    kda::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cu = cu_seqlens; a.N = N; a.T_total = T_total;
+    a.H = H; a.dk = d_k; a.dv = d_v; a.chunk = chunk; a.bf16 = dtype == KDA_BF16; a.gate_head = op.gate_head;
+    a.s0 = state_in; a.dO = d_out; a.dsT = d_state_out;
+    a.gq = dq; a.gk = dk; a.gv = dv; a.gg = dg; a.gbeta = dbeta; a.gs0 = d_state_in;
+    a.ws = static_cast<float*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    return check_hip(kda::launch_chunk_bwd(a, s), s, name);
 }
 
 int kda_decode_step_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,

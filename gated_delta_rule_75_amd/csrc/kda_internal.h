@@ -9,7 +9,17 @@ namespace kda {
 
 // Per-kernel event timing (diagnostics).  When timing is on for the calling
 // thread, launchers bracket each kernel with timed_begin/timed_end.
-enum KernelId { kKernelPrep = 1, kKernelState = 2, kKernelChunkF32 = 3, kKernelDecode = 4 };
+enum KernelId {
+    kKernelPrep = 1,
+    kKernelState = 2,
+    kKernelChunkF32 = 3,
+    kKernelDecode = 4,
+    kKernelBwdFactors = 5,
+    kKernelBwdFwdChain = 6,
+    kKernelBwdRevChain = 7,
+    kKernelBwdGradState = 8,
+    kKernelBwdGradChunk = 9
+};
 bool timing_on();
 void timed_begin(int kernel_id, hipStream_t s);
 void timed_end(hipStream_t s);
@@ -58,6 +68,35 @@ struct DecodeArgs {
     int prologue;   // raw inputs, as in PrefillArgs
     float gate_scale;
 };
+
+// Chunked backward.  Sequences are packed (device cu_seqlens [N+1]); outputs are fp32.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    const int32_t* cu;
+    int64_t N;
+    int64_t T_total;
+    int H, dk, dv, chunk;
+    int bf16;       // storage type of q, k, v, beta
+    int gate_head;  // g is [T_total, H]; gg is then [T_total, H] too
+    const float* s0;   // [N, H, dk, dv] or nullptr
+    const float* dO;   // [T_total, H, dv]
+    const float* dsT;  // [N, H, dk, dv] or nullptr
+    float* gq;         // [T_total, H, dk]
+    float* gk;         // [T_total, H, dk]
+    float* gv;         // [T_total, H, dv]
+    float* gg;         // [T_total, H, dk] or [T_total, H]
+    float* gbeta;      // [T_total, H]
+    float* gs0;        // [N, H, dk, dv] or nullptr
+    float* ws;
+};
+
+bool chunk_bwd_supported(int dk, int dv, int chunk);
+size_t chunk_bwd_workspace(int64_t N, int64_t T_total, int H, int dk, int dv, int chunk);
+hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s);
 
 // generic fp32-arithmetic chunked kernel (any supported shape, either storage type)
 bool chunk_f32_supported(int dk, int dv, int chunk);

@@ -64,7 +64,7 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
-typedef enum { KDA_OP_PREFILL = 0, KDA_OP_APPEND = 1, KDA_OP_DECODE = 2 } kda_op;
+typedef enum { KDA_OP_PREFILL = 0, KDA_OP_APPEND = 1, KDA_OP_DECODE = 2, KDA_OP_BACKWARD = 3 } kda_op;
 
 /*
  * Chunked prefill of B equal-length sequences of T tokens.
@@ -185,8 +185,45 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const float*
                        const float* state_in, float* state_out, float* out, int32_t N, int32_t H,
                        int32_t d_k, int32_t d_v, int32_t dtype, const kda_options* options, void* hip_stream);
 
+/*
+ * kda_chunked_backward — gradients of the chunked prefill (training).
+ *
+ * "Kimi K3, explained" ("How is KDA trained efficiently if it is a
+ * recurrence?"; "Training in chunks") states that training runs the same
+ * recurrence in chunks; it prints no gradient equations.  This call returns
+ * the derivative of the recurrence of kda_append_prefill (same inputs, same
+ * packed layout) with respect to every input, given the gradients of a loss L
+ * with respect to its outputs:
+ *   d_out        [T_total, H, d_v] float   dL/do (required when T_total > 0)
+ *   d_state_out  [N, H, d_k, d_v] float    dL/dS_T, or NULL (zero)
+ * and writes (all float, caller-owned, overlapping no input):
+ *   dq, dk       [T_total, H, d_k]         dL/dq, dL/dk
+ *   dv           [T_total, H, d_v]         dL/dv
+ *   dg           [T_total, H, d_k]         dL/dg (g = log alpha); [T_total, H]
+ *                                          with options->gate = KDA_GATE_HEAD
+ *   dbeta        [T_total, H]              dL/dbeta
+ *   d_state_in   [N, H, d_k, d_v]          dL/dS_0, or NULL (not wanted)
+ * q, k, v, g, beta, cu_seqlens, state_in, dtype and chunk are as for
+ * kda_append_prefill (a batch of B equal sequences is cu_seqlens = 0, T, 2T,
+ * ...).  The arithmetic is fp32 whatever dtype is.  Supported shapes:
+ * d_k = d_v in {16, 32, 64, 128}, chunk in {16, 32, 64}.  options may be NULL;
+ * only options->gate is honoured, and snapshot_every and prologue must be 0
+ * (KDA_ERR_UNSUPPORTED otherwise).  workspace: at least
+ * kda_workspace_size(KDA_OP_BACKWARD, N, T_total, H, d_k, d_v, dtype, chunk)
+ * bytes, 256-byte aligned; it holds the per-chunk factors, the states entering
+ * each chunk and the state gradients leaving it.  Asynchronous on hip_stream;
+ * errors as for the other calls.
+ */
+int kda_chunked_backward(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                         const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in,
+                         const float* d_out, const float* d_state_out, float* dq, float* dk, float* dv,
+                         float* dg, float* dbeta, float* d_state_in, int32_t H, int32_t d_k, int32_t d_v,
+                         int32_t dtype, int32_t chunk, void* workspace, size_t workspace_bytes,
+                         const kda_options* options, void* hip_stream);
+
 /* Workspace bytes an op needs (B_or_N sequences, T tokens per sequence for
- * KDA_OP_PREFILL or T_total for KDA_OP_APPEND).  0 for KDA_OP_DECODE.
+ * KDA_OP_PREFILL or T_total for KDA_OP_APPEND and KDA_OP_BACKWARD).  0 for
+ * KDA_OP_DECODE.
  * Returns (size_t)-1 for an unsupported or invalid combination. */
 size_t kda_workspace_size(int32_t op, int64_t B_or_N, int64_t T, int32_t H, int32_t d_k, int32_t d_v,
                           int32_t dtype, int32_t chunk);
@@ -218,7 +255,12 @@ typedef enum {
     KDA_KERNEL_PREP = 1,      /* chunk-parallel prep of the matrix-core prefill */
     KDA_KERNEL_STATE = 2,     /* sequential state pass of the matrix-core prefill */
     KDA_KERNEL_CHUNK_F32 = 3, /* fp32 chunked prefill */
-    KDA_KERNEL_DECODE = 4     /* decode step */
+    KDA_KERNEL_DECODE = 4,    /* decode step */
+    KDA_KERNEL_BWD_FACTORS = 5,    /* backward: per-chunk factors */
+    KDA_KERNEL_BWD_FWD_CHAIN = 6,  /* backward: states entering each chunk */
+    KDA_KERNEL_BWD_REV_CHAIN = 7,  /* backward: state gradients, chunks in reverse */
+    KDA_KERNEL_BWD_GRAD_STATE = 8, /* backward: products over the value axis */
+    KDA_KERNEL_BWD_GRAD_CHUNK = 9  /* backward: in-chunk gradients */
 } kda_kernel;
 
 int kda_timing_begin(void);

@@ -27,6 +27,7 @@ _OUT = {"f64": (0, np.float64), "f32": (1, np.float32), "bf16": (2, np.uint16), 
 
 # tensor ids inside one workload's stream
 TID_Q, TID_K, TID_V, TID_BETA, TID_G, TID_S0, TID_RATE, TID_LENS = 1, 2, 3, 4, 5, 6, 7, 8
+TID_DO, TID_DST = 9, 10
 
 
 def lib_path() -> str:
@@ -184,6 +185,14 @@ def gen_state(w: Workload, N: int, threads=None):
     if w.s0_std <= 0:
         return None
     return fill(K_NORMAL, w.seed, TID_S0, (N, w.H, w.dk, w.dv), "f32", p0=w.s0_std, threads=threads)
+
+
+def gen_cotangents(w: Workload, T: int, N: int, threads=None):
+    """Upstream gradients of a loss for the backward pass: dL/do [T, H, dv] and dL/dS_T
+    [N, H, dk, dv], both fp32 ~ N(0, 1)."""
+    d_out = fill(K_NORMAL, w.seed, TID_DO, (T, w.H, w.dv), "f32", p0=1.0, threads=threads)
+    d_sT = fill(K_NORMAL, w.seed, TID_DST, (N, w.H, w.dk, w.dv), "f32", p0=1.0, threads=threads)
+    return d_out, d_sT
 
 
 def gen_lengths(w: Workload, N: int, lo: int, hi: int) -> list:

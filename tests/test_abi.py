@@ -143,3 +143,41 @@ def test_python_options_marshalling():
                                                                                                    1, 0.5)
     assert ctypes.sizeof(o) == 32  # int32, int32, pointer, pointer, int32, float
     assert kda._options(_l.KDA_GATE_CHANNEL) is not None
+
+
+def test_backward_call_is_validated():
+    """kda_chunked_backward: shapes, required buffers, options, aliasing and workspace are checked
+    on the host before anything is launched."""
+    import ctypes
+
+    _l, L = _lib()
+    base = 1 << 40
+    p = [base + i * (1 << 30) for i in range(20)]  # valid, non-overlapping fake buffers
+    N, T, H, d, C = 1, 64, 2, 16, 16
+    need = L.kda_workspace_size(_l.KDA_OP_BACKWARD, N, T, H, d, d, 0, C)
+    assert 0 < need < (1 << 40) and L.kda_is_supported(_l.KDA_OP_BACKWARD, 0, d, d, C) == 1
+    assert L.kda_is_supported(_l.KDA_OP_BACKWARD, 1, 128, 64, 64) == 0  # d_k != d_v
+
+    def call(**kw):
+        a = dict(q=p[0], k=p[1], v=p[2], g=p[3], beta=p[4], cu=p[5], s0=None, d_out=p[6], dsT=None, dq=p[7],
+                 dk=p[8], dv=p[9], dg=p[10], db=p[11], ds0=None, d_k=d, d_v=d, chunk=C, ws=p[12], ws_bytes=need,
+                 opts=None)
+        a.update(kw)
+        return L.kda_chunked_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], N, T, a["s0"], a["d_out"],
+                                      a["dsT"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["ds0"], H, a["d_k"],
+                                      a["d_v"], 0, a["chunk"], a["ws"], a["ws_bytes"], a["opts"], None)
+
+    assert call(d_v=32) == _l.KDA_ERR_UNSUPPORTED
+    assert call(chunk=128) == _l.KDA_ERR_UNSUPPORTED
+    assert call(d_out=None) == _l.KDA_ERR_INVALID_ARG and b"d_out" in L.kda_last_error()
+    assert call(cu=None) == _l.KDA_ERR_INVALID_ARG
+    assert call(dq=p[0]) == _l.KDA_ERR_ALIAS  # a gradient on top of q
+    assert call(dk=p[7]) == _l.KDA_ERR_ALIAS  # two gradients on one buffer
+    assert call(ws=p[6]) == _l.KDA_ERR_ALIAS  # workspace on top of d_out
+    assert call(ws_bytes=need - 1) == _l.KDA_ERR_WORKSPACE
+    assert call(ws=None) == _l.KDA_ERR_WORKSPACE
+    assert call(dg=p[10] + 2) == _l.KDA_ERR_MISALIGNED
+    snap = ctypes.byref(_l.Options(0, 1, p[13], p[14], 0, 0.0))
+    assert call(opts=snap) == _l.KDA_ERR_UNSUPPORTED and b"snapshots" in L.kda_last_error()
+    pro = ctypes.byref(_l.Options(0, 0, None, None, 1, 1.0))
+    assert call(opts=pro) == _l.KDA_ERR_UNSUPPORTED
