@@ -30,6 +30,20 @@ PREFILL_BYTES_PER_TOKEN_HEAD = 256 + 256 + 256 + 512 + 2 + 512          # 1794
 PREP_BYTES_PER_TOKEN_HEAD = 256 + 256 + 512 + 2                         # q, k, g, beta read by the prep kernel
 STATE_BYTES_PER_TOKEN_HEAD = 256 + 2 + 512                              # v, beta read, o written by the state pass
 PREFILL_FLOP_PER_TOKEN_HEAD = 139264                                    # chunked form, d=128, C=64
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix-core peak
+# chunked backward, per token-head: read q, k, v (bf16), g (fp32), beta (bf16), dL/do (fp32); write
+# dq, dk, dv, dg (fp32) and dbeta (fp32)
+BWD_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 2 + 512 + 4 * 512 + 4       # 3846
+
+
+def bwd_flop_per_chunk(C, d):
+    """Matrix products of one chunk's backward (d_k = d_v = d), 2 flop per multiply-add:
+    16 C d^2  state-sized products: W S0, K'^T D (states entering each chunk); K' dS1, Q+^T dO,
+              W^T dD (state gradients); D dS1^T, dO S0^T, dD S0^T (their gradients)
+    14 C^2 d  in-chunk products (triangular ones at half size): P, M, W, U; M^T dO; dM; dT (two);
+              T^T dD, T^T dW; the four pairwise contractions of dP and dM
+    C^3       the inverse T and dA = -T^T dT T^T"""
+    return 16 * C * d * d + 14 * C * C * d + C ** 3
 DECODE_BYTES_PER_SEQ_HEAD = 65536 + 65536 + 768 + 512 + 2 + 512         # 132866
 
 
@@ -112,6 +126,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=3, help="timed chunked-backward passes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (the HBM-counter calibration kernel) and exit")
     return ap.parse_args()
@@ -290,6 +306,86 @@ def oracle_sample(args, res, out, wide_all):
     log(f"[oracle] {Ts / t:.1f} tokens/s; parity max err {err:.2e}")
 
 
+def bench_backward(args, res, wide_all):
+    """The chunked backward (training) on the headline prefill's inputs: one pass = one
+    kda_chunked_backward call over all T tokens and H heads with dL/do ~ N(0, 1), dL/dS_T = 0 and
+    a zero initial state.  Parity: one head's gradients on the last tokens, against the oracle's
+    derivative started from the oracle's own state at that point."""
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_75_amd as kda
+    import oracle
+    import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.workload("metric")
+    q, k, v, g, b = wide_all
+    T, H, d = q.shape[0], w.H, w.dk
+    C = 64
+    d_out, _ = synth.gen_cotangents(w, T, 1)
+    tq, tk, tv, tb = (upload(x, "bf16", dev) for x in (q, k, v, b))
+    tg, tdo = upload(g, "f32", dev), upload(d_out, "f32", dev)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    ws = torch.empty(kda.workspace_size(3, 1, T, H, d, d, torch.bfloat16, C), dtype=torch.uint8, device=dev)
+
+    def step():
+        return kda.chunked_backward(tq, tk, tv, tg, tb, cu, None, d_out=tdo, chunk=C, state_grad=False,
+                                    workspace=ws)
+
+    log(f"[backward] T={T} H={H} d={d}: warmup 1, timing {args.backward_steps} passes "
+        f"(workspace {ws.numel() / 2**30:.1f} GiB)")
+    step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.backward_steps)]
+    with kda.kernel_timing() as kt:
+        for e0, e1 in ev:
+            e0.record()
+            grads = step()
+            e1.record()
+        torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg_ms = sum(ms) / len(ms)
+    per = {}
+    for name, t in kt.records:
+        per.setdefault(name, []).append(t)
+    kernels = {n: round(sum(x) / args.backward_steps, 4) for n, x in per.items()}
+    th = T * H
+    flop = bwd_flop_per_chunk(C, d) * (T // C) * H
+    nbytes = BWD_BYTES_PER_TOKEN_HEAD * th
+    tflops = flop / (avg_ms * 1e-3) / 1e12
+    gbps = nbytes / (avg_ms * 1e-3) / 1e9
+    # parity: head 0, last n tokens; the oracle's state entering them from its own forward run
+    n, h = 1024, 0
+    wide = [synth.to_f64(q[:, h:h + 1], "bf16"), synth.to_f64(k[:, h:h + 1], "bf16"),
+            synth.to_f64(v[:, h:h + 1], "bf16"), g[:, h:h + 1].astype(np.float64),
+            synth.to_f64(b[:, h:h + 1], "bf16")]
+    t0 = time.perf_counter()
+    _, s_mid = oracle.recurrence(*(x[:T - n] for x in wide), threads=1)
+    ref = oracle.backward(*(x[T - n:] for x in wide), None, s_mid, d_o=d_out[T - n:, h:h + 1], threads=1)
+    t_or = time.perf_counter() - t0
+    err = 0.0
+    for x, y in zip(grads[:5], ref[:5]):
+        xg = x[T - n:, h:h + 1].detach().cpu().numpy().astype(np.float64)
+        err = max(err, float(np.abs(xg - y).max() / max(np.abs(y).max(), 1e-30)))
+    res["next_rows"]["chunked_backward"] = {
+        "workload": f"gradients of the headline prefill (T={T}, H={H}, d={d}, chunk {C}, bf16 inputs, fp32 "
+                    "arithmetic); dL/do ~ N(0,1)",
+        "ms_per_pass": round(avg_ms, 3), "min_pass_ms": round(min(ms), 3),
+        "tokens_per_s": round(T / (avg_ms * 1e-3), 1), "kernels_ms_per_pass": kernels,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
+                     "algorithmic_flop_per_launch": flop, "dtype": "f32"},
+        "hbm": {"achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": nbytes},
+        "parity": {"head": h, "last_tokens": n, "max_rel_err": err, "tol": 2e-3, "ok": bool(err <= 2e-3),
+                   "oracle_s": round(t_or, 1)},
+    }
+    log(f"[backward] {avg_ms:.3f} ms/pass ({T / (avg_ms * 1e-3) / 1e6:.2f} M tokens/s), {tflops:.1f} TFLOP/s "
+        f"fp32 algorithmic, kernels {kernels}; parity {err:.2e}")
+
+
 def bench_decode(args, res):
     import numpy as np
     import torch
@@ -406,7 +502,11 @@ def main():
         out, sT, wide_all = bench_prefill(args, res)
         if not args.no_cpu_baseline:
             oracle_sample(args, res, out, wide_all)
-        del out, sT, wide_all
+        del out, sT
+        torch.cuda.empty_cache()
+        if not args.skip_backward:
+            bench_backward(args, res, wide_all)
+        del wide_all
         torch.cuda.empty_cache()
     if not args.skip_decode:
         bench_decode(args, res)

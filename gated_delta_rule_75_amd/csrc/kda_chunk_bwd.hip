@@ -200,16 +200,7 @@ __global__ __launch_bounds__(kThreads) void factors_kernel(BwdArgs a, Map<C> mp)
     }
     __syncthreads();
 
-    // T = (I + Diag(beta) P)^{-1}: thread j owns column j, forward substitution down the rows
-    if (tid < C) {
-        const int j = tid;
-        for (int r = 0; r < C; ++r) {
-            float acc = 0.f;
-            for (int s = j; s < r; ++s) acc += sP[r * LC + s] * sT[s * LC + j];
-            sT[r * LC + j] = r < j ? 0.f : (r == j ? 1.f : -sB[r] * acc);
-        }
-    }
-    // Q+, K', gamma, M, P out; then K becomes beta K+ in place
+    // Q+, K', gamma, M, P out
     for (int e = tid; e < C * DK; e += kThreads) {
         const int r = e / DK, cc = e % DK;
         const float g = sG[r * LK + cc], gl = sG[(C - 1) * LK + cc];
@@ -223,6 +214,13 @@ __global__ __launch_bounds__(kThreads) void factors_kernel(BwdArgs a, Map<C> mp)
         rec[R::P + e] = sP[r * LC + s];
     }
     __syncthreads();
+    // A = Diag(beta) P into M's buffer; T zeroed; K becomes beta K+ and q's buffer beta V
+    float* sA = sM;
+    for (int e = tid; e < C * C; e += kThreads) {
+        const int r = e / C, s = e % C;
+        sA[r * LC + s] = sB[r] * sP[r * LC + s];
+        sT[r * LC + s] = 0.f;
+    }
     for (int e = tid; e < C * DK; e += kThreads) {
         const int r = e / DK, cc = e % DK;
         sK[r * LK + cc] *= sB[r] * fast_exp(sG[r * LK + cc]);
@@ -231,11 +229,47 @@ __global__ __launch_bounds__(kThreads) void factors_kernel(BwdArgs a, Map<C> mp)
         const int r = e / DV, j = e % DV;
         sX[r * LX + j] = r < L ? sB[r] * ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j) : 0.f;
     }
-    for (int e = tid; e < C * C; e += kThreads) rec[R::T + e] = sT[(e / C) * LC + e % C];
     __syncthreads();
 
-    // W = T (beta K+), U = T (beta V): 16x16 tiles over the waves
+    // T = (I + A)^{-1}, unit lower triangular.  Diagonal 16x16 blocks by forward substitution (lane =
+    // column, the block's rows in registers); then the blocks below the diagonal, nearest first:
+    // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj.
     constexpr int NR = C / 16;
+    if (w < NR && lane < 16) {
+        const int j = lane, o = 16 * w;
+        float tc[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < rr; ++s2) acc += sA[(o + rr) * LC + o + s2] * tc[s2];
+            tc[rr] = rr < j ? 0.f : (rr == j ? 1.f : -acc);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sT[(o + rr) * LC + o + j] = tc[rr];
+    }
+    __syncthreads();
+    float* sXs = sP + w * 16 * 17;  // per-wave 16x16 scratch (P is in the record already)
+    for (int dist = 1; dist < NR; ++dist) {
+        const int j = w, i = w + dist;
+        if (i < NR) {
+            floatx4 acc = zero4();
+            for (int m = j; m < i; ++m)
+                acc = mma<4>(sA + 16 * i * LC + 16 * m, LC, 1, sT + 16 * m * LC + 16 * j, LC, 1, acc, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sXs[(4 * (lane >> 4) + e) * 17 + (lane & 15)] = acc[e];
+        }
+        __syncthreads();
+        if (i < NR) {
+            const floatx4 t = mma<4>(sT + 16 * i * LC + 16 * i, LC, 1, sXs, 17, 1, zero4(), lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * (lane >> 4) + e) * LC + 16 * j + (lane & 15)] = -t[e];
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < C * C; e += kThreads) rec[R::T + e] = sT[(e / C) * LC + e % C];
+
+    // W = T (beta K+), U = T (beta V): 16x16 tiles over the waves
     for (int t = w; t < NR * (DK / 16); t += 4) {
         const int rb = t % NR, cb = t / NR;
         floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, sK + 16 * cb, LK, 1, zero4(), lane);
@@ -251,12 +285,53 @@ __global__ __launch_bounds__(kThreads) void factors_kernel(BwdArgs a, Map<C> mp)
 }
 
 // ------------------------------------------------------------------------------------------
+// Chain operands: the next chunk's record rows are loaded into registers while the current chunk
+// computes from LDS, then written to LDS for the next step.  rows x cols floats (cols a multiple
+// of 4) go to an LDS array with row stride ld.
+// ------------------------------------------------------------------------------------------
+template <int ROWS, int COLS>
+struct Stage {
+    static constexpr int kVec = ROWS * COLS / 4;
+    static constexpr int kPer = (kVec + kThreads - 1) / kThreads;
+    float4 r[kPer];
+    // src: row-major with row stride src_ld floats (16-byte aligned rows)
+    __device__ __forceinline__ void load(const float* src, int64_t src_ld) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int e = threadIdx.x + m * kThreads;
+            if (kVec % kThreads == 0 || e < kVec) {
+                const int row = e / (COLS / 4), c4 = e % (COLS / 4);
+                r[m] = *reinterpret_cast<const float4*>(src + row * src_ld + 4 * c4);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(float* dst, int ld) const {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int e = threadIdx.x + m * kThreads;
+            if (kVec % kThreads == 0 || e < kVec) {
+                const int row = e / (COLS / 4), c4 = e % (COLS / 4);
+                float* p = dst + row * ld + 4 * c4;
+                p[0] = r[m].x;
+                p[1] = r[m].y;
+                p[2] = r[m].z;
+                p[3] = r[m].w;
+            }
+        }
+    }
+};
+
+// ------------------------------------------------------------------------------------------
 // fwd_chain: one workgroup per (sequence, head, 16 value columns); states entering each chunk
 // ------------------------------------------------------------------------------------------
 template <int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
-    constexpr int NVB = DV / kBV;
+    constexpr int NVB = DV / kBV, LW = DK + 4, LQ = DK + 16;
+    __shared__ float sW[C * LW];   // W rows (A operand by rows)
+    __shared__ float sKd[C * LQ];  // K' rows (A operand by columns)
+    __shared__ float sU[C * kBV];
+    __shared__ float sg[DK];
     __shared__ float sS[DK * kBV];
     __shared__ float sD[C * kBV];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -268,19 +343,37 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
         const int i = e / kBV, j = e % kBV;
         sS[e] = a.s0 ? a.s0[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] : 0.f;
     }
-    __syncthreads();
     const int64_t bos = mp.cu[n], eos = mp.cu[n + 1];
     const int64_t nck = (eos - bos + C - 1) / C, slot0 = mp.base(n);
+    if (nck == 0) return;  // uniform
+    Stage<C, DK> pW, pK;
+    Stage<C, kBV> pU;
+    Stage<1, DK> pg;
+    auto fetch = [&](int64_t c) {
+        const float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
+        pW.load(rec + R::W, DK);
+        pK.load(rec + R::Kd, DK);
+        pU.load(rec + R::U + vb * kBV, DV);
+        pg.load(rec + R::gam, DK);
+    };
+    fetch(0);
     for (int64_t c = 0; c < nck; ++c) {
         float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
+        __syncthreads();  // the previous chunk is done with the LDS operands; sS is its final state
+        pW.store(sW, LW);
+        pK.store(sKd, LQ);
+        pU.store(sU, kBV);
+        pg.store(sg, DK);
+        fetch(c + 1 < nck ? c + 1 : c);
         for (int e = tid; e < DK * kBV; e += kThreads) rec[R::S0 + (e / kBV) * DV + vb * kBV + e % kBV] = sS[e];
-        // D = U - W S (rows 16 w .. 16 w + 15 per wave)
+        __syncthreads();
+        // D = U - W S
         for (int rb = w; rb < C / 16; rb += 4) {
-            floatx4 acc = mma<DK / 4>(rec + R::W + 16 * rb * DK, DK, 1, sS, kBV, 1, zero4(), lane);
+            const floatx4 acc = mma<DK / 4>(sW + 16 * rb * LW, LW, 1, sS, kBV, 1, zero4(), lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * (lane >> 4) + e, j = lane & 15;
-                const float d = rec[R::U + r * DV + vb * kBV + j] - acc[e];
+                const float d = sU[r * kBV + j] - acc[e];
                 sD[r * kBV + j] = d;
                 rec[R::D + r * DV + vb * kBV + j] = d;
             }
@@ -292,13 +385,12 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * cb + 4 * (lane >> 4) + e;
-                acc[e] = rec[R::gam + i] * sS[i * kBV + (lane & 15)];
+                acc[e] = sg[i] * sS[i * kBV + (lane & 15)];
             }
-            acc = mma<C / 4>(rec + R::Kd + 16 * cb, 1, DK, sD, kBV, 1, acc, lane);
+            acc = mma<C / 4>(sKd + 16 * cb, 1, LQ, sD, kBV, 1, acc, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sS[(16 * cb + 4 * (lane >> 4) + e) * kBV + (lane & 15)] = acc[e];
         }
-        __syncthreads();
     }
 }
 
@@ -308,7 +400,12 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
 template <int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
-    constexpr int NVB = DV / kBV;
+    constexpr int NVB = DV / kBV, LW = DK + 4, LQ = DK + 16, LM = C + 16;
+    __shared__ float sKd[C * LW];  // K' rows (A operand by rows)
+    __shared__ float sM[C * LM];   // M (A operand by columns)
+    __shared__ float sQp[C * LQ];  // Q+ (A operand by columns)
+    __shared__ float sW[C * LQ];   // W (A operand by columns)
+    __shared__ float sg[DK];
     __shared__ float sdS[DK * kBV];
     __shared__ float sdO[C * kBV];
     __shared__ float sdD[C * kBV];
@@ -323,20 +420,46 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
     }
     const int64_t bos = mp.cu[n], eos = mp.cu[n + 1];
     const int64_t nck = (eos - bos + C - 1) / C, slot0 = mp.base(n);
+    Stage<C, DK> pK, pQ, pW;
+    Stage<C, C> pM;
+    Stage<1, DK> pg;
+    constexpr int kDoPer = (C * kBV + kThreads - 1) / kThreads;
+    float rdo[kDoPer];
+    auto fetch = [&](int64_t c) {
+        const float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
+        pK.load(rec + R::Kd, DK);
+        pM.load(rec + R::M, C);
+        pQ.load(rec + R::Qp, DK);
+        pW.load(rec + R::W, DK);
+        pg.load(rec + R::gam, DK);
+        const int64_t t0 = bos + c * C;
+#pragma unroll
+        for (int m = 0; m < kDoPer; ++m) {
+            const int e = tid + m * kThreads, r = e / kBV, j = e % kBV;
+            rdo[m] = (e < C * kBV && t0 + r < eos) ? a.dO[((t0 + r) * H + h) * (int64_t)DV + vb * kBV + j] : 0.f;
+        }
+    };
+    if (nck > 0) fetch(nck - 1);
     for (int64_t c = nck - 1; c >= 0; --c) {
         float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
-        const int64_t t0 = bos + c * C;
-        const int L = (int)(eos - t0 < C ? eos - t0 : C);
-        for (int e = tid; e < C * kBV; e += kThreads) {
-            const int r = e / kBV, j = e % kBV;
-            sdO[e] = r < L ? a.dO[((t0 + r) * H + h) * (int64_t)DV + vb * kBV + j] : 0.f;
+        __syncthreads();  // the previous chunk is done with the LDS operands; sdS is its result
+        pK.store(sKd, LW);
+        pM.store(sM, LM);
+        pQ.store(sQp, LQ);
+        pW.store(sW, LQ);
+        pg.store(sg, DK);
+#pragma unroll
+        for (int m = 0; m < kDoPer; ++m) {
+            const int e = tid + m * kThreads;
+            if (e < C * kBV) sdO[e] = rdo[m];
         }
-        __syncthreads();  // sdS (previous chunk or the initial load) and sdO complete
+        fetch(c > 0 ? c - 1 : c);
         for (int e = tid; e < DK * kBV; e += kThreads) rec[R::dS1 + (e / kBV) * DV + vb * kBV + e % kBV] = sdS[e];
+        __syncthreads();
         // dD = K' dS + M^T dO
         for (int rb = w; rb < C / 16; rb += 4) {
-            floatx4 acc = mma<DK / 4>(rec + R::Kd + 16 * rb * DK, DK, 1, sdS, kBV, 1, zero4(), lane);
-            acc = mma<C / 4>(rec + R::M + 16 * rb, 1, C, sdO, kBV, 1, acc, lane);
+            floatx4 acc = mma<DK / 4>(sKd + 16 * rb * LW, LW, 1, sdS, kBV, 1, zero4(), lane);
+            acc = mma<C / 4>(sM + 16 * rb, 1, LM, sdO, kBV, 1, acc, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * (lane >> 4) + e, j = lane & 15;
@@ -351,14 +474,13 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * cb + 4 * (lane >> 4) + e;
-                acc[e] = rec[R::gam + i] * sdS[i * kBV + (lane & 15)];
+                acc[e] = sg[i] * sdS[i * kBV + (lane & 15)];
             }
-            acc = mma<C / 4>(rec + R::Qp + 16 * cb, 1, DK, sdO, kBV, 1, acc, lane);
-            floatx4 wd = mma<C / 4>(rec + R::W + 16 * cb, 1, DK, sdD, kBV, 1, zero4(), lane);
+            acc = mma<C / 4>(sQp + 16 * cb, 1, LQ, sdO, kBV, 1, acc, lane);
+            const floatx4 wd = mma<C / 4>(sW + 16 * cb, 1, LQ, sdD, kBV, 1, zero4(), lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sdS[(16 * cb + 4 * (lane >> 4) + e) * kBV + (lane & 15)] = acc[e] - wd[e];
         }
-        __syncthreads();  // before the next chunk overwrites sdO and reads sdS
     }
     __syncthreads();
     if (a.gs0)
@@ -369,13 +491,20 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
 }
 
 // ------------------------------------------------------------------------------------------
-// grad_state: one workgroup per (chunk slot, head); the products over the value axis
+// grad_state: one workgroup per (chunk slot, head); the products over the value axis, staged
+// through LDS 32 value columns at a time
 // ------------------------------------------------------------------------------------------
 template <int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
-    constexpr int LV = DV + 1;
-    __shared__ float sdO[C * LV];
+    constexpr int JT = DV < 32 ? DV : 32, LJ = JT + 1;
+    constexpr int NR = C / 16, NC = DK / 16, NT3 = NR * NC, NTM = NR * NR;
+    constexpr int T3W = (NT3 + 3) / 4, TMW = (NTM + 3) / 4;
+    __shared__ float sD[C * LJ];
+    __shared__ float sdD[C * LJ];
+    __shared__ float sdO[C * LJ];
+    __shared__ float sS0[DK * LJ];
+    __shared__ float sdS1[DK * LJ];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t slot = blockIdx.x;
     int64_t n, c, t0;
@@ -383,44 +512,70 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
     if (!mp.locate(slot, n, c, t0, L)) return;
     const int H = a.H;
     float* rec = a.ws + (slot * H + h) * R::kFloats;
-    for (int e = tid; e < C * DV; e += kThreads) {
-        const int r = e / DV, j = e % DV;
-        sdO[r * LV + j] = r < L ? a.dO[((t0 + r) * H + h) * (int64_t)DV + j] : 0.f;
-    }
-    __syncthreads();
-    constexpr int NR = C / 16, NC = DK / 16;
-    // dK' = D dS1^T, dQ+ = dO S0^T, dW = -dD S0^T: [C][DK] each
-    for (int t = w; t < NR * NC; t += 4) {
-        const int rb = t % NR, cb = t / NR;
-        const floatx4 kd = mma<DV / 4>(rec + R::D + 16 * rb * DV, DV, 1, rec + R::dS1 + 16 * cb * DV, 1, DV, zero4(), lane);
-        const floatx4 qp = mma<DV / 4>(sdO + 16 * rb * LV, LV, 1, rec + R::S0 + 16 * cb * DV, 1, DV, zero4(), lane);
-        const floatx4 dw = mma<DV / 4>(rec + R::dD + 16 * rb * DV, DV, 1, rec + R::S0 + 16 * cb * DV, 1, DV, zero4(), lane);
+    floatx4 kd[T3W], qp[T3W], dw[T3W], dm[TMW];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t o = (16 * rb + 4 * (lane >> 4) + e) * DK + 16 * cb + (lane & 15);
-            rec[R::dKd + o] = kd[e];
-            rec[R::dQp + o] = qp[e];
-            rec[R::dW + o] = -dw[e];
-        }
-    }
-    // dM = tril(dO D^T): [C][C]
-    for (int t = w; t < NR * NR; t += 4) {
-        const int rb = t / NR, sb = t % NR;
-        floatx4 acc = zero4();
-        if (sb <= rb) acc = mma<DV / 4>(sdO + 16 * rb * LV, LV, 1, rec + R::D + 16 * sb * DV, 1, DV, acc, lane);
+    for (int m = 0; m < T3W; ++m) kd[m] = qp[m] = dw[m] = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rb + 4 * (lane >> 4) + e, s = 16 * sb + (lane & 15);
-            rec[R::dM + r * C + s] = s <= r ? acc[e] : 0.f;
+    for (int m = 0; m < TMW; ++m) dm[m] = zero4();
+    float dgam = 0.f;
+    for (int j0 = 0; j0 < DV; j0 += JT) {
+        for (int e = tid; e < C * JT; e += kThreads) {
+            const int r = e / JT, j = e % JT;
+            sD[r * LJ + j] = rec[R::D + r * DV + j0 + j];
+            sdD[r * LJ + j] = rec[R::dD + r * DV + j0 + j];
+            sdO[r * LJ + j] = r < L ? a.dO[((t0 + r) * H + h) * (int64_t)DV + j0 + j] : 0.f;
         }
+        for (int e = tid; e < DK * JT; e += kThreads) {
+            const int i = e / JT, j = e % JT;
+            sS0[i * LJ + j] = rec[R::S0 + i * DV + j0 + j];
+            sdS1[i * LJ + j] = rec[R::dS1 + i * DV + j0 + j];
+        }
+        __syncthreads();
+        // dK' = D dS1^T, dQ+ = dO S0^T, dW = -dD S0^T   ([C][DK] each)
+#pragma unroll
+        for (int m = 0; m < T3W; ++m) {
+            const int t = w + 4 * m, rb = t % NR, cb = t / NR;
+            if (t < NT3) {
+                kd[m] = mma<JT / 4>(sD + 16 * rb * LJ, LJ, 1, sdS1 + 16 * cb * LJ, 1, LJ, kd[m], lane);
+                qp[m] = mma<JT / 4>(sdO + 16 * rb * LJ, LJ, 1, sS0 + 16 * cb * LJ, 1, LJ, qp[m], lane);
+                dw[m] = mma<JT / 4>(sdD + 16 * rb * LJ, LJ, 1, sS0 + 16 * cb * LJ, 1, LJ, dw[m], lane);
+            }
+        }
+        // dM = tril(dO D^T)   ([C][C], the tiles on or below the diagonal)
+#pragma unroll
+        for (int m = 0; m < TMW; ++m) {
+            const int t = w + 4 * m, rb = t / NR, sb = t % NR;
+            if (t < NTM && sb <= rb)
+                dm[m] = mma<JT / 4>(sdO + 16 * rb * LJ, LJ, 1, sD + 16 * sb * LJ, 1, LJ, dm[m], lane);
+        }
+        // dgamma = rowsum(dS1 * S0)
+        if (tid < DK)
+            for (int j = 0; j < JT; ++j) dgam += sdS1[tid * LJ + j] * sS0[tid * LJ + j];
+        __syncthreads();
     }
-    // dgamma = rowsum(dS1 * S0): one row per wave step, lanes over the value columns
-    for (int i = w; i < DK; i += 4) {
-        float acc = 0.f;
-        for (int j = lane; j < DV; j += 64) acc += rec[R::dS1 + i * DV + j] * rec[R::S0 + i * DV + j];
-        for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-        if (lane == 0) rec[R::dgam + i] = acc;
+#pragma unroll
+    for (int m = 0; m < T3W; ++m) {
+        const int t = w + 4 * m, rb = t % NR, cb = t / NR;
+        if (t < NT3)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t o = (16 * rb + 4 * (lane >> 4) + e) * DK + 16 * cb + (lane & 15);
+                rec[R::dKd + o] = kd[m][e];
+                rec[R::dQp + o] = qp[m][e];
+                rec[R::dW + o] = -dw[m][e];
+            }
     }
+#pragma unroll
+    for (int m = 0; m < TMW; ++m) {
+        const int t = w + 4 * m, rb = t / NR, sb = t % NR;
+        if (t < NTM)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * (lane >> 4) + e, s = 16 * sb + (lane & 15);
+                rec[R::dM + r * C + s] = s <= r ? dm[m][e] : 0.f;
+            }
+    }
+    if (tid < DK) rec[R::dgam + tid] = dgam;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -428,11 +583,14 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
 // ------------------------------------------------------------------------------------------
 template <int DK, int DV, int C>
 struct ChunkLds {
-    static constexpr int LC = C + 1, LK = DK + 1, DX = DK > DV ? DK : DV, LX = DX + 1, LB = 17;
-    static constexpr int kStage = LX > 4 * LB ? LX : 4 * LB;  // floats per row of the staging area
+    static constexpr int LC = C + 1, LK = DK + 1, LB = 17;
+    static constexpr int JT = DV < 32 ? DV : 32, LJ = JT + 1;  // value columns per staged tile
+    static constexpr int CT = DK < 32 ? DK : 32, LCT = CT + 1; // key channels per staged tile
+    static constexpr int kStage0 = 3 * LJ > 2 * LCT ? 3 * LJ : 2 * LCT;
+    static constexpr int kStage = kStage0 > 5 * LB ? kStage0 : 5 * LB;  // floats per row of the staging area
     static constexpr size_t kFloats = 4 * (size_t)C * LC      // T, dM, dT -> dA -> dP, Z
                                       + (size_t)C * LK        // G
-                                      + (size_t)C * kStage    // beta V, beta K+, then the channel-block tiles
+                                      + (size_t)C * kStage    // staged tiles (see the kernel)
                                       + 4 * (size_t)C         // beta, dbeta, dg (one gate per head), spare
                                       + 2 * 16;               // per-block column sums
     static constexpr size_t kBytes = kFloats * sizeof(float);
@@ -442,23 +600,31 @@ template <int DK, int DV, int C, typename TI>
 __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
     using Lds = ChunkLds<DK, DV, C>;
-    constexpr int LC = Lds::LC, LK = Lds::LK, LX = Lds::LX, LB = Lds::LB, NR = C / 16;
+    constexpr int LC = Lds::LC, LK = Lds::LK, LB = Lds::LB, NR = C / 16;
+    constexpr int JT = Lds::JT, LJ = Lds::LJ, CT = Lds::CT, LCT = Lds::LCT;
     extern __shared__ float lds[];
     float* sT = lds;             // [C][LC]
     float* sdM = sT + C * LC;    // [C][LC]
     float* sA = sdM + C * LC;    // [C][LC]  dT, then dP
     float* sZ = sA + C * LC;     // [C][LC]
     float* sG = sZ + C * LC;     // [C][LK]
-    float* sX = sG + C * LK;     // [C][LX]
+    float* sX = sG + C * LK;     // [C][kStage] staging area
     float* sB = sX + C * Lds::kStage;  // [C]
     float* sdb = sB + C;         // [C]
     float* sdgh = sdb + C;       // [C]
     float* sCol = sdgh + 2 * C;  // [16] column sums of dK' * K' in the current channel block
-    // channel-block tiles inside sX: K, Q, dK+, dG, each [C][LB]
+    // staged tiles inside sX: value tiles dD, V, beta V ([C][LJ] each); key tiles dW, beta K+
+    // ([C][LCT] each); channel blocks K, Q, dK+, dG, dW ([C][LB] each)
+    float* tdD = sX;
+    float* tV = tdD + C * LJ;
+    float* tBV = tV + C * LJ;
+    float* tdW = sX;
+    float* tBK = tdW + C * LCT;
     float* tK = sX;
     float* tQ = tK + C * LB;
     float* tKp = tQ + C * LB;
     float* tdG = tKp + C * LB;
+    float* tW = tdG + C * LB;
 
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t slot = blockIdx.x;
@@ -482,37 +648,67 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
         sdb[tid] = 0.f;
         sdgh[tid] = 0.f;
     }
-    for (int e = tid; e < C * DV; e += kThreads) {
-        const int r = e / DV, j = e % DV;
-        sX[r * LX + j] = r < L ? ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j) : 0.f;  // V (beta applied below)
-    }
     cumulative_decay<DK, C>(a, t0, L, h, sG, LK);  // (ends with a barrier)
 
-    // ---- dT = dD (beta V)^T + dW (beta K+)^T, strictly lower part; wave w owns tiles w, w+4, ...
+    // ---- dT = dD (beta V)^T + dW (beta K+)^T, strictly lower part (wave w owns tiles w, w+4, ...),
+    //      and with the value tiles staged: dV = beta (T^T dD), dbeta += rowsum(V * T^T dD)
     constexpr int NT = NR * NR, TPW = (NT + 3) / 4;
     floatx4 dT[TPW];
 #pragma unroll
     for (int m = 0; m < TPW; ++m) dT[m] = zero4();
-    for (int e = tid; e < C * DV; e += kThreads) sX[(e / DV) * LX + e % DV] *= sB[e / DV];
-    __syncthreads();
+    for (int j0 = 0; j0 < DV; j0 += JT) {
+        for (int e = tid; e < C * JT; e += kThreads) {
+            const int r = e / JT, j = e % JT;
+            const float vv = r < L ? ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
+            tdD[r * LJ + j] = rec[R::dD + r * DV + j0 + j];
+            tV[r * LJ + j] = vv;
+            tBV[r * LJ + j] = sB[r] * vv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int t = w + 4 * m, rb = t / NR, sb = t % NR;
+            if (t < NT && sb <= rb)
+                dT[m] = mma<JT / 4>(tdD + 16 * rb * LJ, LJ, 1, tBV + 16 * sb * LJ, 1, LJ, dT[m], lane);
+        }
+        for (int t = w; t < NR * (JT / 16); t += 4) {
+            const int rb = t % NR, jb = t / NR;
+            const floatx4 x = mma<C / 4>(sT + 16 * rb, 1, LC, tdD + 16 * jb, LJ, 1, zero4(), lane);
+            float part[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * (lane >> 4) + e, j = 16 * jb + (lane & 15);
+                part[e] = tV[r * LJ + j] * x[e];
+                if (r < L) a.gv[((t0 + r) * H + h) * (int64_t)DV + j0 + j] = sB[r] * x[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = sum16(part[e]);
+                if ((lane & 15) == 0) atomicAdd(&sdb[16 * rb + 4 * (lane >> 4) + e], p);
+            }
+        }
+        __syncthreads();
+    }
+    for (int c0 = 0; c0 < DK; c0 += CT) {
+        for (int e = tid; e < C * CT; e += kThreads) {
+            const int r = e / CT, cc = e % CT;
+            tdW[r * LCT + cc] = rec[R::dW + r * DK + c0 + cc];
+            tBK[r * LCT + cc] = r < L ? sB[r] * ld_in<TI>(k, ((t0 + r) * H + h) * (int64_t)DK + c0 + cc) *
+                                            fast_exp(sG[r * LK + c0 + cc])
+                                      : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int t = w + 4 * m, rb = t / NR, sb = t % NR;
+            if (t < NT && sb <= rb)
+                dT[m] = mma<CT / 4>(tdW + 16 * rb * LCT, LCT, 1, tBK + 16 * sb * LCT, 1, LCT, dT[m], lane);
+        }
+        __syncthreads();
+    }
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
         const int t = w + 4 * m, rb = t / NR, sb = t % NR;
-        if (t < NT && sb <= rb)
-            dT[m] = mma<DV / 4>(rec + R::dD + 16 * rb * DV, DV, 1, sX + 16 * sb * LX, 1, LX, dT[m], lane);
-    }
-    __syncthreads();
-    for (int e = tid; e < C * DK; e += kThreads) {
-        const int r = e / DK, cc = e % DK;
-        sX[r * LX + cc] = r < L ? sB[r] * ld_in<TI>(k, ((t0 + r) * H + h) * (int64_t)DK + cc) * fast_exp(sG[r * LK + cc])
-                                : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < TPW; ++m) {
-        const int t = w + 4 * m, rb = t / NR, sb = t % NR;
-        if (t < NT && sb <= rb)
-            dT[m] = mma<DK / 4>(rec + R::dW + 16 * rb * DK, DK, 1, sX + 16 * sb * LX, 1, LX, dT[m], lane);
         if (t < NT)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -557,24 +753,6 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
             }
         }
     }
-    // ---- dV = beta (T^T dD), dbeta += rowsum(V * T^T dD)
-    for (int t = w; t < NR * (DV / 16); t += 4) {
-        const int rb = t % NR, jb = t / NR;
-        const floatx4 x = mma<C / 4>(sT + 16 * rb, 1, LC, rec + R::dD + 16 * jb, DV, 1, zero4(), lane);
-        float part[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rb + 4 * (lane >> 4) + e, j = 16 * jb + (lane & 15);
-            const float vv = r < L ? ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j) : 0.f;
-            part[e] = vv * x[e];
-            if (r < L) a.gv[((t0 + r) * H + h) * (int64_t)DV + j] = sB[r] * x[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float p = sum16(part[e]);
-            if ((lane & 15) == 0) atomicAdd(&sdb[16 * rb + 4 * (lane >> 4) + e], p);
-        }
-    }
     __syncthreads();  // dP complete; sX free
 
     // ---- channel blocks of 16: dK+, the pairwise sweeps, dq, dk, dG and its suffix sums
@@ -584,17 +762,18 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
             const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + 16 * cb + cc;
             tK[r * LB + cc] = r < L ? ld_in<TI>(k, idx) : 0.f;
             tQ[r * LB + cc] = r < L ? ld_in<TI>(q, idx) : 0.f;
+            tW[r * LB + cc] = rec[R::dW + r * DK + 16 * cb + cc];
         }
         if (tid < 16) sCol[tid] = 0.f;
+        __syncthreads();
         // X2 = T^T dW (rows block w), dK+ = beta X2, dbeta += rowsum(K+ * X2)
         if (w < NR) {
-            const floatx4 x = mma<C / 4>(sT + 16 * w, 1, LC, rec + R::dW + 16 * cb, DK, 1, zero4(), lane);
+            const floatx4 x = mma<C / 4>(sT + 16 * w, 1, LC, tW, LB, 1, zero4(), lane);
             float part[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + 4 * (lane >> 4) + e, cc = lane & 15;
-                const float kk = r < L ? ld_in<TI>(k, ((t0 + r) * H + h) * (int64_t)DK + 16 * cb + cc) : 0.f;
-                part[e] = kk * fast_exp(sG[r * LK + 16 * cb + cc]) * x[e];
+                part[e] = tK[r * LB + cc] * fast_exp(sG[r * LK + 16 * cb + cc]) * x[e];
                 tKp[r * LB + cc] = sB[r] * x[e];
             }
 #pragma unroll
