@@ -114,46 +114,55 @@ __device__ __forceinline__ float gate_at(const float* g, int gate_head, int64_t 
     return gate_head ? g[t * H + h] : g[(t * H + h) * (int64_t)DK + c];
 }
 
-// In-chunk cumulative log-decay into G[C][ldg] (rows >= L take g = 0, so they repeat G[L-1]).
-// Thread (c, half) sums its half of the rows in registers; the second half then adds the first's total.
-template <int DK, int C>
-__device__ __forceinline__ void cumulative_decay(const BwdArgs& a, int64_t t0, int L, int h, float* G, int ldg) {
-    constexpr int HALF = C / 2;
-    for (int task = threadIdx.x; task < 2 * DK; task += kThreads) {
-        const int c = task % DK, half = task / DK;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int i = 0; i < HALF; ++i) {
-            const int r = half * HALF + i;
-            acc += r < L ? gate_at(a.g, a.gate_head, t0 + r, a.H, h, DK, c) : 0.f;
-            G[r * ldg + c] = acc;
-        }
+// Rows 16 w .. 16 w + 15 of G = tril(ones) g for one 16-channel block (g staged as [C][ldg]);
+// the result has the MFMA accumulator layout (row 16 w + 4 (lane >> 4) + e, column lane & 15).
+template <int C>
+__device__ __forceinline__ floatx4 prefix_rows(const float* g, int ldg, int w, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+    floatx4 acc = zero4();
+#pragma unroll 4
+    for (int ks = 0; ks < C / 4; ++ks) {
+        const int s = 4 * ks + kq;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s <= 16 * w + r ? 1.f : 0.f, g[s * ldg + r], acc, 0, 0, 0);
     }
-    __syncthreads();
-    for (int task = threadIdx.x; task < DK * HALF; task += kThreads) {
-        const int c = task % DK, r = HALF + task / DK;
-        G[r * ldg + c] += G[(HALF - 1) * ldg + c];
-    }
-    __syncthreads();
+    return acc;
 }
 
 // ------------------------------------------------------------------------------------------
-// factors: one workgroup per (chunk slot, head)
+// factors: one workgroup per (chunk slot, head), under 80 KB of LDS (two per CU).  Key channels
+// are visited in tiles of 32, each tile's cumulative log-decay recomputed there as a product with
+// a lower-triangular matrix of ones.
+//   pass 1: P and M.  Pairs (r, s) in different 16-row blocks i > j use the matrix cores with the
+//           decay split at m, the last row of block j: exp(G_r - G_s) = exp(G_r - G_m) exp(G_m - G_s),
+//           both exponents <= 0, applied to the operands as they are loaded.  Pairs inside a block
+//           take the exponential of their own difference on the vector ALUs.
+//   then T = (I + Diag(beta) P)^{-1};
+//   pass 2: Q+, K', gamma and W = T (beta K+) per channel tile;  pass 3: U = T (beta V) per value tile.
 // ------------------------------------------------------------------------------------------
-template <int DK, int DV, int C, typename TI>
-__global__ __launch_bounds__(kThreads) void factors_kernel(BwdArgs a, Map<C> mp) {
-    using R = Rec<DK, DV, C>;
-    constexpr int LK = DK + 1, DX = DK > DV ? DK : DV, LX = DX + 1, LC = C + 1;
-    extern __shared__ float lds[];
-    float* sK = lds;             // [C][LK]  k, then beta K+
-    float* sX = sK + C * LK;     // [C][LX]  q, then beta V
-    float* sG = sX + C * LX;     // [C][LK]
-    float* sP = sG + C * LK;     // [C][LC]
-    float* sM = sP + C * LC;     // [C][LC]
-    float* sT = sM + C * LC;     // [C][LC]
-    float* sB = sT + C * LC;     // [C]
+template <int DK, int DV, int C>
+struct FactorsLds {
+    static constexpr int LC = C + 1, CT = 32, LT = CT + 1;
+    static constexpr size_t kFloats = 3 * (size_t)C * LC + 3 * (size_t)C * LT + C;
+    static constexpr size_t kBytes = kFloats * sizeof(float);
+};
 
-    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+template <int DK, int DV, int C, typename TI>
+__global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> mp) {
+    using R = Rec<DK, DV, C>;
+    using Lds = FactorsLds<DK, DV, C>;
+    constexpr int LC = Lds::LC, LT = Lds::LT, NR = C / 16;
+    constexpr int CT = DK < Lds::CT ? DK : Lds::CT;  // channels per tile
+    constexpr int VT = DV < Lds::CT ? DV : Lds::CT;  // value columns per tile
+    extern __shared__ float lds[];
+    float* sP = lds;            // [C][LC]
+    float* sM = sP + C * LC;    // [C][LC]  M, then A = Diag(beta) P
+    float* sT = sM + C * LC;    // [C][LC]
+    float* tK = sT + C * LC;    // [C][LT]  k, then beta K+
+    float* tQ = tK + C * LT;    // [C][LT]  q, then beta V
+    float* tG = tQ + C * LT;    // [C][LT]  g, then G
+    float* sB = tG + C * LT;    // [C]
+
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int64_t slot = blockIdx.x;
     int64_t n, c, t0;
     int L;
@@ -164,77 +173,143 @@ __global__ __launch_bounds__(kThreads) void factors_kernel(BwdArgs a, Map<C> mp)
     const TI* v = static_cast<const TI*>(a.v);
     const TI* beta = static_cast<const TI*>(a.beta);
     float* rec = a.ws + (slot * H + h) * R::kFloats;
-
-    for (int e = tid; e < C * DK; e += kThreads) {
-        const int r = e / DK, cc = e % DK;
-        const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + cc;
-        sK[r * LK + cc] = r < L ? ld_in<TI>(k, idx) : 0.f;
-        sX[r * LX + cc] = r < L ? ld_in<TI>(q, idx) : 0.f;
-    }
     if (tid < C) sB[tid] = tid < L ? ld_in<TI>(beta, (t0 + tid) * H + h) : 0.f;
-    cumulative_decay<DK, C>(a, t0, L, h, sG, LK);  // (ends with a barrier)
 
-    // pairwise P and M: thread owns column s, rows r = rg, rg + NG, ...
-    {
-        constexpr int NG = kThreads / C;
-        const int s = tid % C, rg = tid / C;
-        for (int r = rg; r < C; r += NG) {
-            float p = 0.f, m = 0.f;
-            if (s <= r) {
-                const float* kr = sK + r * LK;
-                const float* ks = sK + s * LK;
-                const float* qr = sX + r * LX;
-                const float* gr = sG + r * LK;
-                const float* gs = sG + s * LK;
+    // stage channel tile c0 .. c0 + CT - 1 (k, q, g; rows >= L are zero), then G = tril(ones) g
+    auto stage_tile = [&](int c0) {
+        for (int e = tid; e < C * CT; e += kThreads) {
+            const int r = e / CT, cc = e % CT;
+            const bool in = r < L;
+            const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + c0 + cc;
+            tK[r * LT + cc] = in ? ld_in<TI>(k, idx) : 0.f;
+            tQ[r * LT + cc] = in ? ld_in<TI>(q, idx) : 0.f;
+            tG[r * LT + cc] = in ? gate_at(a.g, a.gate_head, t0 + r, H, h, DK, c0 + cc) : 0.f;
+        }
+        __syncthreads();
+        constexpr int NCT = CT / 16;
+        floatx4 G[(NR * NCT + 3) / 4];
+#pragma unroll
+        for (int m = 0; m < (NR * NCT + 3) / 4; ++m) {
+            const int t = w + 4 * m, rb = t % NR, cb = t / NR;
+            if (t < NR * NCT) G[m] = prefix_rows<C>(tG + 16 * cb, LT, rb, lane);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < (NR * NCT + 3) / 4; ++m) {
+            const int t = w + 4 * m, rb = t % NR, cb = t / NR;
+            if (t < NR * NCT)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tG[(16 * rb + 4 * lg + e) * LT + 16 * cb + lr] = G[m][e];
+        }
+        __syncthreads();
+    };
+
+    // ---- pass 1: P and M
+    constexpr int NPAIR = NR * (NR - 1) / 2, PPW = (NPAIR + 3) / 4;  // off-diagonal block pairs
+    floatx4 accP[PPW > 0 ? PPW : 1], accM[PPW > 0 ? PPW : 1];
+    int pi[PPW > 0 ? PPW : 1], pj[PPW > 0 ? PPW : 1];
+#pragma unroll
+    for (int m = 0; m < PPW; ++m) {
+        accP[m] = accM[m] = zero4();
+        int t = w + 4 * m, i = 1;
+        while (t >= i) { t -= i; ++i; }  // pair index -> (i, j), j < i
+        pi[m] = i;
+        pj[m] = t;
+    }
+    constexpr int NDIAG = NR * 136, DPT = (NDIAG + kThreads - 1) / kThreads;  // pairs s <= r inside a block
+    float dp[DPT], dm[DPT];
+    int dr[DPT], ds[DPT];
+#pragma unroll
+    for (int m = 0; m < DPT; ++m) {
+        dp[m] = dm[m] = 0.f;
+        int t = tid + kThreads * m;
+        const int blk = t / 136;
+        t %= 136;
+        int rr = 0;
+        while (t > rr) { t -= rr + 1; ++rr; }
+        dr[m] = 16 * blk + rr;
+        ds[m] = 16 * blk + t;
+    }
+    for (int c0 = 0; c0 < DK; c0 += CT) {
+        stage_tile(c0);
+#pragma unroll
+        for (int m = 0; m < PPW; ++m) {
+            if (w + 4 * m < NPAIR) {
+                const int ra = 16 * pi[m] + lr, sb = 16 * pj[m] + lr, mj = 16 * pj[m] + 15;
 #pragma unroll 4
-                for (int cc = 0; cc < DK; ++cc) {
-                    const float e = fast_exp(gr[cc] - gs[cc]);
-                    const float ke = ks[cc] * e;
-                    p += kr[cc] * ke;
-                    m += qr[cc] * ke;
+                for (int ks = 0; ks < CT / 4; ++ks) {
+                    const int cc = 4 * ks + lg;
+                    const float gm = tG[mj * LT + cc];
+                    const float ea = fast_exp(tG[ra * LT + cc] - gm);
+                    const float bb = tK[sb * LT + cc] * fast_exp(gm - tG[sb * LT + cc]);
+                    accP[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(tK[ra * LT + cc] * ea, bb, accP[m], 0, 0, 0);
+                    accM[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(tQ[ra * LT + cc] * ea, bb, accM[m], 0, 0, 0);
                 }
             }
-            sP[r * LC + s] = s < r ? p : 0.f;
-            sM[r * LC + s] = s <= r ? m : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < DPT; ++m) {
+            if (tid + kThreads * m < NDIAG) {
+                const float* kr = tK + dr[m] * LT;
+                const float* qr = tQ + dr[m] * LT;
+                const float* gr = tG + dr[m] * LT;
+                const float* ks = tK + ds[m] * LT;
+                const float* gs = tG + ds[m] * LT;
+#pragma unroll 8
+                for (int cc = 0; cc < CT; ++cc) {
+                    const float e = fast_exp(gr[cc] - gs[cc]) * ks[cc];
+                    dp[m] += kr[cc] * e;
+                    dm[m] += qr[cc] * e;
+                }
+            }
+        }
+        __syncthreads();  // the tile is restaged next
+    }
+    // P, M into LDS: zero above the blocks' diagonal, then the two kinds of pairs
+    for (int e = tid; e < C * C; e += kThreads) {
+        const int r = e / C, s2 = e % C;
+        if (s2 / 16 > r / 16) {
+            sP[r * LC + s2] = 0.f;
+            sM[r * LC + s2] = 0.f;
+        } else if (s2 / 16 == r / 16 && s2 > r) {
+            sP[r * LC + s2] = 0.f;
+            sM[r * LC + s2] = 0.f;
         }
     }
+#pragma unroll
+    for (int m = 0; m < DPT; ++m)
+        if (tid + kThreads * m < NDIAG) {
+            sP[dr[m] * LC + ds[m]] = ds[m] < dr[m] ? dp[m] : 0.f;
+            sM[dr[m] * LC + ds[m]] = dm[m];
+        }
+#pragma unroll
+    for (int m = 0; m < PPW; ++m)
+        if (w + 4 * m < NPAIR)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * pi[m] + 4 * lg + e, s2 = 16 * pj[m] + lr;
+                sP[r * LC + s2] = accP[m][e];
+                sM[r * LC + s2] = accM[m][e];
+            }
     __syncthreads();
-
-    // Q+, K', gamma, M, P out
-    for (int e = tid; e < C * DK; e += kThreads) {
-        const int r = e / DK, cc = e % DK;
-        const float g = sG[r * LK + cc], gl = sG[(C - 1) * LK + cc];
-        rec[R::Qp + e] = sX[r * LX + cc] * fast_exp(g);
-        rec[R::Kd + e] = sK[r * LK + cc] * fast_exp(gl - g);
-    }
-    for (int cc = tid; cc < DK; cc += kThreads) rec[R::gam + cc] = fast_exp(sG[(C - 1) * LK + cc]);
     for (int e = tid; e < C * C; e += kThreads) {
-        const int r = e / C, s = e % C;
-        rec[R::M + e] = sM[r * LC + s];
-        rec[R::P + e] = sP[r * LC + s];
+        const int r = e / C, s2 = e % C;
+        rec[R::M + e] = sM[r * LC + s2];
+        rec[R::P + e] = sP[r * LC + s2];
     }
     __syncthreads();
-    // A = Diag(beta) P into M's buffer; T zeroed; K becomes beta K+ and q's buffer beta V
+    // A = Diag(beta) P into M's buffer; T zeroed
     float* sA = sM;
     for (int e = tid; e < C * C; e += kThreads) {
-        const int r = e / C, s = e % C;
-        sA[r * LC + s] = sB[r] * sP[r * LC + s];
-        sT[r * LC + s] = 0.f;
-    }
-    for (int e = tid; e < C * DK; e += kThreads) {
-        const int r = e / DK, cc = e % DK;
-        sK[r * LK + cc] *= sB[r] * fast_exp(sG[r * LK + cc]);
-    }
-    for (int e = tid; e < C * DV; e += kThreads) {
-        const int r = e / DV, j = e % DV;
-        sX[r * LX + j] = r < L ? sB[r] * ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j) : 0.f;
+        const int r = e / C, s2 = e % C;
+        sA[r * LC + s2] = sB[r] * sP[r * LC + s2];
+        sT[r * LC + s2] = 0.f;
     }
     __syncthreads();
 
     // T = (I + A)^{-1}, unit lower triangular.  Diagonal 16x16 blocks by forward substitution (lane =
     // column, the block's rows in registers); then the blocks below the diagonal, nearest first:
     // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj.
-    constexpr int NR = C / 16;
     if (w < NR && lane < 16) {
         const int j = lane, o = 16 * w;
         float tc[16];
@@ -257,30 +332,52 @@ __global__ __launch_bounds__(kThreads) void factors_kernel(BwdArgs a, Map<C> mp)
             for (int m = j; m < i; ++m)
                 acc = mma<4>(sA + 16 * i * LC + 16 * m, LC, 1, sT + 16 * m * LC + 16 * j, LC, 1, acc, lane);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sXs[(4 * (lane >> 4) + e) * 17 + (lane & 15)] = acc[e];
+            for (int e = 0; e < 4; ++e) sXs[(4 * lg + e) * 17 + lr] = acc[e];
         }
         __syncthreads();
         if (i < NR) {
             const floatx4 t = mma<4>(sT + 16 * i * LC + 16 * i, LC, 1, sXs, 17, 1, zero4(), lane);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * (lane >> 4) + e) * LC + 16 * j + (lane & 15)] = -t[e];
+            for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * lg + e) * LC + 16 * j + lr] = -t[e];
         }
         __syncthreads();
     }
     for (int e = tid; e < C * C; e += kThreads) rec[R::T + e] = sT[(e / C) * LC + e % C];
 
-    // W = T (beta K+), U = T (beta V): 16x16 tiles over the waves
-    for (int t = w; t < NR * (DK / 16); t += 4) {
-        const int rb = t % NR, cb = t / NR;
-        floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, sK + 16 * cb, LK, 1, zero4(), lane);
+    // ---- pass 2: Q+, K', gamma and W = T (beta K+), channel tile by channel tile
+    for (int c0 = 0; c0 < DK; c0 += CT) {
+        stage_tile(c0);
+        for (int e = tid; e < C * CT; e += kThreads) {
+            const int r = e / CT, cc = e % CT;
+            const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc], kk = tK[r * LT + cc];
+            rec[R::Qp + r * DK + c0 + cc] = tQ[r * LT + cc] * fast_exp(g);
+            rec[R::Kd + r * DK + c0 + cc] = kk * fast_exp(gl - g);
+            tK[r * LT + cc] = sB[r] * kk * fast_exp(g);
+        }
+        if (tid < CT) rec[R::gam + c0 + tid] = fast_exp(tG[(C - 1) * LT + tid]);
+        __syncthreads();
+        for (int t = w; t < NR * (CT / 16); t += 4) {
+            const int rb = t % NR, cb = t / NR;
+            const floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, tK + 16 * cb, LT, 1, zero4(), lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rec[R::W + (16 * rb + 4 * (lane >> 4) + e) * DK + 16 * cb + (lane & 15)] = acc[e];
+            for (int e = 0; e < 4; ++e) rec[R::W + (16 * rb + 4 * lg + e) * DK + c0 + 16 * cb + lr] = acc[e];
+        }
+        __syncthreads();
     }
-    for (int t = w; t < NR * (DV / 16); t += 4) {
-        const int rb = t % NR, cb = t / NR;
-        floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, sX + 16 * cb, LX, 1, zero4(), lane);
+    // ---- pass 3: U = T (beta V), value tile by value tile (beta V staged in q's buffer)
+    for (int j0 = 0; j0 < DV; j0 += VT) {
+        for (int e = tid; e < C * VT; e += kThreads) {
+            const int r = e / VT, j = e % VT;
+            tQ[r * LT + j] = r < L ? sB[r] * ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
+        }
+        __syncthreads();
+        for (int t = w; t < NR * (VT / 16); t += 4) {
+            const int rb = t % NR, cb = t / NR;
+            const floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, tQ + 16 * cb, LT, 1, zero4(), lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rec[R::U + (16 * rb + 4 * (lane >> 4) + e) * DV + 16 * cb + (lane & 15)] = acc[e];
+            for (int e = 0; e < 4; ++e) rec[R::U + (16 * rb + 4 * lg + e) * DV + j0 + 16 * cb + lr] = acc[e];
+        }
+        __syncthreads();
     }
 }
 
@@ -579,52 +676,54 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
 }
 
 // ------------------------------------------------------------------------------------------
-// grad_chunk: one workgroup per (chunk slot, head); dq, dk, dv, dg, dbeta
+// grad_chunk: one workgroup per (chunk slot, head); dq, dk, dv, dg, dbeta.  Under 80 KB of LDS
+// (two workgroups per CU): the key channels are visited in blocks of 16, and each block's
+// cumulative log-decay is recomputed there as a product with a lower-triangular matrix of ones.
 // ------------------------------------------------------------------------------------------
 template <int DK, int DV, int C>
 struct ChunkLds {
-    static constexpr int LC = C + 1, LK = DK + 1, LB = 17;
+    static constexpr int LC = C + 1, LB = 17;
     static constexpr int JT = DV < 32 ? DV : 32, LJ = JT + 1;  // value columns per staged tile
-    static constexpr int CT = DK < 32 ? DK : 32, LCT = CT + 1; // key channels per staged tile
-    static constexpr int kStage0 = 3 * LJ > 2 * LCT ? 3 * LJ : 2 * LCT;
-    static constexpr int kStage = kStage0 > 5 * LB ? kStage0 : 5 * LB;  // floats per row of the staging area
-    static constexpr size_t kFloats = 4 * (size_t)C * LC      // T, dM, dT -> dA -> dP, Z
-                                      + (size_t)C * LK        // G
+    static constexpr int kStage0 = 3 * LJ > 6 * LB ? 3 * LJ : 6 * LB;
+    static constexpr int kStage = kStage0 > LC ? kStage0 : LC;  // floats per row of the staging area
+    static constexpr size_t kFloats = 3 * (size_t)C * LC      // T, dM, dT -> dP
                                       + (size_t)C * kStage    // staged tiles (see the kernel)
-                                      + 4 * (size_t)C         // beta, dbeta, dg (one gate per head), spare
-                                      + 2 * 16;               // per-block column sums
+                                      + 4 * (size_t)C         // beta, dbeta, dg (one gate per head)
+                                      + 2 * 16;               // per-block column sums, dgamma
     static constexpr size_t kBytes = kFloats * sizeof(float);
 };
 
 template <int DK, int DV, int C, typename TI>
-__global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> mp) {
+__global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
     using Lds = ChunkLds<DK, DV, C>;
-    constexpr int LC = Lds::LC, LK = Lds::LK, LB = Lds::LB, NR = C / 16;
-    constexpr int JT = Lds::JT, LJ = Lds::LJ, CT = Lds::CT, LCT = Lds::LCT;
+    constexpr int LC = Lds::LC, LB = Lds::LB, NR = C / 16, JT = Lds::JT, LJ = Lds::LJ;
+    constexpr int RPT = C / 16;  // rows per thread in the channel-block sweeps
     extern __shared__ float lds[];
-    float* sT = lds;             // [C][LC]
-    float* sdM = sT + C * LC;    // [C][LC]
-    float* sA = sdM + C * LC;    // [C][LC]  dT, then dP
-    float* sZ = sA + C * LC;     // [C][LC]
-    float* sG = sZ + C * LC;     // [C][LK]
-    float* sX = sG + C * LK;     // [C][kStage] staging area
-    float* sB = sX + C * Lds::kStage;  // [C]
-    float* sdb = sB + C;         // [C]
-    float* sdgh = sdb + C;       // [C]
-    float* sCol = sdgh + 2 * C;  // [16] column sums of dK' * K' in the current channel block
-    // staged tiles inside sX: value tiles dD, V, beta V ([C][LJ] each); key tiles dW, beta K+
-    // ([C][LCT] each); channel blocks K, Q, dK+, dG, dW ([C][LB] each)
+    float* sT = lds;                    // [C][LC]
+    float* sdM = sT + C * LC;           // [C][LC]
+    float* sA = sdM + C * LC;           // [C][LC]  dT, then dP
+    float* sX = sA + C * LC;            // [C][kStage] staging area
+    float* sB = sX + C * Lds::kStage;   // [C]
+    float* sdb = sB + C;                // [C]
+    float* sdgh = sdb + C;              // [C]
+    float* sCol = sdgh + 2 * C;         // [16] column sums of dK' * K' in the current channel block
+    // value tiles: dD, V, beta V ([C][LJ] each); Z ([C][LC]); channel blocks ([C][LB] each): K, Q,
+    // dW (then K scaled for the row role), G, beta K+ (first pass) or K scaled for the column role
+    // (second pass), g (then Q scaled for the column role, then dG)
     float* tdD = sX;
     float* tV = tdD + C * LJ;
     float* tBV = tV + C * LJ;
-    float* tdW = sX;
-    float* tBK = tdW + C * LCT;
+    float* sZ = sX;
     float* tK = sX;
     float* tQ = tK + C * LB;
-    float* tKp = tQ + C * LB;
+    float* tW = tQ + C * LB;
+    float* tG = tW + C * LB;
+    float* tKp = tG + C * LB;
     float* tdG = tKp + C * LB;
-    float* tW = tdG + C * LB;
+    float* tKc = tW;   // second pass: K_s exp(G_m - G_s), m the last row of s's block
+    float* tKr = tKp;  // second pass: K_r exp(G_r - G_m), m the last row of the block before r's
+    float* tQr = tdG;  // second pass: Q_r exp(G_r - G_m), likewise
 
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t slot = blockIdx.x;
@@ -648,7 +747,49 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
         sdb[tid] = 0.f;
         sdgh[tid] = 0.f;
     }
-    cumulative_decay<DK, C>(a, t0, L, h, sG, LK);  // (ends with a barrier)
+
+    // One 16-channel block of k, q, dW and g, loaded into registers one block ahead, then written to
+    // LDS (k -> tK, q -> tQ, dW -> tW, g -> tdG); element i of a thread is row (tid >> 4) + 16 i,
+    // channel tid & 15.  The second pass also fetches dQ+, dK' and dgamma in the matrix-core layout
+    // (wave w < NR: rows 16 w + 4 (lane >> 4) + e, channel lane & 15).
+    constexpr int NCB = DK / 16;
+    const int cc = tid & 15, r0 = tid >> 4, lr = lane & 15, lg = lane >> 4;
+    struct BlockRegs {
+        float k[RPT], q[RPT], dw[RPT], g[RPT], dqp[4], dkd[4], dgam;
+    };
+    auto fetch_block = [&](int cb, bool second, BlockRegs& br) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = r0 + 16 * i, ch = 16 * cb + cc;
+            const bool in = r < L;
+            const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + ch;
+            br.k[i] = in ? ld_in<TI>(k, idx) : 0.f;
+            br.dw[i] = rec[R::dW + r * DK + ch];
+            br.g[i] = in ? gate_at(a.g, a.gate_head, t0 + r, H, h, DK, ch) : 0.f;
+            if (second) br.q[i] = in ? ld_in<TI>(q, idx) : 0.f;
+        }
+        if (second && w < NR) {
+            const int ch = 16 * cb + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + 4 * lg + e;
+                br.dqp[e] = rec[R::dQp + r * DK + ch];
+                br.dkd[e] = rec[R::dKd + r * DK + ch];
+            }
+            br.dgam = rec[R::dgam + ch];
+        }
+    };
+    auto put_block = [&](const BlockRegs& br, bool second) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = r0 + 16 * i;
+            tK[r * LB + cc] = br.k[i];
+            tW[r * LB + cc] = br.dw[i];
+            tdG[r * LB + cc] = br.g[i];
+            if (second) tQ[r * LB + cc] = br.q[i];
+        }
+        if (second && tid < 16) sCol[tid] = 0.f;
+    };
 
     // ---- dT = dD (beta V)^T + dW (beta K+)^T, strictly lower part (wave w owns tiles w, w+4, ...),
     //      and with the value tiles staged: dV = beta (T^T dD), dbeta += rowsum(V * T^T dD)
@@ -662,7 +803,7 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
             const float vv = r < L ? ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
             tdD[r * LJ + j] = rec[R::dD + r * DV + j0 + j];
             tV[r * LJ + j] = vv;
-            tBV[r * LJ + j] = sB[r] * vv;
+            tBV[r * LJ + j] = (r < L ? ld_in<TI>(beta, (t0 + r) * H + h) : 0.f) * vv;
         }
         __syncthreads();
 #pragma unroll
@@ -689,23 +830,29 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
         }
         __syncthreads();
     }
-    for (int c0 = 0; c0 < DK; c0 += CT) {
-        for (int e = tid; e < C * CT; e += kThreads) {
-            const int r = e / CT, cc = e % CT;
-            tdW[r * LCT + cc] = rec[R::dW + r * DK + c0 + cc];
-            tBK[r * LCT + cc] = r < L ? sB[r] * ld_in<TI>(k, ((t0 + r) * H + h) * (int64_t)DK + c0 + cc) *
-                                            fast_exp(sG[r * LK + c0 + cc])
-                                      : 0.f;
+    BlockRegs br;
+    fetch_block(0, false, br);
+    for (int cb = 0; cb < NCB; ++cb) {
+        put_block(br, false);
+        fetch_block(cb + 1 < NCB ? cb + 1 : cb, false, br);
+        __syncthreads();
+        if (w < NR) {  // G rows of block w, then beta K+ = beta k exp(G) into tKp
+            const floatx4 G = prefix_rows<C>(tdG, LB, w, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + 4 * (lane >> 4) + e, cc = lane & 15;
+                tKp[r * LB + cc] = sB[r] * tK[r * LB + cc] * fast_exp(G[e]);
+            }
         }
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int t = w + 4 * m, rb = t / NR, sb = t % NR;
-            if (t < NT && sb <= rb)
-                dT[m] = mma<CT / 4>(tdW + 16 * rb * LCT, LCT, 1, tBK + 16 * sb * LCT, 1, LCT, dT[m], lane);
+            if (t < NT && sb <= rb) dT[m] = mma<4>(tW + 16 * rb * LB, LB, 1, tKp + 16 * sb * LB, 1, LB, dT[m], lane);
         }
         __syncthreads();
     }
+    fetch_block(0, true, br);  // the second pass's first block, in flight during dA
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
         const int t = w + 4 * m, rb = t / NR, sb = t % NR;
@@ -717,7 +864,8 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
             }
     }
     __syncthreads();
-    // ---- dA = -T^T dT T^T (strictly lower): Z = T^T dT, then dA = -Z T^T
+    // ---- dA = -T^T dT T^T (strictly lower): Z = T^T dT, then dA = -Z T^T; dP = Diag(beta) dA,
+    //      dbeta += rowsum(dA * P)
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
         const int t = w + 4 * m, rb = t / NR, sb = t % NR;
@@ -733,7 +881,7 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
         const int t = w + 4 * m, rb = t / NR, sb = t % NR;
         if (t < NT) dT[m] = mma<C / 4>(sZ + 16 * rb * LC, LC, 1, sT + 16 * sb * LC, 1, LC, zero4(), lane);
     }
-    __syncthreads();  // every read of sA (dT) is done
+    __syncthreads();  // every read of sA (dT) and sZ is done
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
         const int t = w + 4 * m, rb = t / NR, sb = t % NR;
@@ -753,102 +901,149 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
             }
         }
     }
-    __syncthreads();  // dP complete; sX free
+    __syncthreads();
 
-    // ---- channel blocks of 16: dK+, the pairwise sweeps, dq, dk, dG and its suffix sums
-    for (int cb = 0; cb < DK / 16; ++cb) {
-        for (int e = tid; e < C * 16; e += kThreads) {
-            const int r = e / 16, cc = e % 16;
-            const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + 16 * cb + cc;
-            tK[r * LB + cc] = r < L ? ld_in<TI>(k, idx) : 0.f;
-            tQ[r * LB + cc] = r < L ? ld_in<TI>(q, idx) : 0.f;
-            tW[r * LB + cc] = rec[R::dW + r * DK + 16 * cb + cc];
+    // ---- channel blocks of 16, wave w < NR owning row block w: G, dK+ = beta T^T dW, the gradients
+    //      through the pairwise products P and M, dq, dk, dG, and dg as the suffix sums of dG.
+    //      Pairs (r, s) in different 16-row blocks go through the matrix cores: with m a block's last
+    //      row, exp(G_r - G_s) = exp(G_r - G_m) exp(G_m - G_s) where both exponents are <= 0
+    //      (s <= m < r), so every scaled operand is bounded by the unscaled one.  Pairs inside a block
+    //      take the exponential of their own difference.
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int ch = 16 * cb + lr;
+        float rdq[4], rdk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            rdq[e] = br.dqp[e];
+            rdk[e] = br.dkd[e];
         }
-        if (tid < 16) sCol[tid] = 0.f;
+        const float dgam = br.dgam;
+        put_block(br, true);
+        fetch_block(cb + 1 < NCB ? cb + 1 : cb, true, br);
         __syncthreads();
-        // X2 = T^T dW (rows block w), dK+ = beta X2, dbeta += rowsum(K+ * X2)
+        float Gr[4] = {0.f, 0.f, 0.f, 0.f}, xk[4] = {0.f, 0.f, 0.f, 0.f};
         if (w < NR) {
+            const floatx4 G = prefix_rows<C>(tdG, LB, w, lane);
             const floatx4 x = mma<C / 4>(sT + 16 * w, 1, LC, tW, LB, 1, zero4(), lane);
             float part[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * w + 4 * (lane >> 4) + e, cc = lane & 15;
-                part[e] = tK[r * LB + cc] * fast_exp(sG[r * LK + 16 * cb + cc]) * x[e];
-                tKp[r * LB + cc] = sB[r] * x[e];
+                const int r = 16 * w + 4 * lg + e;
+                Gr[e] = G[e];
+                tG[r * LB + lr] = G[e];
+                xk[e] = sB[r] * x[e];
+                part[e] = tK[r * LB + lr] * fast_exp(G[e]) * x[e];
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float p = sum16(part[e]);
-                if ((lane & 15) == 0) atomicAdd(&sdb[16 * w + 4 * (lane >> 4) + e], p);
+                if (lr == 0) atomicAdd(&sdb[16 * w + 4 * lg + e], p);
+            }
+        }
+        __syncthreads();  // G complete; dW and g no longer needed
+        if (w < NR) {
+            const float gend = tG[(16 * w + 15) * LB + lr];
+            const float gprev = w > 0 ? tG[(16 * w - 1) * LB + lr] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + 4 * lg + e;
+                const float kr = tK[r * LB + lr], qr = tQ[r * LB + lr];
+                if (w < NR - 1) tKc[r * LB + lr] = kr * fast_exp(gend - Gr[e]);
+                if (w > 0) {
+                    const float f = fast_exp(Gr[e] - gprev);
+                    tQr[r * LB + lr] = qr * f;
+                    tKr[r * LB + lr] = kr * f;
+                }
             }
         }
         __syncthreads();
-        // thread: channel cc = tid & 15, rows r = (tid >> 4) + 16 i
-        {
-            const int cc = tid & 15, ch = 16 * cb + cc;
-            const float glast = sG[(C - 1) * LK + ch];
-            float colsum = 0.f;
-            for (int r = tid >> 4; r < C; r += 16) {
-                const float gr = sG[r * LK + ch];
-                const float kr = tK[r * LB + cc], qr = tQ[r * LB + cc];
-                float rq = 0.f, rk = 0.f, ck = 0.f;
-                // row role (this row r, columns s <= r) and column role (this row as s, rows r2 >= s)
-                for (int s = 0; s < C; ++s) {
-                    const float gs = sG[s * LK + ch];
-                    if (s <= r) {
-                        const float e = fast_exp(gr - gs) * tK[s * LB + cc];
-                        rq += sdM[r * LC + s] * e;
-                        rk += sA[r * LC + s] * e;  // dP is zero on the diagonal
-                    } else {
-                        const float e = fast_exp(gs - gr);
-                        ck += e * (sdM[s * LC + r] * tQ[s * LB + cc] + sA[s * LC + r] * tK[s * LB + cc]);
-                    }
+        float dGr[4] = {0.f, 0.f, 0.f, 0.f}, glast = 0.f;
+        if (w < NR) {
+            float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f}, ck[4] = {0.f, 0.f, 0.f, 0.f};
+            // row role, blocks j < w:  sum_s dM[r][s] K_s exp(G_r - G_s), and the same with dP
+            for (int j = 0; j < w; ++j) {
+                const floatx4 xm = mma<4>(sdM + 16 * w * LC + 16 * j, LC, 1, tKc + 16 * j * LB, LB, 1, zero4(), lane);
+                const floatx4 xp = mma<4>(sA + 16 * w * LC + 16 * j, LC, 1, tKc + 16 * j * LB, LB, 1, zero4(), lane);
+                const float gm = tG[(16 * j + 15) * LB + lr];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float f = fast_exp(Gr[e] - gm);
+                    rq[e] += f * xm[e];
+                    rk[e] += f * xp[e];
                 }
-                // the diagonal term of the column role: only M has one (dM[r][r] q_r)
-                ck += sdM[r * LC + r] * qr;
-                float dq = 0.f, dk = 0.f, dG = 0.f;
+            }
+            // column role, blocks i > w:  sum_r exp(G_r - G_s) (dM[r][s] Q_r + dP[r][s] K_r)
+            for (int i = w + 1; i < NR; ++i) {
+                floatx4 y = mma<4>(sdM + 16 * i * LC + 16 * w, 1, LC, tQr + 16 * i * LB, LB, 1, zero4(), lane);
+                y = mma<4>(sA + 16 * i * LC + 16 * w, 1, LC, tKr + 16 * i * LB, LB, 1, y, lane);
+                const float gm = tG[(16 * i - 1) * LB + lr];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ck[e] += fast_exp(gm - Gr[e]) * y[e];
+            }
+            // pairs inside block w
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + 4 * lg + e;
+                for (int s2 = 16 * w; s2 <= r; ++s2) {
+                    const float ev = fast_exp(Gr[e] - tG[s2 * LB + lr]) * tK[s2 * LB + lr];
+                    rq[e] += sdM[r * LC + s2] * ev;
+                    rk[e] += sA[r * LC + s2] * ev;  // dP is zero on the diagonal
+                }
+                for (int r2 = r + 1; r2 < 16 * w + 16; ++r2) {
+                    const float ev = fast_exp(tG[r2 * LB + lr] - Gr[e]);
+                    ck[e] += ev * (sdM[r2 * LC + r] * tQ[r2 * LB + lr] + sA[r2 * LC + r] * tK[r2 * LB + lr]);
+                }
+                ck[e] += sdM[r * LC + r] * tQ[r * LB + lr];
+            }
+            glast = tG[(C - 1) * LB + lr];
+            float colsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + 4 * lg + e;
                 if (r < L) {
-                    const float eg = fast_exp(gr), ed = fast_exp(glast - gr);
-                    const int64_t o = r * DK + ch;
-                    const float dQp = rec[R::dQp + o], dKd = rec[R::dKd + o], dKp = tKp[r * LB + cc];
-                    dq = dQp * eg + rq;
-                    dk = dKp * eg + rec[R::dKd + o] * ed + rk + ck;
-                    dG = dKp * kr * eg + dQp * qr * eg - dKd * kr * ed + qr * rq + kr * rk - kr * ck;
-                    colsum += dKd * kr * ed;
+                    const float kr = tK[r * LB + lr], qr = tQ[r * LB + lr];
+                    const float eg = fast_exp(Gr[e]), ed = fast_exp(glast - Gr[e]);
+                    const float dq = rdq[e] * eg + rq[e];
+                    const float dk = xk[e] * eg + rdk[e] * ed + rk[e] + ck[e];
+                    dGr[e] = xk[e] * kr * eg + rdq[e] * qr * eg - rdk[e] * kr * ed + qr * rq[e] + kr * rk[e] -
+                             kr * ck[e];
+                    colsum += rdk[e] * kr * ed;
                     const int64_t go = ((t0 + r) * H + h) * (int64_t)DK + ch;
                     a.gq[go] = dq;
                     a.gk[go] = dk;
                 }
-                tdG[r * LB + cc] = dG;
             }
-            atomicAdd(&sCol[cc], colsum);
+            colsum += __shfl_xor(colsum, 16);
+            colsum += __shfl_xor(colsum, 32);
+            if (lg == 0) atomicAdd(&sCol[lr], colsum);
         }
-        __syncthreads();
-        if (tid < 16) {
-            const int ch = 16 * cb + tid;
-            const float glast = sG[(C - 1) * LK + ch];
-            tdG[(L - 1) * LB + tid] += sCol[tid] + rec[R::dgam + ch] * fast_exp(glast);
-        }
+        __syncthreads();  // every read of the scaled tiles is done; the column sums are complete
+        if (w < NR)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + 4 * lg + e;
+                tdG[r * LB + lr] = dGr[e] + (r == L - 1 ? sCol[lr] + dgam * fast_exp(glast) : 0.f);
+            }
         __syncthreads();
         // dg = suffix sums over the chunk's rows: dg = Triu(ones) dG
         if (w < NR) {
-            const int r = lane & 15, kq = lane >> 4;
             floatx4 acc = zero4();
 #pragma unroll 4
             for (int ks = 0; ks < C / 4; ++ks) {
-                const int s = 4 * ks + kq;
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s >= 16 * w + r ? 1.f : 0.f, tdG[s * LB + r], acc, 0, 0, 0);
+                const int s2 = 4 * ks + lg;
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s2 >= 16 * w + lr ? 1.f : 0.f, tdG[s2 * LB + lr], acc, 0, 0,
+                                                           0);
             }
             float hsum[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * w + 4 * (lane >> 4) + e, cc = lane & 15;
-                if (!a.gate_head && rr < L) a.gg[((t0 + rr) * H + h) * (int64_t)DK + 16 * cb + cc] = acc[e];
+                const int rr = 16 * w + 4 * lg + e;
+                if (!a.gate_head && rr < L) a.gg[((t0 + rr) * H + h) * (int64_t)DK + ch] = acc[e];
                 hsum[e] = sum16(acc[e]);
             }
-            if (a.gate_head && (lane & 15) == 0)
+            if (a.gate_head && lr == 0)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sdgh[16 * w + 4 * (lane >> 4) + e] += hsum[e];
+                for (int e = 0; e < 4; ++e) sdgh[16 * w + 4 * lg + e] += hsum[e];
         }
         __syncthreads();  // the tiles are rewritten by the next block
     }
@@ -861,12 +1056,6 @@ __global__ __launch_bounds__(kThreads) void grad_chunk_kernel(BwdArgs a, Map<C> 
 // ------------------------------------------------------------------------------------------
 // launch
 // ------------------------------------------------------------------------------------------
-template <int DK, int DV, int C>
-constexpr size_t factors_lds() {
-    constexpr int DX = DK > DV ? DK : DV;
-    return ((size_t)C * (DK + 1) * 2 + (size_t)C * (DX + 1) + 3 * (size_t)C * (C + 1) + C) * sizeof(float);
-}
-
 template <typename K>
 hipError_t set_lds(K kernel, size_t bytes) {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -882,7 +1071,7 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
     const dim3 per_chunk((unsigned)slots, (unsigned)a.H), chains((unsigned)(a.N * a.H * (DV / kBV)));
     const bool timed = timing_on();
     hipError_t e;
-    constexpr size_t f_lds = factors_lds<DK, DV, C>(), c_lds = ChunkLds<DK, DV, C>::kBytes;
+    constexpr size_t f_lds = FactorsLds<DK, DV, C>::kBytes, c_lds = ChunkLds<DK, DV, C>::kBytes;
     if ((e = set_lds(factors_kernel<DK, DV, C, TI>, f_lds)) != hipSuccess) return e;
     if ((e = set_lds(grad_chunk_kernel<DK, DV, C, TI>, c_lds)) != hipSuccess) return e;
     if (a.T_total > 0) {
