@@ -38,6 +38,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kBV = 16;        // value columns per chain workgroup
+constexpr int kWarm = 3;       // chunks between a chain's L2 warm-up of a record and its use
 
 // acc += A (16 x 4KS) * B (4KS x 16) with A(r, k) = A[r * ar + k * ak] and B(k, c) = B[k * bk + c * bc].
 // Result layout: acc[e] is row 4 * (lane >> 4) + e, column lane & 15.
@@ -54,6 +55,36 @@ __device__ __forceinline__ floatx4 mma(const float* A, int ar, int ak, const flo
 }
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations (lgkmcnt) but not for
+// its outstanding global loads and stores, so loads issued one step ahead stay in flight across it
+// (a __syncthreads() fence would drain them).  No kernel here reads global memory that another
+// workgroup thread wrote in the same launch.  The empty asm statements keep the compiler from
+// moving memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // gfx9 encoding: vmcnt/expcnt at max, lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// mma with the k-steps alternating between two accumulators: half the dependent chain, for the
+// latency-bound sequential kernels (KS even)
+template <int KS>
+__device__ __forceinline__ floatx4 mma2(const float* A, int ar, int ak, const float* B, int bk, int bc, floatx4 acc,
+                                        int lane) {
+    static_assert(KS % 2 == 0, "even number of k-steps");
+    const int r = lane & 15, kq = lane >> 4;
+    const float* pa = A + r * ar + kq * ak;
+    const float* pb = B + kq * bk + r * bc;
+    floatx4 acc1 = zero4();
+#pragma unroll 4
+    for (int ks = 0; ks < KS; ks += 2) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * ks * ak], pb[4 * ks * bk], acc, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * (ks + 1) * ak], pb[4 * (ks + 1) * bk], acc1, 0, 0, 0);
+    }
+    return acc + acc1;
+}
 
 // sum over the 16 lanes that share (lane >> 4)
 __device__ __forceinline__ float sum16(float x) {
@@ -185,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             tQ[r * LT + cc] = in ? ld_in<TI>(q, idx) : 0.f;
             tG[r * LT + cc] = in ? gate_at(a.g, a.gate_head, t0 + r, H, h, DK, c0 + cc) : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
         constexpr int NCT = CT / 16;
         floatx4 G[(NR * NCT + 3) / 4];
 #pragma unroll
@@ -193,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             const int t = w + 4 * m, rb = t % NR, cb = t / NR;
             if (t < NR * NCT) G[m] = prefix_rows<C>(tG + 16 * cb, LT, rb, lane);
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int m = 0; m < (NR * NCT + 3) / 4; ++m) {
             const int t = w + 4 * m, rb = t % NR, cb = t / NR;
@@ -201,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tG[(16 * rb + 4 * lg + e) * LT + 16 * cb + lr] = G[m][e];
         }
-        __syncthreads();
+        lds_barrier();
     };
 
     // ---- pass 1: P and M
@@ -263,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
                 }
             }
         }
-        __syncthreads();  // the tile is restaged next
+        lds_barrier();  // the tile is restaged next
     }
     // P, M into LDS: zero above the blocks' diagonal, then the two kinds of pairs
     for (int e = tid; e < C * C; e += kThreads) {
@@ -291,13 +322,13 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
                 sP[r * LC + s2] = accP[m][e];
                 sM[r * LC + s2] = accM[m][e];
             }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < C * C; e += kThreads) {
         const int r = e / C, s2 = e % C;
         rec[R::M + e] = sM[r * LC + s2];
         rec[R::P + e] = sP[r * LC + s2];
     }
-    __syncthreads();
+    lds_barrier();
     // A = Diag(beta) P into M's buffer; T zeroed
     float* sA = sM;
     for (int e = tid; e < C * C; e += kThreads) {
@@ -305,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         sA[r * LC + s2] = sB[r] * sP[r * LC + s2];
         sT[r * LC + s2] = 0.f;
     }
-    __syncthreads();
+    lds_barrier();
 
     // T = (I + A)^{-1}, unit lower triangular.  Diagonal 16x16 blocks by forward substitution (lane =
     // column, the block's rows in registers); then the blocks below the diagonal, nearest first:
@@ -323,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) sT[(o + rr) * LC + o + j] = tc[rr];
     }
-    __syncthreads();
+    lds_barrier();
     float* sXs = sP + w * 16 * 17;  // per-wave 16x16 scratch (P is in the record already)
     for (int dist = 1; dist < NR; ++dist) {
         const int j = w, i = w + dist;
@@ -334,13 +365,13 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
 #pragma unroll
             for (int e = 0; e < 4; ++e) sXs[(4 * lg + e) * 17 + lr] = acc[e];
         }
-        __syncthreads();
+        lds_barrier();
         if (i < NR) {
             const floatx4 t = mma<4>(sT + 16 * i * LC + 16 * i, LC, 1, sXs, 17, 1, zero4(), lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * lg + e) * LC + 16 * j + lr] = -t[e];
         }
-        __syncthreads();
+        lds_barrier();
     }
     for (int e = tid; e < C * C; e += kThreads) rec[R::T + e] = sT[(e / C) * LC + e % C];
 
@@ -355,14 +386,14 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             tK[r * LT + cc] = sB[r] * kk * fast_exp(g);
         }
         if (tid < CT) rec[R::gam + c0 + tid] = fast_exp(tG[(C - 1) * LT + tid]);
-        __syncthreads();
+        lds_barrier();
         for (int t = w; t < NR * (CT / 16); t += 4) {
             const int rb = t % NR, cb = t / NR;
             const floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, tK + 16 * cb, LT, 1, zero4(), lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) rec[R::W + (16 * rb + 4 * lg + e) * DK + c0 + 16 * cb + lr] = acc[e];
         }
-        __syncthreads();
+        lds_barrier();
     }
     // ---- pass 3: U = T (beta V), value tile by value tile (beta V staged in q's buffer)
     for (int j0 = 0; j0 < DV; j0 += VT) {
@@ -370,14 +401,14 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             const int r = e / VT, j = e % VT;
             tQ[r * LT + j] = r < L ? sB[r] * ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
         for (int t = w; t < NR * (VT / 16); t += 4) {
             const int rb = t % NR, cb = t / NR;
             const floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, tQ + 16 * cb, LT, 1, zero4(), lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) rec[R::U + (16 * rb + 4 * lg + e) * DV + j0 + 16 * cb + lr] = acc[e];
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -408,7 +439,7 @@ struct Stage {
             const int e = threadIdx.x + m * kThreads;
             if (kVec % kThreads == 0 || e < kVec) {
                 const int row = e / (COLS / 4), c4 = e % (COLS / 4);
-                float* p = dst + row * ld + 4 * c4;
+                float* p = dst + row * ld + 4 * c4;  // 16-byte aligned: ld is a multiple of 4
                 p[0] = r[m].x;
                 p[1] = r[m].y;
                 p[2] = r[m].z;
@@ -418,6 +449,41 @@ struct Stage {
     }
 };
 
+// Warm L2 with floats [off, off + n) of a record ahead of its use: the nvb chain workgroups of a
+// sequence-head read the same record, so value block vb touches every nvb-th 128-byte line of the
+// range, with 4-byte direct-to-LDS loads into a dummy slot (no registers are written and nothing
+// waits on them).  Unconditional (lanes past the end repeat the last line), so the compiler's
+// load counting for the operand prefetch stays exact.
+template <int64_t N>
+__device__ __forceinline__ void warm_range(const float* rec, int64_t off, int vb, int nvb,
+                                           __attribute__((address_space(3))) void* dummy) {
+    constexpr int64_t kLines = (N * 4 + 127) / 128;
+    const int64_t per = (kLines + nvb - 1) / nvb;
+#pragma unroll
+    for (int m = 0; m < (int)((kLines + kThreads - 1) / kThreads); ++m) {
+        int64_t i = threadIdx.x + (int64_t)kThreads * m;
+        if (i >= per) i = per - 1;
+        int64_t line = vb + (int64_t)nvb * i;
+        if (line >= kLines) line = kLines - 1;
+        __builtin_amdgcn_global_load_lds(rec + off + line * 32, dummy, 4, 0, 0);
+    }
+}
+
+// Chain workgroup -> (sequence-head, value block).  Workgroups are dealt to the 8 XCDs round-robin;
+// when the sequence-heads divide into 8, the value blocks of one sequence-head go to one XCD so that
+// they share its L2 (each reads the same per-chunk record).
+template <int NVB>
+__device__ __forceinline__ void chain_unit(int64_t gid, int64_t nh_total, int64_t& nh, int& vb) {
+    if ((nh_total & 7) == 0) {
+        const int64_t xcd = gid & 7, u = gid >> 3;
+        vb = (int)(u % NVB);
+        nh = xcd + 8 * (u / NVB);
+    } else {
+        vb = (int)(gid % NVB);
+        nh = gid / NVB;
+    }
+}
+
 // ------------------------------------------------------------------------------------------
 // fwd_chain: one workgroup per (sequence, head, 16 value columns); states entering each chunk
 // ------------------------------------------------------------------------------------------
@@ -425,16 +491,20 @@ template <int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
     constexpr int NVB = DV / kBV, LW = DK + 4, LQ = DK + 16;
-    __shared__ float sW[C * LW];   // W rows (A operand by rows)
-    __shared__ float sKd[C * LQ];  // K' rows (A operand by columns)
-    __shared__ float sU[C * kBV];
-    __shared__ float sg[DK];
-    __shared__ float sS[DK * kBV];
-    __shared__ float sD[C * kBV];
+    __shared__ __attribute__((aligned(16))) float sW[C * LW];   // W rows (A operand by rows)
+    __shared__ __attribute__((aligned(16))) float sKd[C * LQ];  // K' rows (A operand by columns)
+    __shared__ __attribute__((aligned(16))) float sU[C * kBV];
+    __shared__ __attribute__((aligned(16))) float sg[DK];
+    __shared__ __attribute__((aligned(16))) float sS[DK * kBV];
+    __shared__ __attribute__((aligned(16))) float sD[C * kBV];
+    __shared__ __attribute__((aligned(16))) float sDummy[64];  // sink of the L2 warm-up loads
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t gid = blockIdx.x;
-    const int vb = (int)(gid % NVB), h = (int)((gid / NVB) % a.H);
-    const int64_t n = gid / NVB / a.H;
+    int64_t nh;
+    int vb;
+    chain_unit<NVB>(blockIdx.x, mp.N * a.H, nh, vb);
+    auto* dummy = reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&sDummy[0]));
+    const int h = (int)(nh % a.H);
+    const int64_t n = nh / a.H;
     const int H = a.H;
     for (int e = tid; e < DK * kBV; e += kThreads) {
         const int i = e / kBV, j = e % kBV;
@@ -456,17 +526,21 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
     fetch(0);
     for (int64_t c = 0; c < nck; ++c) {
         float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
-        __syncthreads();  // the previous chunk is done with the LDS operands; sS is its final state
+        lds_barrier();  // the previous chunk is done with the LDS operands; sS is its final state
         pW.store(sW, LW);
         pK.store(sKd, LQ);
         pU.store(sU, kBV);
         pg.store(sg, DK);
         fetch(c + 1 < nck ? c + 1 : c);
+        {  // W, U and K' (one contiguous range) of the chunk kWarm ahead
+            const float* wrec = a.ws + ((slot0 + (c + kWarm < nck ? c + kWarm : nck - 1)) * H + h) * R::kFloats;
+            warm_range<R::Kd + C * DK>(wrec, 0, vb, NVB, dummy);
+        }
         for (int e = tid; e < DK * kBV; e += kThreads) rec[R::S0 + (e / kBV) * DV + vb * kBV + e % kBV] = sS[e];
-        __syncthreads();
+        lds_barrier();
         // D = U - W S
         for (int rb = w; rb < C / 16; rb += 4) {
-            const floatx4 acc = mma<DK / 4>(sW + 16 * rb * LW, LW, 1, sS, kBV, 1, zero4(), lane);
+            const floatx4 acc = mma2<DK / 4>(sW + 16 * rb * LW, LW, 1, sS, kBV, 1, zero4(), lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * (lane >> 4) + e, j = lane & 15;
@@ -475,8 +549,9 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
                 rec[R::D + r * DV + vb * kBV + j] = d;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // S <- Diag(gamma) S + K'^T D
+#pragma unroll
         for (int cb = w; cb < DK / 16; cb += 4) {
             floatx4 acc;
 #pragma unroll
@@ -484,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
                 const int i = 16 * cb + 4 * (lane >> 4) + e;
                 acc[e] = sg[i] * sS[i * kBV + (lane & 15)];
             }
-            acc = mma<C / 4>(sKd + 16 * cb, 1, LQ, sD, kBV, 1, acc, lane);
+            acc = mma2<C / 4>(sKd + 16 * cb, 1, LQ, sD, kBV, 1, acc, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sS[(16 * cb + 4 * (lane >> 4) + e) * kBV + (lane & 15)] = acc[e];
         }
@@ -498,18 +573,22 @@ template <int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
     constexpr int NVB = DV / kBV, LW = DK + 4, LQ = DK + 16, LM = C + 16;
-    __shared__ float sKd[C * LW];  // K' rows (A operand by rows)
-    __shared__ float sM[C * LM];   // M (A operand by columns)
-    __shared__ float sQp[C * LQ];  // Q+ (A operand by columns)
-    __shared__ float sW[C * LQ];   // W (A operand by columns)
-    __shared__ float sg[DK];
-    __shared__ float sdS[DK * kBV];
-    __shared__ float sdO[C * kBV];
-    __shared__ float sdD[C * kBV];
+    __shared__ __attribute__((aligned(16))) float sKd[C * LW];  // K' rows (A operand by rows)
+    __shared__ __attribute__((aligned(16))) float sM[C * LM];   // M (A operand by columns)
+    __shared__ __attribute__((aligned(16))) float sQp[C * LQ];  // Q+ (A operand by columns)
+    __shared__ __attribute__((aligned(16))) float sW[C * LQ];   // W (A operand by columns)
+    __shared__ __attribute__((aligned(16))) float sg[DK];
+    __shared__ __attribute__((aligned(16))) float sdS[DK * kBV];
+    __shared__ __attribute__((aligned(16))) float sdO[C * kBV];
+    __shared__ __attribute__((aligned(16))) float sdD[C * kBV];
+    __shared__ __attribute__((aligned(16))) float sDummy[64];  // sink of the L2 warm-up loads
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t gid = blockIdx.x;
-    const int vb = (int)(gid % NVB), h = (int)((gid / NVB) % a.H);
-    const int64_t n = gid / NVB / a.H;
+    int64_t nh;
+    int vb;
+    chain_unit<NVB>(blockIdx.x, mp.N * a.H, nh, vb);
+    auto* dummy = reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&sDummy[0]));
+    const int h = (int)(nh % a.H);
+    const int64_t n = nh / a.H;
     const int H = a.H;
     for (int e = tid; e < DK * kBV; e += kThreads) {
         const int i = e / kBV, j = e % kBV;
@@ -539,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
     if (nck > 0) fetch(nck - 1);
     for (int64_t c = nck - 1; c >= 0; --c) {
         float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
-        __syncthreads();  // the previous chunk is done with the LDS operands; sdS is its result
+        lds_barrier();  // the previous chunk is done with the LDS operands; sdS is its result
         pK.store(sKd, LW);
         pM.store(sM, LM);
         pQ.store(sQp, LQ);
@@ -551,12 +630,17 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
             if (e < C * kBV) sdO[e] = rdo[m];
         }
         fetch(c > 0 ? c - 1 : c);
+        {  // W (first range), then K', Q+ and M (second range) of the chunk kWarm behind
+            const float* wrec = a.ws + ((slot0 + (c >= kWarm ? c - kWarm : 0)) * H + h) * R::kFloats;
+            warm_range<C * DK>(wrec, R::W, vb, NVB, dummy);
+            warm_range<R::T - R::Kd>(wrec, R::Kd, vb, NVB, dummy);
+        }
         for (int e = tid; e < DK * kBV; e += kThreads) rec[R::dS1 + (e / kBV) * DV + vb * kBV + e % kBV] = sdS[e];
-        __syncthreads();
+        lds_barrier();
         // dD = K' dS + M^T dO
         for (int rb = w; rb < C / 16; rb += 4) {
-            floatx4 acc = mma<DK / 4>(sKd + 16 * rb * LW, LW, 1, sdS, kBV, 1, zero4(), lane);
-            acc = mma<C / 4>(sM + 16 * rb, 1, LM, sdO, kBV, 1, acc, lane);
+            floatx4 acc = mma2<DK / 4>(sKd + 16 * rb * LW, LW, 1, sdS, kBV, 1, zero4(), lane);
+            acc = mma2<C / 4>(sM + 16 * rb, 1, LM, sdO, kBV, 1, acc, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * (lane >> 4) + e, j = lane & 15;
@@ -564,8 +648,9 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
                 rec[R::dD + r * DV + vb * kBV + j] = acc[e];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // dS <- Diag(gamma) dS + Q+^T dO - W^T dD
+#pragma unroll
         for (int cb = w; cb < DK / 16; cb += 4) {
             floatx4 acc;
 #pragma unroll
@@ -573,13 +658,13 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
                 const int i = 16 * cb + 4 * (lane >> 4) + e;
                 acc[e] = sg[i] * sdS[i * kBV + (lane & 15)];
             }
-            acc = mma<C / 4>(sQp + 16 * cb, 1, LQ, sdO, kBV, 1, acc, lane);
-            const floatx4 wd = mma<C / 4>(sW + 16 * cb, 1, LQ, sdD, kBV, 1, zero4(), lane);
+            acc = mma2<C / 4>(sQp + 16 * cb, 1, LQ, sdO, kBV, 1, acc, lane);
+            const floatx4 wd = mma2<C / 4>(sW + 16 * cb, 1, LQ, sdD, kBV, 1, zero4(), lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sdS[(16 * cb + 4 * (lane >> 4) + e) * kBV + (lane & 15)] = acc[e] - wd[e];
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (a.gs0)
         for (int e = tid; e < DK * kBV; e += kThreads) {
             const int i = e / kBV, j = e % kBV;
@@ -594,14 +679,14 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
 template <int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
-    constexpr int JT = DV < 32 ? DV : 32, LJ = JT + 1;
+    constexpr int JT = DV < 32 ? DV : 32, LJ = JT + 4;
     constexpr int NR = C / 16, NC = DK / 16, NT3 = NR * NC, NTM = NR * NR;
     constexpr int T3W = (NT3 + 3) / 4, TMW = (NTM + 3) / 4;
-    __shared__ float sD[C * LJ];
-    __shared__ float sdD[C * LJ];
-    __shared__ float sdO[C * LJ];
-    __shared__ float sS0[DK * LJ];
-    __shared__ float sdS1[DK * LJ];
+    __shared__ __attribute__((aligned(16))) float sD[C * LJ];
+    __shared__ __attribute__((aligned(16))) float sdD[C * LJ];
+    __shared__ __attribute__((aligned(16))) float sdO[C * LJ];
+    __shared__ __attribute__((aligned(16))) float sS0[DK * LJ];
+    __shared__ __attribute__((aligned(16))) float sdS1[DK * LJ];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t slot = blockIdx.x;
     int64_t n, c, t0;
@@ -615,19 +700,35 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
 #pragma unroll
     for (int m = 0; m < TMW; ++m) dm[m] = zero4();
     float dgam = 0.f;
+    // value tile j0 .. j0 + JT - 1 of D, dD, S0, dS1 (record) and dO (rows >= L zero), one tile ahead
+    Stage<C, JT> pD, pdD;
+    Stage<DK, JT> pS, pdS;
+    constexpr int kDoPer = (C * JT + kThreads - 1) / kThreads;
+    float rdo[kDoPer];
+    auto fetch = [&](int j0) {
+        pD.load(rec + R::D + j0, DV);
+        pdD.load(rec + R::dD + j0, DV);
+        pS.load(rec + R::S0 + j0, DV);
+        pdS.load(rec + R::dS1 + j0, DV);
+#pragma unroll
+        for (int m = 0; m < kDoPer; ++m) {
+            const int e = tid + m * kThreads, r = e / JT, j = e % JT;
+            rdo[m] = (e < C * JT && r < L) ? a.dO[((t0 + r) * H + h) * (int64_t)DV + j0 + j] : 0.f;
+        }
+    };
+    fetch(0);
     for (int j0 = 0; j0 < DV; j0 += JT) {
-        for (int e = tid; e < C * JT; e += kThreads) {
-            const int r = e / JT, j = e % JT;
-            sD[r * LJ + j] = rec[R::D + r * DV + j0 + j];
-            sdD[r * LJ + j] = rec[R::dD + r * DV + j0 + j];
-            sdO[r * LJ + j] = r < L ? a.dO[((t0 + r) * H + h) * (int64_t)DV + j0 + j] : 0.f;
+        pD.store(sD, LJ);
+        pdD.store(sdD, LJ);
+        pS.store(sS0, LJ);
+        pdS.store(sdS1, LJ);
+#pragma unroll
+        for (int m = 0; m < kDoPer; ++m) {
+            const int e = tid + m * kThreads;
+            if (e < C * JT) sdO[(e / JT) * LJ + e % JT] = rdo[m];
         }
-        for (int e = tid; e < DK * JT; e += kThreads) {
-            const int i = e / JT, j = e % JT;
-            sS0[i * LJ + j] = rec[R::S0 + i * DV + j0 + j];
-            sdS1[i * LJ + j] = rec[R::dS1 + i * DV + j0 + j];
-        }
-        __syncthreads();
+        fetch(j0 + JT < DV ? j0 + JT : j0);
+        lds_barrier();
         // dK' = D dS1^T, dQ+ = dO S0^T, dW = -dD S0^T   ([C][DK] each)
 #pragma unroll
         for (int m = 0; m < T3W; ++m) {
@@ -648,7 +749,7 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
         // dgamma = rowsum(dS1 * S0)
         if (tid < DK)
             for (int j = 0; j < JT; ++j) dgam += sdS1[tid * LJ + j] * sS0[tid * LJ + j];
-        __syncthreads();
+        lds_barrier();
     }
 #pragma unroll
     for (int m = 0; m < T3W; ++m) {
@@ -805,7 +906,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             tV[r * LJ + j] = vv;
             tBV[r * LJ + j] = (r < L ? ld_in<TI>(beta, (t0 + r) * H + h) : 0.f) * vv;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int t = w + 4 * m, rb = t / NR, sb = t % NR;
@@ -828,14 +929,14 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
                 if ((lane & 15) == 0) atomicAdd(&sdb[16 * rb + 4 * (lane >> 4) + e], p);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     BlockRegs br;
     fetch_block(0, false, br);
     for (int cb = 0; cb < NCB; ++cb) {
         put_block(br, false);
         fetch_block(cb + 1 < NCB ? cb + 1 : cb, false, br);
-        __syncthreads();
+        lds_barrier();
         if (w < NR) {  // G rows of block w, then beta K+ = beta k exp(G) into tKp
             const floatx4 G = prefix_rows<C>(tdG, LB, w, lane);
 #pragma unroll
@@ -844,13 +945,13 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
                 tKp[r * LB + cc] = sB[r] * tK[r * LB + cc] * fast_exp(G[e]);
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int t = w + 4 * m, rb = t / NR, sb = t % NR;
             if (t < NT && sb <= rb) dT[m] = mma<4>(tW + 16 * rb * LB, LB, 1, tKp + 16 * sb * LB, 1, LB, dT[m], lane);
         }
-        __syncthreads();
+        lds_barrier();
     }
     fetch_block(0, true, br);  // the second pass's first block, in flight during dA
 #pragma unroll
@@ -863,7 +964,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
                 sA[r * LC + s] = s < r ? dT[m][e] : 0.f;
             }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- dA = -T^T dT T^T (strictly lower): Z = T^T dT, then dA = -Z T^T; dP = Diag(beta) dA,
     //      dbeta += rowsum(dA * P)
 #pragma unroll
@@ -875,13 +976,13 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             for (int e = 0; e < 4; ++e) sZ[(16 * rb + 4 * (lane >> 4) + e) * LC + 16 * sb + (lane & 15)] = z[e];
         }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
         const int t = w + 4 * m, rb = t / NR, sb = t % NR;
         if (t < NT) dT[m] = mma<C / 4>(sZ + 16 * rb * LC, LC, 1, sT + 16 * sb * LC, 1, LC, zero4(), lane);
     }
-    __syncthreads();  // every read of sA (dT) and sZ is done
+    lds_barrier();  // every read of sA (dT) and sZ is done
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
         const int t = w + 4 * m, rb = t / NR, sb = t % NR;
@@ -901,7 +1002,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- channel blocks of 16, wave w < NR owning row block w: G, dK+ = beta T^T dW, the gradients
     //      through the pairwise products P and M, dq, dk, dG, and dg as the suffix sums of dG.
@@ -920,7 +1021,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         const float dgam = br.dgam;
         put_block(br, true);
         fetch_block(cb + 1 < NCB ? cb + 1 : cb, true, br);
-        __syncthreads();
+        lds_barrier();
         float Gr[4] = {0.f, 0.f, 0.f, 0.f}, xk[4] = {0.f, 0.f, 0.f, 0.f};
         if (w < NR) {
             const floatx4 G = prefix_rows<C>(tdG, LB, w, lane);
@@ -940,7 +1041,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
                 if (lr == 0) atomicAdd(&sdb[16 * w + 4 * lg + e], p);
             }
         }
-        __syncthreads();  // G complete; dW and g no longer needed
+        lds_barrier();  // G complete; dW and g no longer needed
         if (w < NR) {
             const float gend = tG[(16 * w + 15) * LB + lr];
             const float gprev = w > 0 ? tG[(16 * w - 1) * LB + lr] : 0.f;
@@ -956,7 +1057,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         float dGr[4] = {0.f, 0.f, 0.f, 0.f}, glast = 0.f;
         if (w < NR) {
             float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f}, ck[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1017,14 +1118,14 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             colsum += __shfl_xor(colsum, 32);
             if (lg == 0) atomicAdd(&sCol[lr], colsum);
         }
-        __syncthreads();  // every read of the scaled tiles is done; the column sums are complete
+        lds_barrier();  // every read of the scaled tiles is done; the column sums are complete
         if (w < NR)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + 4 * lg + e;
                 tdG[r * LB + lr] = dGr[e] + (r == L - 1 ? sCol[lr] + dgam * fast_exp(glast) : 0.f);
             }
-        __syncthreads();
+        lds_barrier();
         // dg = suffix sums over the chunk's rows: dg = Triu(ones) dG
         if (w < NR) {
             floatx4 acc = zero4();
@@ -1045,7 +1146,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sdgh[16 * w + 4 * lg + e] += hsum[e];
         }
-        __syncthreads();  // the tiles are rewritten by the next block
+        lds_barrier();  // the tiles are rewritten by the next block
     }
     if (tid < L) {
         a.gbeta[(t0 + tid) * H + h] = sdb[tid];
