@@ -59,6 +59,8 @@ _MFMA_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_mfma.hip"
 _MFMA_SHA = "073509a341f83dcb2bc156c5079270578a9c9eca013c0bdef30ca97e79c440bb"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
 _DECODE_SHA = "2994ede3f200b6caf1eb3a50f86a9e66dce4f573b9f983c576d7d490a90a2b4d"
+_BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
+_BWD_SHA = "b7b192fa82c941f9633a5c4e12404792480455cd0c0564ccf09d0bee82af58fb"
 
 
 def _counted(fetch_kib, write_kib):
@@ -73,6 +75,10 @@ MEASURED_TRAFFIC = {
                   "bytes": _counted(2674432.0, 1094098.0)},
     "kda_decode": {"source": _DECODE_SRC, "sha256": _DECODE_SHA, "workload": "decode N=256 H=32",
                    "bytes": _counted(267360.0, 528670.0)},
+    # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
+    "kda_backward": {"source": _BWD_SRC, "sha256": _BWD_SHA, "workload": "backward T=65536 H=32",
+                     "bytes": _counted(3459980.0 + 1585003.2 + 2908331.8 + 3795354.0 + 8924190.3,
+                                       5784155.7 + 3226206.7 + 3446224.5 + 3686734.1 + 4399252.3)},
 }
 
 
@@ -378,7 +384,8 @@ def bench_backward(args, res, wide_all):
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
                      "algorithmic_flop_per_launch": flop, "dtype": "f32"},
         "hbm": {"achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": nbytes},
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": nbytes,
+                "traffic": traffic_of("kda_backward", f"backward T={T} H={H}")},
         "parity": {"head": h, "last_tokens": n, "max_rel_err": err, "tol": 2e-3, "ok": bool(err <= 2e-3),
                    "oracle_s": round(t_or, 1)},
     }

@@ -144,3 +144,43 @@ def test_long_context_prefill_then_decode():
     oref2, sref2 = oracle.recurrence(*_heads((dq, dk_, dv_, dg, db), heads, "bf16"), None, sref, vcols=8)
     assert_close(host(outs[:, heads]), oref2, TOL, None, "o (decode tail)")
     assert_close(host(S[:, heads]), sref2, TOL, None, "S (decode tail)")
+
+
+def _backward_full(w, T, heads, with_state):
+    """The chunked backward over all heads of a T-token sequence (the launch bench.py times: B=1, bf16
+    inputs, chunk 64); the oracle's derivative on the sampled heads."""
+    print(f"[{w.name}] backward: generate T={T} H={w.H}", flush=True)
+    q, k, v, g, b = synth.gen_tokens(w, T)
+    s0 = synth.gen_state(w, 1) if with_state else None
+    d_out, d_sT = synth.gen_cotangents(w, T, 1)
+    cu = np.array([0, T], np.int32)
+    print(f"[{w.name}] gpu backward", flush=True)
+    grads = kda.chunked_backward(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(g, "f32"), dev(b, "bf16"),
+                                 torch.from_numpy(cu).cuda(), dev(s0, "f32") if s0 is not None else None,
+                                 d_out=dev(d_out, "f32"), d_state_out=dev(d_sT, "f32"), chunk=w.chunk)
+    torch.cuda.synchronize()
+    for x in grads:
+        assert torch.isfinite(x).all()
+    got = [host(x[:, heads]) for x in grads]
+    print(f"[{w.name}] oracle backward on heads {heads}", flush=True)
+    ref = oracle.backward(*_heads((q, k, v, g, b), heads, "bf16"), cu,
+                          s0[:, heads] if s0 is not None else None, d_o=d_out[:, heads], d_sT=d_sT[:, heads])
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dbeta"), got[:5], ref[:5]):
+        if x.ndim == 2:
+            x, y = x[:, :, None], y[:, :, None]
+        assert_close(x, y, TOL, cu, name)
+    assert_close(got[5], ref[5], TOL, None, "dS0")
+
+
+def test_backward_prefill_workload_all_heads():
+    """Gradients at the prefill workload's size (T=8192, H=32), every head, with a carried state."""
+    w = synth.workload("prefill")
+    w.s0_std = 0.02
+    _backward_full(w, w.T, list(range(w.H)), True)
+
+
+@pytest.mark.timeout(600)
+def test_backward_metric_sampled_heads():
+    """Gradients at the headline prefill's size (T=65,536, H=32), two heads checked."""
+    w = synth.workload("metric")
+    _backward_full(w, w.T, [3, 28], False)
