@@ -150,13 +150,14 @@ __device__ __forceinline__ float gate_at(const float* g, int gate_head, int64_t 
 template <int C>
 __device__ __forceinline__ floatx4 prefix_rows(const float* g, int ldg, int w, int lane) {
     const int r = lane & 15, kq = lane >> 4;
-    floatx4 acc = zero4();
-#pragma unroll 4
-    for (int ks = 0; ks < C / 4; ++ks) {
-        const int s = 4 * ks + kq;
+    floatx4 acc = zero4(), acc1 = zero4();
+#pragma unroll
+    for (int ks = 0; ks < C / 4; ks += 2) {
+        const int s = 4 * ks + kq, s1 = s + 4;
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s <= 16 * w + r ? 1.f : 0.f, g[s * ldg + r], acc, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(s1 <= 16 * w + r ? 1.f : 0.f, g[s1 * ldg + r], acc1, 0, 0, 0);
     }
-    return acc;
+    return acc + acc1;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -838,6 +839,22 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
     const TI* beta = static_cast<const TI*>(a.beta);
     const float* rec = a.ws + (slot * H + h) * R::kFloats;
 
+    // value tiles (dD, v, beta), loaded into registers one tile ahead
+    constexpr int VPT = (C * JT + kThreads - 1) / kThreads;
+    struct ValueRegs {
+        float dd[VPT], v[VPT], b[VPT];
+    } vr;
+    auto fetch_value = [&](int j0) {
+#pragma unroll
+        for (int m = 0; m < VPT; ++m) {
+            const int e = tid + kThreads * m, r = e / JT, j = e % JT;
+            const bool in = (VPT * kThreads == C * JT || e < C * JT) && r < L;
+            vr.dd[m] = (VPT * kThreads == C * JT || e < C * JT) ? rec[R::dD + r * DV + j0 + j] : 0.f;
+            vr.v[m] = in ? ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
+            vr.b[m] = in ? ld_in<TI>(beta, (t0 + r) * H + h) : 0.f;
+        }
+    };
+    fetch_value(0);
     for (int e = tid; e < C * C; e += kThreads) {
         const int r = e / C, s = e % C;
         sT[r * LC + s] = rec[R::T + e];
@@ -899,13 +916,17 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
     for (int m = 0; m < TPW; ++m) dT[m] = zero4();
     for (int j0 = 0; j0 < DV; j0 += JT) {
-        for (int e = tid; e < C * JT; e += kThreads) {
-            const int r = e / JT, j = e % JT;
-            const float vv = r < L ? ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
-            tdD[r * LJ + j] = rec[R::dD + r * DV + j0 + j];
-            tV[r * LJ + j] = vv;
-            tBV[r * LJ + j] = (r < L ? ld_in<TI>(beta, (t0 + r) * H + h) : 0.f) * vv;
+        // this tile from registers; the next one is loaded while this one is used
+#pragma unroll
+        for (int m = 0; m < VPT; ++m) {
+            const int e = tid + kThreads * m, r = e / JT, j = e % JT;
+            if (VPT * kThreads == C * JT || e < C * JT) {
+                tdD[r * LJ + j] = vr.dd[m];
+                tV[r * LJ + j] = vr.v[m];
+                tBV[r * LJ + j] = vr.b[m] * vr.v[m];
+            }
         }
+        fetch_value(j0 + JT < DV ? j0 + JT : j0);
         lds_barrier();
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
@@ -966,7 +987,15 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
     }
     lds_barrier();
     // ---- dA = -T^T dT T^T (strictly lower): Z = T^T dT, then dA = -Z T^T; dP = Diag(beta) dA,
-    //      dbeta += rowsum(dA * P)
+    //      dbeta += rowsum(dA * P) (P loaded first, in flight during the two products)
+    float pv[TPW][4];
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+        const int t = w + 4 * m, rb = t / NR, sb = t % NR;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pv[m][e] = t < NT ? rec[R::P + (16 * rb + 4 * (lane >> 4) + e) * C + 16 * sb + (lane & 15)] : 0.f;
+    }
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
         const int t = w + 4 * m, rb = t / NR, sb = t % NR;
@@ -992,7 +1021,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * (lane >> 4) + e, s = 16 * sb + (lane & 15);
                 const float da = s < r ? -dT[m][e] : 0.f;
-                part[e] = da * rec[R::P + r * C + s];
+                part[e] = da * pv[m][e];
                 sA[r * LC + s] = sB[r] * da;  // dP
             }
 #pragma unroll
@@ -1081,20 +1110,24 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ck[e] += fast_exp(gm - Gr[e]) * y[e];
             }
-            // pairs inside block w
+            // pairs inside block w: all 16 rows of the block, the wrong side of the diagonal masked
+            // (its exponent set to -inf, so the factor is exactly 0), so that the loops unroll
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + 4 * lg + e;
-                for (int s2 = 16 * w; s2 <= r; ++s2) {
-                    const float ev = fast_exp(Gr[e] - tG[s2 * LB + lr]) * tK[s2 * LB + lr];
-                    rq[e] += sdM[r * LC + s2] * ev;
-                    rk[e] += sA[r * LC + s2] * ev;  // dP is zero on the diagonal
+#pragma unroll 2
+                for (int i = 0; i < 16; ++i) {
+                    const int s2 = 16 * w + i;
+                    const float gs = tG[s2 * LB + lr];
+                    // row role: s2 <= r
+                    const float er = fast_exp(s2 <= r ? Gr[e] - gs : -INFINITY) * tK[s2 * LB + lr];
+                    rq[e] += sdM[r * LC + s2] * er;
+                    rk[e] += sA[r * LC + s2] * er;  // dP is zero on the diagonal
+                    // column role: s2 > r, and the diagonal term dM[r][r] q_r
+                    const float ec = s2 > r ? fast_exp(gs - Gr[e]) : (s2 == r ? 1.f : 0.f);
+                    ck[e] += ec * (sdM[s2 * LC + r] * tQ[s2 * LB + lr] + (s2 > r ? sA[s2 * LC + r] : 0.f) *
+                                                                             tK[s2 * LB + lr]);
                 }
-                for (int r2 = r + 1; r2 < 16 * w + 16; ++r2) {
-                    const float ev = fast_exp(tG[r2 * LB + lr] - Gr[e]);
-                    ck[e] += ev * (sdM[r2 * LC + r] * tQ[r2 * LB + lr] + sA[r2 * LC + r] * tK[r2 * LB + lr]);
-                }
-                ck[e] += sdM[r * LC + r] * tQ[r * LB + lr];
             }
             glast = tG[(C - 1) * LB + lr];
             float colsum = 0.f;
@@ -1128,13 +1161,16 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         lds_barrier();
         // dg = suffix sums over the chunk's rows: dg = Triu(ones) dG
         if (w < NR) {
-            floatx4 acc = zero4();
-#pragma unroll 4
-            for (int ks = 0; ks < C / 4; ++ks) {
-                const int s2 = 4 * ks + lg;
+            floatx4 acc = zero4(), acc1 = zero4();
+#pragma unroll
+            for (int ks = 0; ks < C / 4; ks += 2) {
+                const int s2 = 4 * ks + lg, s3 = s2 + 4;
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s2 >= 16 * w + lr ? 1.f : 0.f, tdG[s2 * LB + lr], acc, 0, 0,
                                                            0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(s3 >= 16 * w + lr ? 1.f : 0.f, tdG[s3 * LB + lr], acc1, 0,
+                                                            0, 0);
             }
+            acc += acc1;
             float hsum[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
