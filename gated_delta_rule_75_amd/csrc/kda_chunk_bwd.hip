@@ -790,8 +790,8 @@ struct ChunkLds {
     static constexpr int kStage = kStage0 > LC ? kStage0 : LC;  // floats per row of the staging area
     static constexpr size_t kFloats = 3 * (size_t)C * LC      // T, dM, dT -> dP
                                       + (size_t)C * kStage    // staged tiles (see the kernel)
-                                      + 4 * (size_t)C         // beta, dbeta, dg (one gate per head)
-                                      + 2 * 16;               // per-block column sums, dgamma
+                                      + 6 * (size_t)C         // beta, dbeta per wave, dg (one gate per head)
+                                      + 4 * 16;               // per-wave column sums of a channel block
     static constexpr size_t kBytes = kFloats * sizeof(float);
 };
 
@@ -807,9 +807,11 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
     float* sA = sdM + C * LC;           // [C][LC]  dT, then dP
     float* sX = sA + C * LC;            // [C][kStage] staging area
     float* sB = sX + C * Lds::kStage;   // [C]
-    float* sdb = sB + C;                // [C]
-    float* sdgh = sdb + C;              // [C]
-    float* sCol = sdgh + 2 * C;         // [16] column sums of dK' * K' in the current channel block
+    // dbeta and the column sums are accumulated per wave and added in wave order at the end, so
+    // the result does not depend on the order the waves run in (no atomics)
+    float* sdbw = sB + C;               // [4][C] dbeta partial sums of each wave
+    float* sdgh = sdbw + 4 * C;         // [C]
+    float* sColw = sdgh + C;            // [4][16] column sums of dK' * K' in the current channel block
     // value tiles: dD, V, beta V ([C][LJ] each); Z ([C][LC]); channel blocks ([C][LB] each): K, Q,
     // dW (then K scaled for the row role), G, beta K+ (first pass) or K scaled for the column role
     // (second pass), g (then Q scaled for the column role, then dG)
@@ -862,7 +864,8 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
     }
     if (tid < C) {
         sB[tid] = tid < L ? ld_in<TI>(beta, (t0 + tid) * H + h) : 0.f;
-        sdb[tid] = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) sdbw[wv * C + tid] = 0.f;
         sdgh[tid] = 0.f;
     }
 
@@ -906,7 +909,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             tdG[r * LB + cc] = br.g[i];
             if (second) tQ[r * LB + cc] = br.q[i];
         }
-        if (second && tid < 16) sCol[tid] = 0.f;
+        if (second && tid < 64) sColw[tid] = 0.f;
     };
 
     // ---- dT = dD (beta V)^T + dW (beta K+)^T, strictly lower part (wave w owns tiles w, w+4, ...),
@@ -947,7 +950,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float p = sum16(part[e]);
-                if ((lane & 15) == 0) atomicAdd(&sdb[16 * rb + 4 * (lane >> 4) + e], p);
+                if ((lane & 15) == 0) sdbw[w * C + 16 * rb + 4 * (lane >> 4) + e] += p;
             }
         }
         lds_barrier();
@@ -1027,7 +1030,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float p = sum16(part[e]);
-                if ((lane & 15) == 0) atomicAdd(&sdb[16 * rb + 4 * (lane >> 4) + e], p);
+                if ((lane & 15) == 0) sdbw[w * C + 16 * rb + 4 * (lane >> 4) + e] += p;
             }
         }
     }
@@ -1067,7 +1070,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float p = sum16(part[e]);
-                if (lr == 0) atomicAdd(&sdb[16 * w + 4 * lg + e], p);
+                if (lr == 0) sdbw[w * C + 16 * w + 4 * lg + e] += p;
             }
         }
         lds_barrier();  // G complete; dW and g no longer needed
@@ -1149,14 +1152,17 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             }
             colsum += __shfl_xor(colsum, 16);
             colsum += __shfl_xor(colsum, 32);
-            if (lg == 0) atomicAdd(&sCol[lr], colsum);
+            if (lg == 0) sColw[16 * w + lr] = colsum;
         }
         lds_barrier();  // every read of the scaled tiles is done; the column sums are complete
         if (w < NR)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + 4 * lg + e;
-                tdG[r * LB + lr] = dGr[e] + (r == L - 1 ? sCol[lr] + dgam * fast_exp(glast) : 0.f);
+                float col = 0.f;
+#pragma unroll
+                for (int wv = 0; wv < NR; ++wv) col += sColw[16 * wv + lr];
+                tdG[r * LB + lr] = dGr[e] + (r == L - 1 ? col + dgam * fast_exp(glast) : 0.f);
             }
         lds_barrier();
         // dg = suffix sums over the chunk's rows: dg = Triu(ones) dG
@@ -1185,7 +1191,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         lds_barrier();  // the tiles are rewritten by the next block
     }
     if (tid < L) {
-        a.gbeta[(t0 + tid) * H + h] = sdb[tid];
+        a.gbeta[(t0 + tid) * H + h] = sdbw[tid] + sdbw[C + tid] + sdbw[2 * C + tid] + sdbw[3 * C + tid];
         if (a.gate_head) a.gg[(t0 + tid) * H + h] = sdgh[tid];
     }
 }

@@ -79,3 +79,22 @@ def test_backward_empty_segments_pass_the_state_gradient():
     """Segments with no tokens: dL/dS_0 = dL/dS_T exactly, nothing else is written."""
     got, ref = _run("f32", 16, 16, [0, 0], True, True)
     np.testing.assert_array_equal(got[5], ref[5])
+
+
+def test_backward_is_deterministic():
+    """Two calls on the same inputs give bitwise equal gradients (no atomics; fixed summation order)."""
+    w = synth.Workload("bwd", 9, H=4, dk=128, dv=128, dtype="bf16", chunk=64, s0_std=0.05)
+    lengths = [700, 64, 333]
+    cu = synth.cu_seqlens(lengths)
+    T, N = int(cu[-1]), len(lengths)
+    st, _ = make_inputs(w, T)
+    s0 = synth.gen_state(w, N)
+    d_out, d_sT = synth.gen_cotangents(w, T, N)
+    args = [dev(st[0], "bf16"), dev(st[1], "bf16"), dev(st[2], "bf16"), dev(st[3], "f32"), dev(st[4], "bf16"),
+            torch.from_numpy(cu).cuda(), dev(s0, "f32")]
+    kw = dict(d_out=dev(d_out, "f32"), d_state_out=dev(d_sT, "f32"))
+    first = kda.chunked_backward(*args, **kw)
+    second = kda.chunked_backward(*args, **kw)
+    torch.cuda.synchronize()
+    for x, y in zip(first, second):
+        assert torch.equal(x, y)
