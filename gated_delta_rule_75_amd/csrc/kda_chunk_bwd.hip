@@ -56,6 +56,30 @@ __device__ __forceinline__ floatx4 mma(const float* A, int ar, int ak, const flo
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// acc += A (16 x 16 KS) * B (16 KS x 16) with both operands contiguous along k in LDS:
+// A(r, k) = A[r * ar + k] and B(k, c) = Bt[c * bc + k], ar and bc multiples of 4.  Lane (r, kq) feeds
+// k = 16 s + 4 kq + i at the i-th of the four steps of group s (any assignment of k to steps gives the
+// same sum), so each group takes one 16-byte LDS read per operand; even and odd groups go to two
+// accumulators.
+template <int KS>
+__device__ __forceinline__ floatx4 mma_k4(const float* A, int ar, const float* Bt, int bc, floatx4 acc, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+    const float* pa = A + r * ar + 4 * kq;
+    const float* pb = Bt + r * bc + 4 * kq;
+    floatx4 acc1 = zero4();
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const float4 a4 = *reinterpret_cast<const float4*>(pa + 16 * s);
+        const float4 b4 = *reinterpret_cast<const float4*>(pb + 16 * s);
+        floatx4& x = (s & 1) ? acc1 : acc;
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, b4.x, x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, b4.y, x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, b4.z, x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, b4.w, x, 0, 0, 0);
+    }
+    return acc + acc1;
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations (lgkmcnt) but not for
 // its outstanding global loads and stores, so loads issued one step ahead stay in flight across it
 // (a __syncthreads() fence would drain them).  No kernel here reads global memory that another
@@ -98,12 +122,16 @@ __device__ __forceinline__ float sum16(float x) {
 // Workspace record of one (chunk slot, head), in floats.
 template <int DK, int DV, int C>
 struct Rec {
+    // the forward chain's operands (W, U, K'^T), then the reverse chain's (K', Q+^T, W^T, M^T): each
+    // stored with the contraction index contiguous, as the chains consume it
     static constexpr int64_t W = 0;                       // [C][DK]  T Diag(beta) K+
     static constexpr int64_t U = W + C * DK;              // [C][DV]  T Diag(beta) V
-    static constexpr int64_t Kd = U + C * DV;             // [C][DK]  K'
-    static constexpr int64_t Qp = Kd + C * DK;            // [C][DK]  Q+
-    static constexpr int64_t M = Qp + C * DK;             // [C][C]
-    static constexpr int64_t T = M + C * C;               // [C][C]
+    static constexpr int64_t KdT = U + C * DV;            // [DK][C]  K'^T
+    static constexpr int64_t Kd = KdT + DK * C;           // [C][DK]  K'
+    static constexpr int64_t QpT = Kd + C * DK;           // [DK][C]  Q+^T
+    static constexpr int64_t WT = QpT + DK * C;           // [DK][C]  W^T
+    static constexpr int64_t MT = WT + DK * C;            // [C][C]   M^T
+    static constexpr int64_t T = MT + C * C;              // [C][C]
     static constexpr int64_t P = T + C * C;               // [C][C]   strictly lower
     static constexpr int64_t gam = P + C * C;             // [DK]
     static constexpr int64_t S0 = gam + DK;               // [DK][DV] state entering the chunk
@@ -326,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
     lds_barrier();
     for (int e = tid; e < C * C; e += kThreads) {
         const int r = e / C, s2 = e % C;
-        rec[R::M + e] = sM[r * LC + s2];
+        rec[R::MT + e] = sM[s2 * LC + r];  // M^T[r][s2] = M[s2][r]
         rec[R::P + e] = sP[r * LC + s2];
     }
     lds_barrier();
@@ -376,13 +404,19 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
     }
     for (int e = tid; e < C * C; e += kThreads) rec[R::T + e] = sT[(e / C) * LC + e % C];
 
-    // ---- pass 2: Q+, K', gamma and W = T (beta K+), channel tile by channel tile
+    // ---- pass 2: Q+^T, K', K'^T, gamma and W = T (beta K+), channel tile by channel tile
     for (int c0 = 0; c0 < DK; c0 += CT) {
         stage_tile(c0);
-        for (int e = tid; e < C * CT; e += kThreads) {
+        for (int e = tid; e < C * CT; e += kThreads) {  // channel-major outputs (token index fastest)
+            const int cc = e / C, r = e % C;
+            const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc];
+            rec[R::QpT + (c0 + cc) * C + r] = tQ[r * LT + cc] * fast_exp(g);
+            rec[R::KdT + (c0 + cc) * C + r] = tK[r * LT + cc] * fast_exp(gl - g);
+        }
+        lds_barrier();
+        for (int e = tid; e < C * CT; e += kThreads) {  // token-major outputs; K becomes beta K+ in place
             const int r = e / CT, cc = e % CT;
             const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc], kk = tK[r * LT + cc];
-            rec[R::Qp + r * DK + c0 + cc] = tQ[r * LT + cc] * fast_exp(g);
             rec[R::Kd + r * DK + c0 + cc] = kk * fast_exp(gl - g);
             tK[r * LT + cc] = sB[r] * kk * fast_exp(g);
         }
@@ -393,6 +427,8 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             const floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, tK + 16 * cb, LT, 1, zero4(), lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) rec[R::W + (16 * rb + 4 * lg + e) * DK + c0 + 16 * cb + lr] = acc[e];
+            *reinterpret_cast<float4*>(rec + R::WT + (int64_t)(c0 + 16 * cb + lr) * C + 16 * rb + 4 * lg) =
+                make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
         lds_barrier();
     }
@@ -486,20 +522,22 @@ __device__ __forceinline__ void chain_unit(int64_t gid, int64_t nh_total, int64_
 }
 
 // ------------------------------------------------------------------------------------------
-// fwd_chain: one workgroup per (sequence, head, 16 value columns); states entering each chunk
+// fwd_chain: one workgroup per (sequence, head, 16 value columns); states entering each chunk.
+// Every product reads both operands contiguous along its contraction index (mma_k4): the state
+// block and D are kept transposed in LDS ([value column][contraction index]).
 // ------------------------------------------------------------------------------------------
 template <int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
-    constexpr int NVB = DV / kBV, LW = DK + 4, LQ = DK + 16;
-    __shared__ __attribute__((aligned(16))) float sW[C * LW];   // W rows (A operand by rows)
-    __shared__ __attribute__((aligned(16))) float sKd[C * LQ];  // K' rows (A operand by columns)
+    constexpr int NVB = DV / kBV, LW = DK + 4, LT = C + 4;
+    __shared__ __attribute__((aligned(16))) float sW[C * LW];    // W: A of W S
+    __shared__ __attribute__((aligned(16))) float sKT[DK * LT];  // K'^T: A of K'^T D
     __shared__ __attribute__((aligned(16))) float sU[C * kBV];
     __shared__ __attribute__((aligned(16))) float sg[DK];
-    __shared__ __attribute__((aligned(16))) float sS[DK * kBV];
-    __shared__ __attribute__((aligned(16))) float sD[C * kBV];
-    __shared__ __attribute__((aligned(16))) float sDummy[64];  // sink of the L2 warm-up loads
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __shared__ __attribute__((aligned(16))) float sSt[kBV * LW];  // state block [column][key channel]
+    __shared__ __attribute__((aligned(16))) float sDt[kBV * LT];  // D [column][token]
+    __shared__ __attribute__((aligned(16))) float sDummy[64];     // sink of the L2 warm-up loads
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     int64_t nh;
     int vb;
     chain_unit<NVB>(blockIdx.x, mp.N * a.H, nh, vb);
@@ -509,81 +547,82 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
     const int H = a.H;
     for (int e = tid; e < DK * kBV; e += kThreads) {
         const int i = e / kBV, j = e % kBV;
-        sS[e] = a.s0 ? a.s0[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] : 0.f;
+        sSt[j * LW + i] = a.s0 ? a.s0[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] : 0.f;
     }
     const int64_t bos = mp.cu[n], eos = mp.cu[n + 1];
     const int64_t nck = (eos - bos + C - 1) / C, slot0 = mp.base(n);
     if (nck == 0) return;  // uniform
-    Stage<C, DK> pW, pK;
+    Stage<C, DK> pW;
+    Stage<DK, C> pK;
     Stage<C, kBV> pU;
     Stage<1, DK> pg;
     auto fetch = [&](int64_t c) {
         const float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
         pW.load(rec + R::W, DK);
-        pK.load(rec + R::Kd, DK);
+        pK.load(rec + R::KdT, C);
         pU.load(rec + R::U + vb * kBV, DV);
         pg.load(rec + R::gam, DK);
     };
     fetch(0);
     for (int64_t c = 0; c < nck; ++c) {
         float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
-        lds_barrier();  // the previous chunk is done with the LDS operands; sS is its final state
+        lds_barrier();  // the previous chunk is done with the LDS operands; sSt is its final state
         pW.store(sW, LW);
-        pK.store(sKd, LQ);
+        pK.store(sKT, LT);
         pU.store(sU, kBV);
         pg.store(sg, DK);
         fetch(c + 1 < nck ? c + 1 : c);
-        {  // W, U and K' (one contiguous range) of the chunk kWarm ahead
+        {  // W, U and K'^T (one contiguous range) of the chunk kWarm ahead
             const float* wrec = a.ws + ((slot0 + (c + kWarm < nck ? c + kWarm : nck - 1)) * H + h) * R::kFloats;
-            warm_range<R::Kd + C * DK>(wrec, 0, vb, NVB, dummy);
+            warm_range<R::Kd>(wrec, 0, vb, NVB, dummy);
         }
-        for (int e = tid; e < DK * kBV; e += kThreads) rec[R::S0 + (e / kBV) * DV + vb * kBV + e % kBV] = sS[e];
+        for (int e = tid; e < DK * kBV; e += kThreads)
+            rec[R::S0 + (e / kBV) * DV + vb * kBV + e % kBV] = sSt[(e % kBV) * LW + e / kBV];
         lds_barrier();
-        // D = U - W S
+        // D = U - W S (rows 16 w .. 16 w + 15 per wave)
         for (int rb = w; rb < C / 16; rb += 4) {
-            const floatx4 acc = mma2<DK / 4>(sW + 16 * rb * LW, LW, 1, sS, kBV, 1, zero4(), lane);
+            const floatx4 acc = mma_k4<DK / 16>(sW + 16 * rb * LW, LW, sSt, LW, zero4(), lane);
+            float4 dv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * (lane >> 4) + e, j = lane & 15;
-                const float d = sU[r * kBV + j] - acc[e];
-                sD[r * kBV + j] = d;
-                rec[R::D + r * DV + vb * kBV + j] = d;
+                const int r = 16 * rb + 4 * lg + e;
+                const float d = sU[r * kBV + lr] - acc[e];
+                (&dv.x)[e] = d;
+                rec[R::D + r * DV + vb * kBV + lr] = d;
             }
+            *reinterpret_cast<float4*>(sDt + lr * LT + 16 * rb + 4 * lg) = dv;
         }
         lds_barrier();
         // S <- Diag(gamma) S + K'^T D
 #pragma unroll
         for (int cb = w; cb < DK / 16; cb += 4) {
-            floatx4 acc;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * cb + 4 * (lane >> 4) + e;
-                acc[e] = sg[i] * sS[i * kBV + (lane & 15)];
-            }
-            acc = mma2<C / 4>(sKd + 16 * cb, 1, LQ, sD, kBV, 1, acc, lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sS[(16 * cb + 4 * (lane >> 4) + e) * kBV + (lane & 15)] = acc[e];
+            const int i0 = 16 * cb + 4 * lg;
+            const float4 s4 = *reinterpret_cast<const float4*>(sSt + lr * LW + i0);
+            floatx4 acc = {sg[i0] * s4.x, sg[i0 + 1] * s4.y, sg[i0 + 2] * s4.z, sg[i0 + 3] * s4.w};
+            acc = mma_k4<C / 16>(sKT + 16 * cb * LT, LT, sDt, LT, acc, lane);
+            *reinterpret_cast<float4*>(sSt + lr * LW + i0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
 }
 
 // ------------------------------------------------------------------------------------------
-// rev_chain: one workgroup per (sequence, head, 16 value columns); chunks in reverse
+// rev_chain: one workgroup per (sequence, head, 16 value columns); chunks in reverse.  dS, dO and
+// dD are kept transposed in LDS ([value column][contraction index]).
 // ------------------------------------------------------------------------------------------
 template <int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
-    constexpr int NVB = DV / kBV, LW = DK + 4, LQ = DK + 16, LM = C + 16;
-    __shared__ __attribute__((aligned(16))) float sKd[C * LW];  // K' rows (A operand by rows)
-    __shared__ __attribute__((aligned(16))) float sM[C * LM];   // M (A operand by columns)
-    __shared__ __attribute__((aligned(16))) float sQp[C * LQ];  // Q+ (A operand by columns)
-    __shared__ __attribute__((aligned(16))) float sW[C * LQ];   // W (A operand by columns)
+    constexpr int NVB = DV / kBV, LW = DK + 4, LT = C + 4;
+    __shared__ __attribute__((aligned(16))) float sKd[C * LW];   // K': A of K' dS
+    __shared__ __attribute__((aligned(16))) float sMT[C * LT];   // M^T: A of M^T dO
+    __shared__ __attribute__((aligned(16))) float sQT[DK * LT];  // Q+^T: A of Q+^T dO
+    __shared__ __attribute__((aligned(16))) float sWT[DK * LT];  // W^T: A of W^T dD
     __shared__ __attribute__((aligned(16))) float sg[DK];
-    __shared__ __attribute__((aligned(16))) float sdS[DK * kBV];
-    __shared__ __attribute__((aligned(16))) float sdO[C * kBV];
-    __shared__ __attribute__((aligned(16))) float sdD[C * kBV];
-    __shared__ __attribute__((aligned(16))) float sDummy[64];  // sink of the L2 warm-up loads
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __shared__ __attribute__((aligned(16))) float sdSt[kBV * LW];  // dS [column][key channel]
+    __shared__ __attribute__((aligned(16))) float sdOt[kBV * LT];  // dO [column][token]
+    __shared__ __attribute__((aligned(16))) float sdDt[kBV * LT];  // dD [column][token]
+    __shared__ __attribute__((aligned(16))) float sDummy[64];      // sink of the L2 warm-up loads
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     int64_t nh;
     int vb;
     chain_unit<NVB>(blockIdx.x, mp.N * a.H, nh, vb);
@@ -593,21 +632,22 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
     const int H = a.H;
     for (int e = tid; e < DK * kBV; e += kThreads) {
         const int i = e / kBV, j = e % kBV;
-        sdS[e] = a.dsT ? a.dsT[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] : 0.f;
+        sdSt[j * LW + i] = a.dsT ? a.dsT[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] : 0.f;
     }
     const int64_t bos = mp.cu[n], eos = mp.cu[n + 1];
     const int64_t nck = (eos - bos + C - 1) / C, slot0 = mp.base(n);
-    Stage<C, DK> pK, pQ, pW;
+    Stage<C, DK> pK;
     Stage<C, C> pM;
+    Stage<DK, C> pQ, pW;
     Stage<1, DK> pg;
     constexpr int kDoPer = (C * kBV + kThreads - 1) / kThreads;
     float rdo[kDoPer];
     auto fetch = [&](int64_t c) {
         const float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
         pK.load(rec + R::Kd, DK);
-        pM.load(rec + R::M, C);
-        pQ.load(rec + R::Qp, DK);
-        pW.load(rec + R::W, DK);
+        pM.load(rec + R::MT, C);
+        pQ.load(rec + R::QpT, C);
+        pW.load(rec + R::WT, C);
         pg.load(rec + R::gam, DK);
         const int64_t t0 = bos + c * C;
 #pragma unroll
@@ -619,57 +659,51 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
     if (nck > 0) fetch(nck - 1);
     for (int64_t c = nck - 1; c >= 0; --c) {
         float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
-        lds_barrier();  // the previous chunk is done with the LDS operands; sdS is its result
+        lds_barrier();  // the previous chunk is done with the LDS operands; sdSt is its result
         pK.store(sKd, LW);
-        pM.store(sM, LM);
-        pQ.store(sQp, LQ);
-        pW.store(sW, LQ);
+        pM.store(sMT, LT);
+        pQ.store(sQT, LT);
+        pW.store(sWT, LT);
         pg.store(sg, DK);
 #pragma unroll
         for (int m = 0; m < kDoPer; ++m) {
             const int e = tid + m * kThreads;
-            if (e < C * kBV) sdO[e] = rdo[m];
+            if (e < C * kBV) sdOt[(e % kBV) * LT + e / kBV] = rdo[m];
         }
         fetch(c > 0 ? c - 1 : c);
-        {  // W (first range), then K', Q+ and M (second range) of the chunk kWarm behind
+        {  // K', Q+^T, W^T and M^T (one contiguous range) of the chunk kWarm behind
             const float* wrec = a.ws + ((slot0 + (c >= kWarm ? c - kWarm : 0)) * H + h) * R::kFloats;
-            warm_range<C * DK>(wrec, R::W, vb, NVB, dummy);
             warm_range<R::T - R::Kd>(wrec, R::Kd, vb, NVB, dummy);
         }
-        for (int e = tid; e < DK * kBV; e += kThreads) rec[R::dS1 + (e / kBV) * DV + vb * kBV + e % kBV] = sdS[e];
+        for (int e = tid; e < DK * kBV; e += kThreads)
+            rec[R::dS1 + (e / kBV) * DV + vb * kBV + e % kBV] = sdSt[(e % kBV) * LW + e / kBV];
         lds_barrier();
         // dD = K' dS + M^T dO
         for (int rb = w; rb < C / 16; rb += 4) {
-            floatx4 acc = mma2<DK / 4>(sKd + 16 * rb * LW, LW, 1, sdS, kBV, 1, zero4(), lane);
-            acc = mma2<C / 4>(sM + 16 * rb, 1, LM, sdO, kBV, 1, acc, lane);
+            floatx4 acc = mma_k4<DK / 16>(sKd + 16 * rb * LW, LW, sdSt, LW, zero4(), lane);
+            acc = mma_k4<C / 16>(sMT + 16 * rb * LT, LT, sdOt, LT, acc, lane);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * (lane >> 4) + e, j = lane & 15;
-                sdD[r * kBV + j] = acc[e];
-                rec[R::dD + r * DV + vb * kBV + j] = acc[e];
-            }
+            for (int e = 0; e < 4; ++e) rec[R::dD + (16 * rb + 4 * lg + e) * DV + vb * kBV + lr] = acc[e];
+            *reinterpret_cast<float4*>(sdDt + lr * LT + 16 * rb + 4 * lg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
         lds_barrier();
         // dS <- Diag(gamma) dS + Q+^T dO - W^T dD
 #pragma unroll
         for (int cb = w; cb < DK / 16; cb += 4) {
-            floatx4 acc;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * cb + 4 * (lane >> 4) + e;
-                acc[e] = sg[i] * sdS[i * kBV + (lane & 15)];
-            }
-            acc = mma2<C / 4>(sQp + 16 * cb, 1, LQ, sdO, kBV, 1, acc, lane);
-            const floatx4 wd = mma2<C / 4>(sW + 16 * cb, 1, LQ, sdD, kBV, 1, zero4(), lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sdS[(16 * cb + 4 * (lane >> 4) + e) * kBV + (lane & 15)] = acc[e] - wd[e];
+            const int i0 = 16 * cb + 4 * lg;
+            const float4 s4 = *reinterpret_cast<const float4*>(sdSt + lr * LW + i0);
+            floatx4 acc = {sg[i0] * s4.x, sg[i0 + 1] * s4.y, sg[i0 + 2] * s4.z, sg[i0 + 3] * s4.w};
+            acc = mma_k4<C / 16>(sQT + 16 * cb * LT, LT, sdOt, LT, acc, lane);
+            const floatx4 wd = mma_k4<C / 16>(sWT + 16 * cb * LT, LT, sdDt, LT, zero4(), lane);
+            *reinterpret_cast<float4*>(sdSt + lr * LW + i0) =
+                make_float4(acc[0] - wd[0], acc[1] - wd[1], acc[2] - wd[2], acc[3] - wd[3]);
         }
     }
     lds_barrier();
     if (a.gs0)
         for (int e = tid; e < DK * kBV; e += kThreads) {
             const int i = e / kBV, j = e % kBV;
-            a.gs0[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] = sdS[e];
+            a.gs0[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] = sdSt[j * LW + i];
         }
 }
 
@@ -735,9 +769,9 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
         for (int m = 0; m < T3W; ++m) {
             const int t = w + 4 * m, rb = t % NR, cb = t / NR;
             if (t < NT3) {
-                kd[m] = mma<JT / 4>(sD + 16 * rb * LJ, LJ, 1, sdS1 + 16 * cb * LJ, 1, LJ, kd[m], lane);
-                qp[m] = mma<JT / 4>(sdO + 16 * rb * LJ, LJ, 1, sS0 + 16 * cb * LJ, 1, LJ, qp[m], lane);
-                dw[m] = mma<JT / 4>(sdD + 16 * rb * LJ, LJ, 1, sS0 + 16 * cb * LJ, 1, LJ, dw[m], lane);
+                kd[m] = mma_k4<JT / 16>(sD + 16 * rb * LJ, LJ, sdS1 + 16 * cb * LJ, LJ, kd[m], lane);
+                qp[m] = mma_k4<JT / 16>(sdO + 16 * rb * LJ, LJ, sS0 + 16 * cb * LJ, LJ, qp[m], lane);
+                dw[m] = mma_k4<JT / 16>(sdD + 16 * rb * LJ, LJ, sS0 + 16 * cb * LJ, LJ, dw[m], lane);
             }
         }
         // dM = tril(dO D^T)   ([C][C], the tiles on or below the diagonal)
@@ -745,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
         for (int m = 0; m < TMW; ++m) {
             const int t = w + 4 * m, rb = t / NR, sb = t % NR;
             if (t < NTM && sb <= rb)
-                dm[m] = mma<JT / 4>(sdO + 16 * rb * LJ, LJ, 1, sD + 16 * sb * LJ, 1, LJ, dm[m], lane);
+                dm[m] = mma_k4<JT / 16>(sdO + 16 * rb * LJ, LJ, sD + 16 * sb * LJ, LJ, dm[m], lane);
         }
         // dgamma = rowsum(dS1 * S0)
         if (tid < DK)
