@@ -178,14 +178,13 @@ __device__ __forceinline__ float gate_at(const float* g, int gate_head, int64_t 
 template <int C>
 __device__ __forceinline__ floatx4 prefix_rows(const float* g, int ldg, int w, int lane) {
     const int r = lane & 15, kq = lane >> 4;
-    floatx4 acc = zero4(), acc1 = zero4();
-#pragma unroll
-    for (int ks = 0; ks < C / 4; ks += 2) {
-        const int s = 4 * ks + kq, s1 = s + 4;
+    floatx4 acc = zero4();
+#pragma unroll 4
+    for (int ks = 0; ks < C / 4; ++ks) {
+        const int s = 4 * ks + kq;
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s <= 16 * w + r ? 1.f : 0.f, g[s * ldg + r], acc, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(s1 <= 16 * w + r ? 1.f : 0.f, g[s1 * ldg + r], acc1, 0, 0, 0);
     }
-    return acc + acc1;
+    return acc;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1108,19 +1107,20 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             }
         }
         lds_barrier();  // G complete; dW and g no longer needed
+        // block w's scaled tiles: against its last row (K) and against the row before it (Q, K; row -1
+        // has G = 0)
+        float gend = 0.f, gprev = 0.f;
         if (w < NR) {
-            const float gend = tG[(16 * w + 15) * LB + lr];
-            const float gprev = w > 0 ? tG[(16 * w - 1) * LB + lr] : 0.f;
+            gend = tG[(16 * w + 15) * LB + lr];
+            gprev = w > 0 ? tG[(16 * w - 1) * LB + lr] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + 4 * lg + e;
                 const float kr = tK[r * LB + lr], qr = tQ[r * LB + lr];
-                if (w < NR - 1) tKc[r * LB + lr] = kr * fast_exp(gend - Gr[e]);
-                if (w > 0) {
-                    const float f = fast_exp(Gr[e] - gprev);
-                    tQr[r * LB + lr] = qr * f;
-                    tKr[r * LB + lr] = kr * f;
-                }
+                tKc[r * LB + lr] = kr * fast_exp(gend - Gr[e]);
+                const float f = fast_exp(Gr[e] - gprev);
+                tQr[r * LB + lr] = qr * f;
+                tKr[r * LB + lr] = kr * f;
             }
         }
         lds_barrier();
@@ -1147,12 +1147,28 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ck[e] += fast_exp(gm - Gr[e]) * y[e];
             }
-            // pairs inside block w: all 16 rows of the block, the wrong side of the diagonal masked
-            // (its exponent set to -inf, so the factor is exactly 0), so that the loops unroll
+            // pairs inside block w.  On the matrix cores with the decay split at the block's last row
+            // (row role) or at the row before it (column role): the products are bounded by the scaled
+            // tiles, and the other factor by exp(D), D the block's 16-token decay.  If D > 64 for some
+            // channel of the wave the pairs take their own exponentials instead (the wrong side of the
+            // diagonal masked with a -inf exponent).
+            if (!__any(gprev - gend > 64.f)) {
+                const floatx4 xm = mma<4>(sdM + 16 * w * LC + 16 * w, LC, 1, tKc + 16 * w * LB, LB, 1, zero4(), lane);
+                const floatx4 xp = mma<4>(sA + 16 * w * LC + 16 * w, LC, 1, tKc + 16 * w * LB, LB, 1, zero4(), lane);
+                floatx4 y = mma<4>(sdM + 16 * w * LC + 16 * w, 1, LC, tQr + 16 * w * LB, LB, 1, zero4(), lane);
+                y = mma<4>(sA + 16 * w * LC + 16 * w, 1, LC, tKr + 16 * w * LB, LB, 1, y, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float fr = fast_exp(Gr[e] - gend), fc = fast_exp(gprev - Gr[e]);
+                    rq[e] += fr * xm[e];
+                    rk[e] += fr * xp[e];
+                    ck[e] += fc * y[e];
+                }
+            } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + 4 * lg + e;
-#pragma unroll 2
+#pragma unroll 1
                 for (int i = 0; i < 16; ++i) {
                     const int s2 = 16 * w + i;
                     const float gs = tG[s2 * LB + lr];
@@ -1165,6 +1181,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
                     ck[e] += ec * (sdM[s2 * LC + r] * tQ[s2 * LB + lr] + (s2 > r ? sA[s2 * LC + r] : 0.f) *
                                                                              tK[s2 * LB + lr]);
                 }
+            }
             }
             glast = tG[(C - 1) * LB + lr];
             float colsum = 0.f;

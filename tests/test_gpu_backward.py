@@ -21,13 +21,17 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(),
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 
 
-def _run(dtype, d, chunk, lengths, with_state, with_dsT, head_gate=False, seed=5, H=3):
+def _run(dtype, d, chunk, lengths, with_state, with_dsT, head_gate=False, seed=5, H=3, g_override=None):
     print(f"backward dtype={dtype} d={d} chunk={chunk} lengths={lengths} state={with_state} dsT={with_dsT} "
           f"head_gate={head_gate}", flush=True)
     w = synth.Workload("bwd", seed, H=H, dk=d, dv=d, dtype=dtype, chunk=chunk, s0_std=0.05 if with_state else 0.0)
     cu = synth.cu_seqlens(lengths)
     T, N = int(cu[-1]), len(lengths)
     st, wide = make_inputs(w, T)
+    if g_override is not None:
+        g2 = np.ascontiguousarray(np.broadcast_to(g_override(T, H, d), st[3].shape), dtype=np.float32)
+        st = (st[0], st[1], st[2], g2, st[4])
+        wide = (wide[0], wide[1], wide[2], g2.astype(np.float64), wide[4])
     if head_gate:
         gh = np.ascontiguousarray(st[3][..., 0])
         st = (st[0], st[1], st[2], gh, st[4])
@@ -98,3 +102,13 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(first, second):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("f32", 32, 32)])
+def test_backward_strong_decay(dtype, d, chunk):
+    """Per-channel decay rates from 0.01 to 8 per token: the weak channels take the matrix-core path
+    for pairs inside a 16-token block, the strong ones (16-token decay above e^64) the exact
+    per-pair exponentials; both against the oracle."""
+    def g_of(T, H, dk):
+        return -np.linspace(0.01, 8.0, dk, dtype=np.float32)[None, None, :]
+    _run(dtype, d, chunk, [200, 77], True, True, g_override=g_of)
