@@ -201,7 +201,7 @@ __device__ __forceinline__ floatx4 prefix_rows(const float* g, int ldg, int w, i
 template <int DK, int DV, int C>
 struct FactorsLds {
     static constexpr int LC = C + 1, CT = 32, LT = CT + 1;
-    static constexpr size_t kFloats = 3 * (size_t)C * LC + 3 * (size_t)C * LT + C;
+    static constexpr size_t kFloats = 3 * (size_t)C * LC + 3 * (size_t)C * LT + C + 4;
     static constexpr size_t kBytes = kFloats * sizeof(float);
 };
 
@@ -220,6 +220,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
     float* tQ = tK + C * LT;    // [C][LT]  q, then beta V
     float* tG = tQ + C * LT;    // [C][LT]  g, then G
     float* sB = tG + C * LT;    // [C]
+    int* sFlag = reinterpret_cast<int*>(sB + C);  // a block of the current tile decays by more than e^64
 
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int64_t slot = blockIdx.x;
@@ -289,8 +290,35 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         dr[m] = 16 * blk + rr;
         ds[m] = 16 * blk + t;
     }
+    // pairs inside block w, on the matrix cores as the pairs across blocks but split at the block's
+    // own last row: the row factor exp(G_r - G_m) is then >= 1, bounded by exp(D) with D the block's
+    // 16-token decay.  A tile where D > 64 for some block and channel takes the exact per-pair
+    // exponentials instead (vector ALUs, pairs spread over the workgroup).
+    floatx4 accPd = zero4(), accMd = zero4();
+    bool any_exact = false;
+    if (tid == 0) *sFlag = 0;
     for (int c0 = 0; c0 < DK; c0 += CT) {
         stage_tile(c0);
+        if (tid < NR * CT) {
+            const int b = tid / CT, cc = tid % CT;
+            const float D = (b > 0 ? tG[(16 * b - 1) * LT + cc] : 0.f) - tG[(16 * b + 15) * LT + cc];
+            if (D > 64.f) *sFlag = 1;  // benign race: every writer stores 1
+        }
+        lds_barrier();
+        const bool exact = *sFlag != 0;
+        any_exact |= exact;
+        if (!exact && w < NR) {
+            const int ra = 16 * w + lr, mj = 16 * w + 15;
+#pragma unroll 4
+            for (int ks = 0; ks < CT / 4; ++ks) {
+                const int cc = 4 * ks + lg;
+                const float gm = tG[mj * LT + cc];
+                const float ea = fast_exp(tG[ra * LT + cc] - gm);
+                const float bb = tK[ra * LT + cc] * fast_exp(gm - tG[ra * LT + cc]);
+                accPd = __builtin_amdgcn_mfma_f32_16x16x4f32(tK[ra * LT + cc] * ea, bb, accPd, 0, 0, 0);
+                accMd = __builtin_amdgcn_mfma_f32_16x16x4f32(tQ[ra * LT + cc] * ea, bb, accMd, 0, 0, 0);
+            }
+        }
 #pragma unroll
         for (int m = 0; m < PPW; ++m) {
             if (w + 4 * m < NPAIR) {
@@ -308,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         }
 #pragma unroll
         for (int m = 0; m < DPT; ++m) {
-            if (tid + kThreads * m < NDIAG) {
+            if (exact && tid + kThreads * m < NDIAG) {
                 const float* kr = tK + dr[m] * LT;
                 const float* qr = tQ + dr[m] * LT;
                 const float* gr = tG + dr[m] * LT;
@@ -323,6 +351,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             }
         }
         lds_barrier();  // the tile is restaged next
+        if (tid == 0) *sFlag = 0;
     }
     // P, M into LDS: zero above the blocks' diagonal, then the two kinds of pairs
     for (int e = tid; e < C * C; e += kThreads) {
@@ -335,12 +364,22 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             sM[r * LC + s2] = 0.f;
         }
     }
+    if (w < NR)
 #pragma unroll
-    for (int m = 0; m < DPT; ++m)
-        if (tid + kThreads * m < NDIAG) {
-            sP[dr[m] * LC + ds[m]] = ds[m] < dr[m] ? dp[m] : 0.f;
-            sM[dr[m] * LC + ds[m]] = dm[m];
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * w + 4 * lg + e, s2 = 16 * w + lr;
+            sP[r * LC + s2] = s2 < r ? accPd[e] : 0.f;
+            sM[r * LC + s2] = s2 <= r ? accMd[e] : 0.f;
         }
+    if (any_exact) {  // uniform: every thread read the same flags
+        lds_barrier();
+#pragma unroll
+        for (int m = 0; m < DPT; ++m)
+            if (tid + kThreads * m < NDIAG) {
+                sP[dr[m] * LC + ds[m]] += ds[m] < dr[m] ? dp[m] : 0.f;
+                sM[dr[m] * LC + ds[m]] += dm[m];
+            }
+    }
 #pragma unroll
     for (int m = 0; m < PPW; ++m)
         if (w + 4 * m < NPAIR)
