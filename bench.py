@@ -60,7 +60,7 @@ _MFMA_SHA = "073509a341f83dcb2bc156c5079270578a9c9eca013c0bdef30ca97e79c440bb"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
 _DECODE_SHA = "2994ede3f200b6caf1eb3a50f86a9e66dce4f573b9f983c576d7d490a90a2b4d"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
-_BWD_SHA = "b7b192fa82c941f9633a5c4e12404792480455cd0c0564ccf09d0bee82af58fb"
+_BWD_SHA = "e705678989d53d6458dee4352847a85ab91e4647833a2cb8056fc4cfde1ca763"
 
 
 def _counted(fetch_kib, write_kib):
@@ -77,8 +77,8 @@ MEASURED_TRAFFIC = {
                    "bytes": _counted(267360.0, 528670.0)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
     "kda_backward": {"source": _BWD_SRC, "sha256": _BWD_SHA, "workload": "backward T=65536 H=32",
-                     "bytes": _counted(3459980.0 + 1585003.2 + 2908331.8 + 3795354.0 + 8924190.3,
-                                       5784155.7 + 3226206.7 + 3446224.5 + 3686734.1 + 4399252.3)},
+                     "bytes": _counted(3469931.2 + 1600676.5 + 2776968.0 + 3793498.4 + 9373238.4,
+                                       7881154.8 + 3319811.7 + 3470525.9 + 3686796.7 + 4492731.2)},
 }
 
 
