@@ -235,15 +235,45 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
     float* rec = a.ws + (slot * H + h) * R::kFloats;
     if (tid < C) sB[tid] = tid < L ? ld_in<TI>(beta, (t0 + tid) * H + h) : 0.f;
 
-    // stage channel tile c0 .. c0 + CT - 1 (k, q, g; rows >= L are zero), then G = tril(ones) g
-    auto stage_tile = [&](int c0) {
-        for (int e = tid; e < C * CT; e += kThreads) {
-            const int r = e / CT, cc = e % CT;
-            const bool in = r < L;
+    // Channel tiles c0 .. c0 + CT - 1 of k, q and g (rows >= L are zero) and value tiles of v go
+    // through registers one tile ahead of their use: the tile sequence is the channel tiles of
+    // pass 1, the same tiles again for pass 2, then the value tiles of pass 3.  Element m of a
+    // thread is row (tid + kThreads m) / CT, column (tid + kThreads m) % CT.
+    constexpr int EPT = (C * CT + kThreads - 1) / kThreads, NCTILE = DK / CT;
+    struct TileRegs {
+        float k[EPT], q[EPT], g[EPT];
+    } tr;
+    constexpr int VPT = (C * VT + kThreads - 1) / kThreads;
+    float vr[VPT];
+    auto fetch_tile = [&](int c0) {
+#pragma unroll
+        for (int m = 0; m < EPT; ++m) {
+            const int e = tid + kThreads * m, r = e / CT, cc = e % CT;
+            const bool in = (EPT * kThreads == C * CT || e < C * CT) && r < L;
             const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + c0 + cc;
-            tK[r * LT + cc] = in ? ld_in<TI>(k, idx) : 0.f;
-            tQ[r * LT + cc] = in ? ld_in<TI>(q, idx) : 0.f;
-            tG[r * LT + cc] = in ? gate_at(a.g, a.gate_head, t0 + r, H, h, DK, c0 + cc) : 0.f;
+            tr.k[m] = in ? ld_in<TI>(k, idx) : 0.f;
+            tr.q[m] = in ? ld_in<TI>(q, idx) : 0.f;
+            tr.g[m] = in ? gate_at(a.g, a.gate_head, t0 + r, H, h, DK, c0 + cc) : 0.f;
+        }
+    };
+    auto fetch_value = [&](int j0) {
+#pragma unroll
+        for (int m = 0; m < VPT; ++m) {
+            const int e = tid + kThreads * m, r = e / VT, j = e % VT;
+            const bool in = (VPT * kThreads == C * VT || e < C * VT) && r < L;
+            vr[m] = in ? ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
+        }
+    };
+    // registers -> tK, tQ, tG (raw g), then G = tril(ones) g into tG
+    auto put_tile = [&]() {
+#pragma unroll
+        for (int m = 0; m < EPT; ++m) {
+            const int e = tid + kThreads * m, r = e / CT, cc = e % CT;
+            if (EPT * kThreads == C * CT || e < C * CT) {
+                tK[r * LT + cc] = tr.k[m];
+                tQ[r * LT + cc] = tr.q[m];
+                tG[r * LT + cc] = tr.g[m];
+            }
         }
         lds_barrier();
         constexpr int NCT = CT / 16;
@@ -263,6 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         }
         lds_barrier();
     };
+    fetch_tile(0);
 
     // ---- pass 1: P and M
     constexpr int NPAIR = NR * (NR - 1) / 2, PPW = (NPAIR + 3) / 4;  // off-diagonal block pairs
@@ -297,8 +328,10 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
     floatx4 accPd = zero4(), accMd = zero4();
     bool any_exact = false;
     if (tid == 0) *sFlag = 0;
-    for (int c0 = 0; c0 < DK; c0 += CT) {
-        stage_tile(c0);
+#pragma unroll
+    for (int ti = 0; ti < NCTILE; ++ti) {
+        put_tile();
+        fetch_tile(ti + 1 < NCTILE ? (ti + 1) * CT : 0);  // the last one is pass 2's first tile
         if (tid < NR * CT) {
             const int b = tid / CT, cc = tid % CT;
             const float D = (b > 0 ? tG[(16 * b - 1) * LT + cc] : 0.f) - tG[(16 * b + 15) * LT + cc];
@@ -443,8 +476,14 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
     for (int e = tid; e < C * C; e += kThreads) rec[R::T + e] = sT[(e / C) * LC + e % C];
 
     // ---- pass 2: Q+^T, K', K'^T, gamma and W = T (beta K+), channel tile by channel tile
-    for (int c0 = 0; c0 < DK; c0 += CT) {
-        stage_tile(c0);
+#pragma unroll
+    for (int ti = 0; ti < NCTILE; ++ti) {
+        const int c0 = ti * CT;
+        put_tile();
+        if (ti + 1 < NCTILE)
+            fetch_tile((ti + 1) * CT);
+        else
+            fetch_value(0);
         for (int e = tid; e < C * CT; e += kThreads) {  // channel-major outputs (token index fastest)
             const int cc = e / C, r = e % C;
             const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc];
@@ -471,11 +510,14 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         lds_barrier();
     }
     // ---- pass 3: U = T (beta V), value tile by value tile (beta V staged in q's buffer)
+#pragma unroll
     for (int j0 = 0; j0 < DV; j0 += VT) {
-        for (int e = tid; e < C * VT; e += kThreads) {
-            const int r = e / VT, j = e % VT;
-            tQ[r * LT + j] = r < L ? sB[r] * ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
+#pragma unroll
+        for (int m = 0; m < VPT; ++m) {
+            const int e = tid + kThreads * m, r = e / VT, j = e % VT;
+            if (VPT * kThreads == C * VT || e < C * VT) tQ[r * LT + j] = sB[r] * vr[m];
         }
+        fetch_value(j0 + VT < DV ? j0 + VT : j0);
         lds_barrier();
         for (int t = w; t < NR * (VT / 16); t += 4) {
             const int rb = t % NR, cb = t / NR;
