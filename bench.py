@@ -60,7 +60,7 @@ _MFMA_SHA = "073509a341f83dcb2bc156c5079270578a9c9eca013c0bdef30ca97e79c440bb"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
 _DECODE_SHA = "2994ede3f200b6caf1eb3a50f86a9e66dce4f573b9f983c576d7d490a90a2b4d"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
-_BWD_SHA = "18b4d73114a8c9e732bdf606411be8ff8e66ffef18c8a84766f050e786ae5b0c"
+_BWD_SHA = "14f6690038584df786cb954ead7ffa654108c4499cccaa27c71aaefa09dd4a81"
 
 
 def _counted(fetch_kib, write_kib):
@@ -77,8 +77,8 @@ MEASURED_TRAFFIC = {
                    "bytes": _counted(267360.0, 528670.0)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
     "kda_backward": {"source": _BWD_SRC, "sha256": _BWD_SHA, "workload": "backward T=65536 H=32",
-                     "bytes": _counted(3546043.7 + 1603160.8 + 2790300.6 + 3792872.2 + 9351581.7,
-                                       7883065.9 + 3343743.4 + 3470574.5 + 3686838.3 + 4531341.8)},
+                     "bytes": _counted(3553838.0 + 1604452.3 + 2780012.4 + 3788357.1 + 9377751.2,
+                                       7883223.0 + 3381520.5 + 3470729.5 + 3686914.2 + 4522764.3)},
 }
 
 

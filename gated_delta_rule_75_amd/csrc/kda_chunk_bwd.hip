@@ -27,7 +27,11 @@
 //   grad_chunk  (chunk, head)          dq, dk, dv, dg, dbeta
 // The two chains are sequential over chunks and split by 16 value columns (columns of S and dS
 // never interact); the three per-chunk kernels are fully parallel.  Every product is a 16x16
-// tile on the fp32 matrix cores (v_mfma_f32_16x16x4f32).
+// tile on the fp32 matrix cores (v_mfma_f32_16x16x4f32), the pairwise products P, M and their
+// gradients included: the decay exp(G_r - G_s) of a pair is split at a 16-row block boundary m,
+// exp(G_r - G_m) exp(G_m - G_s), and the two factors scale the two operands.  Across blocks both
+// exponents are <= 0.  Inside a block one factor can exceed 1; where a block's 16-token decay
+// exceeds e^64 those pairs take their own exponentials on the vector ALUs instead.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -90,24 +94,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // gfx9 encoding: vmcnt/expcnt at max, lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// mma with the k-steps alternating between two accumulators: half the dependent chain, for the
-// latency-bound sequential kernels (KS even)
-template <int KS>
-__device__ __forceinline__ floatx4 mma2(const float* A, int ar, int ak, const float* B, int bk, int bc, floatx4 acc,
-                                        int lane) {
-    static_assert(KS % 2 == 0, "even number of k-steps");
-    const int r = lane & 15, kq = lane >> 4;
-    const float* pa = A + r * ar + kq * ak;
-    const float* pb = B + kq * bk + r * bc;
-    floatx4 acc1 = zero4();
-#pragma unroll 4
-    for (int ks = 0; ks < KS; ks += 2) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * ks * ak], pb[4 * ks * bk], acc, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * (ks + 1) * ak], pb[4 * (ks + 1) * bk], acc1, 0, 0, 0);
-    }
-    return acc + acc1;
 }
 
 // sum over the 16 lanes that share (lane >> 4)
