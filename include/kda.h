@@ -210,9 +210,11 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const float*
  * only options->gate is honoured, and snapshot_every and prologue must be 0
  * (KDA_ERR_UNSUPPORTED otherwise).  workspace: at least
  * kda_workspace_size(KDA_OP_BACKWARD, N, T_total, H, d_k, d_v, dtype, chunk)
- * bytes, 256-byte aligned; it holds the per-chunk factors, the states entering
- * each chunk and the state gradients leaving it.  Asynchronous on hip_stream;
- * errors as for the other calls.
+ * bytes, 256-byte aligned, overlapping no argument; it holds the per-chunk
+ * factors, the states entering each chunk and the state gradients leaving it.
+ * The gradient outputs must not overlap one another either (KDA_ERR_ALIAS).
+ * Repeated calls on the same inputs give bitwise equal results (no atomics).
+ * Asynchronous on hip_stream; errors as for the other calls.
  */
 int kda_chunked_backward(const void* q, const void* k, const void* v, const float* g, const void* beta,
                          const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in,
