@@ -29,8 +29,8 @@
 //   exp(G_r - G_s) = exp(G_r - P_i) * exp(P_i - P_{j+1}) * exp(P_{j+1} - G_s)
 // (P_i = G at the end of block i-1), every factor <= 1.  Inside a diagonal block the
 // reference is the block's 8th token; those factors are bounded by the decay of at
-// most 8 tokens, which must stay below e^10 for fp16 (checked per chunk; a chunk that
-// violates it poisons its outputs with NaN rather than returning wrong numbers).
+// most 8 tokens.  Where that decay exceeds e^10 for some channel (beyond fp16), the
+// chunk's diagonal tiles are summed exactly in fp32 with per-pair exponentials instead.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -140,7 +140,7 @@ struct PrepLds {
         float X[4][16][17];        // per-wave scratch of the inverse
         _Float16 bkT[DK][C + 8];   // Diag(beta) K+ as [channel][token]: B operand of W
     } u;
-    int unsafe;
+    int exact_diag;  // some channel's 8-token decay is beyond the fp16 factors
 };
 
 __device__ __forceinline__ float dpp_row_shr(float x, int d) {
@@ -159,19 +159,28 @@ __device__ __forceinline__ float* t_block(PrepLds& L, int i, int j) {
     return i == j ? &L.AT[16 * i][16 * i] : &L.AT[16 * j][16 * i];
 }
 
+// bfloat16 element i (0..7) of a packed 8-element row fragment
+__device__ __forceinline__ uint32_t bf_elem(const uint4& v, int i) {
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    return (i & 1) ? (wv[i >> 1] >> 16) : (wv[i >> 1] & 0xFFFF);
+}
+
 // PRO: fused input prologue (raw q, k, beta logits, raw gate inputs); a template parameter so
 // that the plain kernel carries none of its code.
-template <bool PRO>
-__global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) {
-    __shared__ PrepLds L;
+// EXACT: the second pass, which redoes the chunks that the first pass flagged (one word per
+// slot and head in `exact_flags`) with exact diagonal Gram tiles.  The first pass writes every
+// flag and leaves the records of flagged chunks to the second.
+// One (slot, head) unit; the whole workgroup calls it with the same arguments.
+template <bool PRO, bool EXACT>
+__device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm, int64_t slot, int h,
+                                          int32_t* exact_flags, PrepLds& L) {
     // wave index, wave-uniform (readfirstlane lets the compiler keep it in a scalar register)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int H = a.H;
-    const int h = blockIdx.y;
-    const int64_t slot = blockIdx.x;
     int64_t n, c;
     if (!sm.locate(slot, n, c)) return;  // uniform over the workgroup
+    int32_t* flag = exact_flags + slot * H + h;
     int64_t bos, eos;
     sm.bounds(n, bos, eos);
     const int64_t t0 = bos + c * C;
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
     const uint16_t* k = static_cast<const uint16_t*>(a.k);
     const uint16_t* beta = static_cast<const uint16_t*>(a.beta);
 
-    if (threadIdx.x == 0) L.unsafe = 0;
+    if (threadIdx.x == 0) L.exact_diag = 0;
 
     // ---- this lane: token r = 16w + lr, channels 32*ks + 8*lg + i (the matrix-core operand
     //      layout); rows past the chunk end load a clamped row and are zeroed
@@ -261,15 +270,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
             L.emr[b][ch] = fast_exp(-gm);
             L.emc[b][ch] = fast_exp(gm - Db[b]);
             // diagonal-block factors are bounded by exp(-gm) (rows) and exp(gm - D_b) (columns);
-            // both must stay below e^10 to fit fp16
+            // beyond e^10 they leave the fp16 range, and the chunk is redone by the second pass
             bad |= (-gm > 10.f) || (gm - Db[b] > 10.f);
         }
         L.Z[0][ch] = fast_exp(d1);
         L.Z[1][ch] = fast_exp(d2);
         L.Z[2][ch] = fast_exp(d1 + d2);
-        if (bad) L.unsafe = 1;  // benign race: every writer stores 1
+        if (bad) L.exact_diag = 1;  // benign race: every writer stores 1
     }
     __syncthreads();
+    if (!EXACT && threadIdx.x == 0) *flag = L.exact_diag;
 
     // ---- operand tiles for this lane's token and 32 channels
     // beta of this lane's token (0 past the chunk end) for Diag(beta) K+
@@ -298,6 +308,51 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
         sq += __shfl_xor(sq, 32, 64);
         inv_k = sk > 0.f ? rsqrtf(sk) : 0.f;
         inv_q = sq > 0.f ? rsqrtf(sq) : 0.f;
+    }
+    // Second pass: some channel decays so fast over 8 tokens that the half-block factors of the
+    // diagonal Gram tile (w, w) would leave the fp16 range, so that tile takes its exact fp32
+    // sums instead, sum_c k_rc k_sc exp(G_rc - G_sc) (q_rc in place of k_rc for M) with
+    // G_rc - G_sc <= 0.  The lanes of row r sum their 8 channels of each k-step for every column
+    // s of the block (row s sits in lane s of the same 16-lane row), add their partial sums, and
+    // keep their own four columns.
+    if (EXACT) {
+        float accA[4] = {0.f, 0.f, 0.f, 0.f}, accM[4] = {0.f, 0.f, 0.f, 0.f};  // columns 4*lg + j
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float kk[8], qq[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                kk[i] = valid ? bf(bf_elem(kv[ks], i)) * inv_k : 0.f;
+                qq[i] = valid ? bf(bf_elem(qv[ks], i)) * inv_q : 0.f;
+            }
+#pragma unroll 1
+            for (int s2 = 0; s2 < 16; ++s2) {
+                float pa = 0.f, pm = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float ksv = __shfl(kk[i], 16 * lg + s2, 64), gs = __shfl(gl[ks][i], 16 * lg + s2, 64);
+                    const float e = fast_exp(fminf(gl[ks][i] - gs, 0.f)) * ksv;
+                    pa += kk[i] * e;
+                    pm += qq[i] * e;
+                }
+                pa += __shfl_xor(pa, 16, 64);
+                pa += __shfl_xor(pa, 32, 64);
+                pm += __shfl_xor(pm, 16, 64);
+                pm += __shfl_xor(pm, 32, 64);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool mine = s2 == 4 * lg + j;
+                    accA[j] += mine ? pa : 0.f;
+                    accM[j] += mine ? pm : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s2 = 4 * lg + j;
+            L.AT[r][16 * w + s2] = (s2 < lr) ? brow_r * accA[j] : 0.f;
+            L.M[r][16 * w + s2] = (_Float16)((s2 <= lr) ? accM[j] : 0.f);
+        }
     }
     half8 KR[4], QR[4], BKp[4];
     floatx4 diagA = {0.f, 0.f, 0.f, 0.f}, diagM = {0.f, 0.f, 0.f, 0.f};  // tile (w, w)
@@ -329,8 +384,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
         }
         // diagonal Gram tile (w, w): this lane's operands are both the row and the column
         // fragments, so it accumulates k-step by k-step with nothing exchanged
-        diagA = mfma16x16x32(krd, kcd, diagA);
-        diagM = mfma16x16x32(qrd, kcd, diagM);
+        if (!EXACT) {
+            diagA = mfma16x16x32(krd, kcd, diagA);
+            diagM = mfma16x16x32(qrd, kcd, diagM);
+        }
         BKp[ks] = kp;  // Diag(beta) K+, consumed by W after T is known
         *reinterpret_cast<half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16) = qp;
         if (w < 3) *reinterpret_cast<half8*>(&L.u.kc[w][ks][lane][0]) = kc;
@@ -349,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
         const float bv = bf(beta[(t0 + (rr < Lc ? rr : Lc - 1)) * H + h]);
         brow[i] = rr < Lc ? (PRO ? sigmoid(bv) : bv) : 0.f;
     }
-    {
+    if (!EXACT) {  // the second pass has its exact tile in place already
         const floatx4 accA = diagA, accM = diagM;
         // accumulator: column s = lr of block j, rows 4*lg + i of block w
 #pragma unroll
@@ -358,10 +415,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
             L.AT[rr][ss] = (ss < rr) ? brow[i] * accA[i] : 0.f;
             L.M[rr][ss] = (_Float16)((ss <= rr) ? accM[i] : 0.f);
         }
-        for (int j = w + 1; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) L.M[16 * w + 4 * lg + i][16 * j + lr] = (_Float16)0.f;
     }
+    for (int j = w + 1; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.M[16 * w + 4 * lg + i][16 * j + lr] = (_Float16)0.f;
     __syncthreads();
     for (int j = 0; j < w; ++j) {
         floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
@@ -477,9 +534,35 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm) 
 
     if (w == 0) {
         float* gam = reinterpret_cast<float*>(rec + kOffGamma);
-        const float poison = L.unsafe ? __builtin_nanf("") : 0.f;
         for (int ch = lane; ch < DK; ch += 64)
-            gam[ch] = fast_exp(L.tot[0][ch] + L.tot[1][ch] + L.tot[2][ch] + L.tot[3][ch]) + poison;
+            gam[ch] = fast_exp(L.tot[0][ch] + L.tot[1][ch] + L.tot[2][ch] + L.tot[3][ch]);
+    }
+}
+
+// First pass: one workgroup (4 waves) per (slot, head).
+template <bool PRO>
+__global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm, int32_t* exact_flags) {
+    __shared__ PrepLds L;
+    prep_unit<PRO, false>(a, sm, blockIdx.x, blockIdx.y, exact_flags, L);
+}
+
+// Second pass: workgroup b reads the flags of units 64b .. 64b + 63 (unit = slot * H + head) and
+// redoes the flagged ones in turn.  A flag of a slot that no chunk uses is never written and
+// may hold anything; such a unit returns at once.
+template <bool PRO>
+__global__ __launch_bounds__(256, 2) void prep_exact_kernel(PrefillArgs a, SeqMap sm, int32_t* exact_flags,
+                                                            int64_t units) {
+    __shared__ PrepLds L;
+    const int64_t u0 = (int64_t)blockIdx.x * 64;
+    const int64_t u = u0 + (threadIdx.x & 63);
+    const bool set = u < units && exact_flags[u] != 0;
+    uint64_t todo = __ballot(set);  // the same mask in every wave
+    while (todo) {
+        const int bit = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int64_t unit = u0 + bit;
+        prep_unit<PRO, true>(a, sm, unit / a.H, (int)(unit % a.H), exact_flags, L);
+        __syncthreads();  // the next unit rewrites the LDS this one still reads at its end
     }
 }
 
@@ -871,7 +954,9 @@ bool chunk_mfma_supported(int bf16, int dk, int dv, int chunk) {
 
 size_t chunk_mfma_workspace(int64_t N, int64_t T_fixed, int64_t T_total, bool fixed, int H, int chunk) {
     (void)chunk;
-    return (size_t)num_slots(N, T_fixed, T_total, fixed) * (size_t)H * (size_t)kRecord;
+    const size_t units = (size_t)num_slots(N, T_fixed, T_total, fixed) * (size_t)H;
+    // the records, then one flag word per record (rounded up to 256 bytes)
+    return units * (size_t)kRecord + ((units * sizeof(int32_t) + 255) / 256) * 256;
 }
 
 hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
@@ -880,11 +965,20 @@ hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
     const int64_t slots = num_slots(a.N, a.T_fixed, a.T_total, a.cu == nullptr);
     const bool timed = timing_on();
     if (slots > 0 && a.T_total > 0) {
+        int32_t* flags = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) +
+                                                    slots * (int64_t)a.H * kRecord);
+        const dim3 grid((unsigned)slots, (unsigned)a.H);
+        const int64_t units = slots * (int64_t)a.H;
+        const dim3 grid2((unsigned)((units + 63) / 64));
         if (timed) timed_begin(kKernelPrep, s);
-        if (a.prologue)
-            hipLaunchKernelGGL(prep_kernel<true>, dim3((unsigned)slots, (unsigned)a.H), dim3(256), 0, s, a, sm);
-        else
-            hipLaunchKernelGGL(prep_kernel<false>, dim3((unsigned)slots, (unsigned)a.H), dim3(256), 0, s, a, sm);
+        // first pass over every chunk, then the chunks it flagged for exact diagonal tiles
+        if (a.prologue) {
+            hipLaunchKernelGGL(prep_kernel<true>, grid, dim3(256), 0, s, a, sm, flags);
+            hipLaunchKernelGGL(prep_exact_kernel<true>, grid2, dim3(256), 0, s, a, sm, flags, units);
+        } else {
+            hipLaunchKernelGGL(prep_kernel<false>, grid, dim3(256), 0, s, a, sm, flags);
+            hipLaunchKernelGGL(prep_exact_kernel<false>, grid2, dim3(256), 0, s, a, sm, flags, units);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (timed) timed_end(s);

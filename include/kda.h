@@ -38,9 +38,11 @@
  *   - bfloat16 path numerics: products inside a chunk use fp16 matrix-core
  *     operands with fp32 accumulation; the state, the decays and all outputs are
  *     fp32.  Values of v, of the state and of the intermediate corrections must
- *     stay within fp16 range (|x| < 6e4); within every 8-token window the
- *     per-channel decay must satisfy sum(-g) <= 10 (alpha >= ~0.29 on average).
- *     The fp32 path has no such limits.
+ *     stay within fp16 range (|x| < 6e4).  Decays of any strength are exact up
+ *     to rounding: a chunk in which some channel decays by more than e^10 over 8
+ *     tokens sums its diagonal 16x16 Gram tiles in fp32 with one exponential per
+ *     token pair, which costs that chunk extra time.  The fp32 path has no such
+ *     limits.
  */
 #ifndef KDA_H_
 #define KDA_H_

@@ -203,17 +203,53 @@ def test_prefill_equals_append_and_decode_composition():
     assert_close(dec, host(o)[0, :40], 2e-3, None, "prefill vs decode")
 
 
-def test_strong_decay_is_flagged_not_wrong():
-    """Per-channel decays beyond the fp16 range of the matrix-core path (8-token decay > e^10)
-    must not produce silently wrong numbers: outputs of such chunks are NaN."""
-    w = _w("bf16", H=1, seed=51)
-    T = 64
-    st, _ = make_inputs(w, T)
-    q, k, v, g, b = upload(w, st, (1, T))
-    g = torch.full_like(g, -3.0)
-    o, s = kda.prefill_chunked(q, k, v, g, b)
+@pytest.mark.parametrize("gate,head_gate", [
+    (synth.Gate("softplus", scale=4.0), False),     # every chunk decays by e^-25 or more over 8 tokens
+    (synth.Gate("rate", lo=0.001, hi=8.0), False),  # per-channel rates from weak to very strong
+    (synth.Gate("softplus", scale=4.0), True),      # one strong log-decay per token and head
+])
+def test_strong_decay_matches_oracle(gate, head_gate):
+    """Decays beyond the fp16 range of the half-block decay factors (an 8-token decay above e^10 on
+    some channel): the matrix-core path sums those chunks' diagonal Gram tiles exactly in fp32,
+    and outputs and states match the oracle."""
+    print(f"strong decay gate={gate} head_gate={head_gate}", flush=True)
+    w = _w("bf16", H=3, seed=51, s0_std=0.02, gate=gate)
+    B, T = 2, 333
+    st, wide = make_inputs(w, B * T)
+    if head_gate:
+        st, wide = _head_gate(st, wide)
+    assert np.max(-np.asarray(st[3], np.float64)) > 10.0 / 8  # some token needs the exact tiles
+    s0 = synth.gen_state(w, B)
+    q, k, v, g, b = upload(w, st, (B, T))
+    o, sT = kda.prefill_chunked(q, k, v, g, b, dev(s0, "f32"))
     torch.cuda.synchronize()
-    assert torch.isnan(s).all()
+    cu = np.arange(B + 1) * T
+    oref, sref = oracle.recurrence(*wide, cu, s0)
+    assert_close(host(o).reshape(B * T, w.H, w.dv), oref, TOL["bf16"], cu, "o")
+    assert_close(host(sT), sref, TOL["bf16"], None, "S_T")
+
+
+def test_strong_and_weak_decay_segments_in_one_call():
+    """Packed segments, one of them decaying 40 times faster: the strong chunks take the exact
+    diagonal tiles, the weak ones the matrix-core tiles, in the same launch."""
+    w = _w("bf16", H=3, seed=53, s0_std=0.02)
+    lengths = [200, 130, 64, 77]
+    cu = synth.cu_seqlens(lengths)
+    T, N = int(cu[-1]), len(lengths)
+    print(f"strong and weak segments lengths={lengths}", flush=True)
+    st, wide = make_inputs(w, T)
+    g = st[3].copy()
+    g[cu[1]:cu[2]] *= 40.0
+    g[cu[3]:cu[4]] *= 40.0
+    st = (st[0], st[1], st[2], g, st[4])
+    wide = (wide[0], wide[1], wide[2], g.astype(np.float64), wide[4])
+    s0 = synth.gen_state(w, N)
+    q, k, v, gd, b = upload(w, st)
+    o, sT = kda.append_prefill(q, k, v, gd, b, torch.from_numpy(cu).cuda(), dev(s0, "f32"))
+    torch.cuda.synchronize()
+    oref, sref = oracle.recurrence(*wide, cu, s0)
+    assert_close(host(o), oref, TOL["bf16"], cu, "o")
+    assert_close(host(sT), sref, TOL["bf16"], None, "S_T")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -287,12 +323,14 @@ def test_snapshots_match_oracle(dtype, d, chunk, every):
 # ---------------------------------------------------------------------------------------------
 # Fused input prologue: raw q, k (normalised in the kernels), beta logits, raw gate inputs
 # ---------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,d,chunk,gate_head", [("bf16", 128, 64, False), ("bf16", 128, 64, True),
-                                                      ("f32", 32, 32, False), ("f32", 16, 16, True)])
-def test_fused_prologue_matches_oracle(dtype, d, chunk, gate_head):
-    print(f"prologue dtype={dtype} d={d} chunk={chunk} gate_head={gate_head}", flush=True)
+@pytest.mark.parametrize("dtype,d,chunk,gate_head,scale", [
+    ("bf16", 128, 64, False, 0.1), ("bf16", 128, 64, True, 0.1), ("f32", 32, 32, False, 0.1),
+    ("f32", 16, 16, True, 0.1),
+    ("bf16", 128, 64, False, 4.0),  # strong decays: the exact diagonal tiles, from raw gate inputs
+])
+def test_fused_prologue_matches_oracle(dtype, d, chunk, gate_head, scale):
+    print(f"prologue dtype={dtype} d={d} chunk={chunk} gate_head={gate_head} scale={scale}", flush=True)
     w = _w(dtype, H=3, d=d, chunk=chunk, seed=43, s0_std=0.02)
-    scale = 0.1
     B, T = 2, 333
     q, k, v, a, b = synth.gen_raw_tokens(w, B * T + B, gate_head=gate_head)
     s0 = synth.gen_state(w, B)
