@@ -539,11 +539,13 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
     }
 }
 
-// First pass: one workgroup (4 waves) per (slot, head).
+// First pass: one workgroup (4 waves) per (slot, head), heads fastest: workgroups that run at
+// the same time read neighbouring token rows and write neighbouring records.
 template <bool PRO>
 __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm, int32_t* exact_flags) {
     __shared__ PrepLds L;
-    prep_unit<PRO, false>(a, sm, blockIdx.x, blockIdx.y, exact_flags, L);
+    const int64_t unit = blockIdx.x;
+    prep_unit<PRO, false>(a, sm, unit / a.H, (int)(unit % a.H), exact_flags, L);
 }
 
 // Second pass: workgroup b reads the flags of units 64b .. 64b + 63 (unit = slot * H + head) and
@@ -967,8 +969,8 @@ hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
     if (slots > 0 && a.T_total > 0) {
         int32_t* flags = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) +
                                                     slots * (int64_t)a.H * kRecord);
-        const dim3 grid((unsigned)slots, (unsigned)a.H);
         const int64_t units = slots * (int64_t)a.H;
+        const dim3 grid((unsigned)units);
         const dim3 grid2((unsigned)((units + 63) / 64));
         if (timed) timed_begin(kKernelPrep, s);
         // first pass over every chunk, then the chunks it flagged for exact diagonal tiles
