@@ -965,6 +965,9 @@ hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
     if (a.N * a.H == 0) return hipSuccess;
     const SeqMap sm = make_map(a);
     const int64_t slots = num_slots(a.N, a.T_fixed, a.T_total, a.cu == nullptr);
+    // one-dimensional grids: one prep workgroup per (slot, head), NVB state workgroups per
+    // (sequence, head)
+    if (slots * (int64_t)a.H > INT32_MAX || a.N * (int64_t)a.H * NVB > INT32_MAX) return hipErrorInvalidConfiguration;
     const bool timed = timing_on();
     if (slots > 0 && a.T_total > 0) {
         int32_t* flags = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) +
