@@ -134,6 +134,8 @@ def parse():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=3, help="timed chunked-backward passes")
+    ap.add_argument("--skip-workloads", action="store_true",
+                    help="skip the varlen append and long-context workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (the HBM-counter calibration kernel) and exit")
     return ap.parse_args()
@@ -483,6 +485,148 @@ def bench_decode(args, res):
     log(f"[decode] parity max err {worst:.2e}")
 
 
+def _events_ms(fn, n):
+    """Average ms of n calls of fn, each bracketed by HIP events on the current stream."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in ev) / n
+
+
+def _head_err(x, y):
+    import numpy as np
+
+    return float(np.abs(x - y).max() / max(np.abs(y).max(), 1e-300))
+
+
+def bench_workloads(args, res):
+    """The varlen append workload (8 carried segments of 1K-32K tokens) and the long-context one
+    (a 2^20-token prefill, then 4096 decode steps of the same sequence), each parity-checked on one
+    sampled head against the oracle."""
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_75_amd as kda
+    import oracle
+    import synth
+
+    dev = torch.device("cuda:0")
+    out = {}
+    # ---- varlen append-prefill from carried states
+    w = synth.workload("varlen")
+    cu = synth.cu_seqlens(w.lengths)
+    T, N, H, dk, dv = int(cu[-1]), len(w.lengths), w.H, w.dk, w.dv
+    log(f"[varlen] generating T_total={T} in {N} segments, H={H}")
+    q, k, v, g, b = synth.gen_tokens(w, T)
+    s0 = synth.gen_state(w, N)
+    tq, tk, tv, tb = (upload(x, "bf16", dev) for x in (q, k, v, b))
+    tg, ts0 = upload(g, "f32", dev), upload(s0, "f32", dev)
+    tcu = torch.from_numpy(cu).to(dev)
+    o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    sT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(1, N, T, H, dk, dv, torch.bfloat16, 64), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.append_prefill(tq, tk, tv, tg, tb, tcu, ts0, out=o, state_out=sT, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ms = _events_ms(step, 5)
+    nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * T * H + 2 * N * H * dk * dv * 4
+    h = 5
+    wide = [synth.to_f64(x[:, h:h + 1], "bf16") for x in (q, k, v)] + [g[:, h:h + 1].astype(np.float64),
+                                                                       synth.to_f64(b[:, h:h + 1], "bf16")]
+    t0 = time.perf_counter()
+    oref, sref = oracle.recurrence(*wide, cu, s0[:, h:h + 1], vcols=32)
+    t_or = time.perf_counter() - t0
+    err = max(_head_err(o[:, h:h + 1].cpu().numpy().astype(np.float64), oref),
+              _head_err(sT[:, h:h + 1].cpu().numpy().astype(np.float64), sref))
+    out["varlen_append"] = {
+        "workload": f"append-prefill of {N} segments ({T} tokens, lengths {list(map(int, w.lengths))}) "
+                    f"from carried fp32 states, H={H}, d=128, bf16, chunk 64",
+        "ms_per_pass": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "parity": {"head": h, "all_tokens_and_states": True, "max_rel_err": err, "tol": 2e-3,
+                   "ok": bool(err <= 2e-3), "oracle_s": round(t_or, 1)}}
+    log(f"[varlen] {ms:.3f} ms/pass ({T / (ms * 1e-3) / 1e6:.2f} M tokens/s); parity {err:.2e}")
+    del tq, tk, tv, tb, tg, ts0, o, sT, ws, q, k, v, g, b, wide, oref
+    torch.cuda.empty_cache()
+
+    # ---- long context: 2^20-token prefill, then decode steps from its final state
+    w = synth.workload("long")
+    T, H, steps = w.T, w.H, w.decode_steps
+    log(f"[long] generating T={T} H={H}")
+    q, k, v, g, b = synth.gen_tokens(w, T)
+    tq, tk, tv, tb = (upload(x, "bf16", dev).reshape(1, T, *x.shape[1:]) for x in (q, k, v, b))
+    tg = upload(g, "f32", dev).reshape(1, T, H, dk)
+    o = torch.empty((1, T, H, dv), dtype=torch.float32, device=dev)
+    sT = torch.empty((1, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(0, 1, T, H, dk, dv, torch.bfloat16, 64), dtype=torch.uint8, device=dev)
+
+    def lstep():
+        kda.prefill_chunked(tq, tk, tv, tg, tb, None, out=o, state_out=sT, workspace=ws)
+
+    lstep()
+    torch.cuda.synchronize()
+    ms = _events_ms(lstep, 2)
+    nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * T * H
+    del tq, tk, tv, tb, tg, ws
+    torch.cuda.empty_cache()
+    dq, dk_, dv_, dg, db = synth.gen_tokens(w, steps, offset_tokens=T)
+    sq, sk, sv, sb = (upload(x, "bf16", dev) for x in (dq, dk_, dv_, db))
+    sg = upload(dg, "f32", dev)
+    S = sT.clone()
+    dout = torch.empty((1, H, dv), dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with kda.kernel_timing() as kt:
+        e0.record()
+        for t in range(steps):
+            kda.decode_step(sq[t:t + 1], sk[t:t + 1], sv[t:t + 1], sg[t:t + 1], sb[t:t + 1], S, out=dout)
+        e1.record()
+        torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1)
+    kus = [m * 1e3 for n, m in kt.records if n == "kda_decode"]
+    h = 11
+    log(f"[long] oracle on head {h}")
+    wide = [synth.to_f64(x[:, h:h + 1], "bf16") for x in (q, k, v)] + [g[:, h:h + 1].astype(np.float64),
+                                                                       synth.to_f64(b[:, h:h + 1], "bf16")]
+    t0 = time.perf_counter()
+    oref, sref = oracle.recurrence(*wide, vcols=8)
+    dwide = [synth.to_f64(x[:, h:h + 1], "bf16") for x in (dq, dk_, dv_)] + [
+        dg[:, h:h + 1].astype(np.float64), synth.to_f64(db[:, h:h + 1], "bf16")]
+    doref, dsref = oracle.recurrence(*dwide, None, sref, vcols=8)
+    t_or = time.perf_counter() - t0
+    err = max(_head_err(o[0, :, h:h + 1].cpu().numpy().astype(np.float64), oref),
+              _head_err(sT[:, h:h + 1].cpu().numpy().astype(np.float64), sref),
+              _head_err(dout[:, h:h + 1].cpu().numpy().astype(np.float64), doref[-1:]),
+              _head_err(S[:, h:h + 1].cpu().numpy().astype(np.float64), dsref))
+    out["long_context"] = {
+        "workload": f"B=1 prefill of T={T} tokens, H={H}, d=128, bf16, chunk 64, then {steps} decode steps "
+                    f"(B=1) from its final state",
+        "prefill_ms_per_pass": round(ms, 3), "prefill_tokens_per_s": round(T / (ms * 1e-3), 1),
+        "prefill_roofline": {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                             "algorithmic_bytes_per_launch": nbytes},
+        "decode_steps": steps, "decode_us_per_step": round(dms * 1e3 / steps, 2),
+        "decode_steps_per_s": round(steps / (dms * 1e-3), 1),
+        "decode_kernel_avg_us": round(sum(kus) / len(kus), 2),
+        "decode_note": "one sequence: 32 workgroups per step, bound by launch latency, not by HBM; the "
+                       "per-step time includes the host's calls through the Python binding",
+        "parity": {"head": h, "prefill_tokens_checked": T, "decode_steps_checked": steps, "max_rel_err": err,
+                   "tol": 2e-3, "ok": bool(err <= 2e-3), "oracle_s": round(t_or, 1)}}
+    log(f"[long] prefill {ms:.2f} ms ({T / (ms * 1e-3) / 1e6:.2f} M tokens/s), decode {dms * 1e3 / steps:.1f} "
+        f"us/step (kernel {sum(kus) / len(kus):.1f} us); parity {err:.2e}")
+    res["workloads"] = out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -517,6 +661,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.skip_decode:
         bench_decode(args, res)
+    if not args.skip_workloads:
+        torch.cuda.empty_cache()
+        bench_workloads(args, res)
     print(json.dumps(res), flush=True)
 
 
