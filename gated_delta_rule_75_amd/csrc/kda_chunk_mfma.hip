@@ -893,28 +893,20 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
         *reinterpret_cast<half4*>(&L.S[lr][16 * (2 * w + t) + 4 * lg]) = hv;
     }
 
-    // Simple (not unrolled) loop: the copy cur = nxt at the top is the only place that waits on
-    // the operand loads, which were issued a whole chunk earlier; the prefetch of the next chunk
-    // and the previous chunk's output store follow it, so the chunk's compute overlaps both.
-    // (With two register sets alternating in an unrolled loop, the compiler's wait insertion
-    // became conservative at the back-edge and made each chunk wait for its own prefetch.)
-    ChunkFrags nxt;
-    if (nchunks > 0) load_chunk(nxt, rec_of(0), w, lane);
+    // Two chunks per iteration with alternating operand registers: chunk c reads fa and loads
+    // chunk c+1 into fb, chunk c+1 reads fb and loads chunk c+2 into fa, so no registers are
+    // copied.  The explicit wait at the top of each chunk is the only place that waits on the
+    // operand loads, which were issued a whole chunk earlier; the previous chunk's output store
+    // follows it, so the chunk's compute overlaps both.
+    ChunkFrags fa, fb;
+    if (nchunks > 0) load_chunk(fa, rec_of(0), w, lane);
     lds_barrier();
 
     float* obase0 = a.o + (bos * H + h) * (int64_t)DV + vb * BV;
     const int64_t ostep = (int64_t)C * H * DV;
     floatx4 Oprev = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t c = 0; c < nchunks; ++c) {
-        // every load issued during the previous chunk (this chunk's operands) and the previous
-        // output store are complete here; stating it explicitly keeps the compiler's own wait
-        // placement exact inside the chunk (it cannot track loads carried around the loop)
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0), expcnt/lgkmcnt at max
-        const ChunkFrags cur = nxt;
-        if (c > 0) store_o(L, Oprev, obase0 + (c - 1) * ostep, len_of(c - 1), H, w, lane);
-        const bool has_next = c + 1 < nchunks;
-        Oprev = state_chunk(L, cur, nxt, rec_of(has_next ? c + 1 : c), has_next, (int)(c & 1), Sf, w, lane);
-        // state snapshot after every snap_every full chunks
+    // state snapshot after every snap_every full chunks
+    auto snapshot = [&](int64_t c) {
         if (a.snap && (c + 1) % a.snap_every == 0 && len_of(c) == C) {
             const int64_t row = (a.snap_cu ? (int64_t)a.snap_cu[n] : n * a.snap_per_seq) + (c + 1) / a.snap_every - 1;
             float* dst = a.snap + (row * H + h) * (int64_t)DK * DV + vb * BV;
@@ -923,6 +915,22 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * (2 * w + t) + 4 * lg + i) * DV + lr] = Sf[t][i];
         }
+    };
+    for (int64_t c = 0; c < nchunks; c += 2) {
+        // every load issued during the previous chunk (this chunk's operands) and the previous
+        // output store are complete here; stating it explicitly keeps the compiler's own wait
+        // placement exact inside the chunk (it cannot track loads carried around the loop)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0), expcnt/lgkmcnt at max
+        if (c > 0) store_o(L, Oprev, obase0 + (c - 1) * ostep, len_of(c - 1), H, w, lane);
+        const bool has_next = c + 1 < nchunks;
+        Oprev = state_chunk(L, fa, fb, rec_of(has_next ? c + 1 : c), has_next, 0, Sf, w, lane);
+        snapshot(c);
+        if (!has_next) break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        store_o(L, Oprev, obase0 + c * ostep, len_of(c), H, w, lane);
+        const bool has_next2 = c + 2 < nchunks;
+        Oprev = state_chunk(L, fb, fa, rec_of(has_next2 ? c + 2 : c + 1), has_next2, 1, Sf, w, lane);
+        snapshot(c + 1);
     }
     if (nchunks > 0) store_o(L, Oprev, obase0 + (nchunks - 1) * ostep, len_of(nchunks - 1), H, w, lane);
 
