@@ -604,8 +604,10 @@ __device__ __forceinline__ half8 as_half8(u32x4 x) { return __builtin_bit_cast(h
 
 // The operand loads of one chunk in four groups.  Each wave-wide load costs the CU's address
 // unit about as much whatever its width, and a wave stalls at issue when that unit is busy, so
-// the groups are issued at four points spread over the previous chunk's compute rather than
-// back to back.
+// the groups are issued at three points spread over the previous chunk's compute rather than
+// back to back: W before X, Q+ after it, and T, M and K'^T after the first barrier (measured on
+// MI355X; any group moved into the stretch before the first barrier, or interleaved one load per
+// matrix-core step, made the pass slower).
 __device__ __forceinline__ void load_group(ChunkFrags& f, __amdgpu_buffer_rsrc_t rr, int g, int w, int lane) {
     const int lo = lane * 16;
     if (g == 0) {
@@ -759,15 +761,14 @@ __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cu
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) Y = mfma16x16x32(cur.qp[ks], sb[ks], Y);
     __builtin_amdgcn_sched_barrier(0);
-    if (has_next) load_group(nxt, nr, 2, w, lane);
-    __builtin_amdgcn_sched_barrier(0);
     half4 dh;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dh[i] = (_Float16)(U[i] - X[i]);
     *reinterpret_cast<half4*>(&L.D[lr][16 * w + 4 * lg]) = dh;
     lds_barrier();
 
-    if (has_next) load_group(nxt, nr, 3, w, lane);
+    if (has_next) load_group(nxt, nr, 3, w, lane);  // T, M
+    if (has_next) load_group(nxt, nr, 2, w, lane);  // K'^T
     __builtin_amdgcn_sched_barrier(0);
     half8 db[2];
 #pragma unroll
