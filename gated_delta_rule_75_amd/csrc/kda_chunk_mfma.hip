@@ -839,15 +839,16 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
     };
 
     if (w == 4) {
-        // warm-up wave: touch chunks 1..kWarmAhead now, then one chunk per iteration, and take
-        // part in the compute waves' barriers (one before the loop, two per chunk)
+        // warm-up wave: touch chunks 1..kWarmAhead now, then one chunk per iteration between the
+        // two barriers, and take part in the compute waves' barriers (one before the loop, two
+        // per chunk)
         auto* dummy = reinterpret_cast<__attribute__((address_space(3))) void*>(
             reinterpret_cast<uintptr_t>(&L.warm_dummy[0]));
         for (int64_t c = 1; c <= kWarmAhead && c < nchunks; ++c) warm_l2(rec_of(c), vb, lane, dummy);
         lds_barrier();
         for (int64_t c = 0; c < nchunks; ++c) {
-            if (c + 1 + kWarmAhead < nchunks) warm_l2(rec_of(c + 1 + kWarmAhead), vb, lane, dummy);
             lds_barrier();
+            if (c + 1 + kWarmAhead < nchunks) warm_l2(rec_of(c + 1 + kWarmAhead), vb, lane, dummy);
             lds_barrier();
         }
         __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS write may outlive the workgroup
@@ -855,8 +856,8 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
     }
     if (w == 5) {
         // staging wave: chunk c+1's beta*V and gamma go to LDS between the two barriers of
-        // chunk c (from registers loaded one chunk earlier); loads for chunk c+2 are issued
-        // at the start of chunk c
+        // chunk c (from registers loaded one chunk earlier), and chunk c+2's loads are issued
+        // right after, away from the compute waves' operand loads before the first barrier
         StageRegs ra, rb;
         if (nchunks > 0) {
             stage_load(ra, v, beta, rec_of(0), bos, len_of(0), H, h, vb, lane);
@@ -865,14 +866,14 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
         if (nchunks > 1) stage_load(rb, v, beta, rec_of(1), bos + C, len_of(1), H, h, vb, lane);
         lds_barrier();
         for (int64_t c = 0; c < nchunks; c += 2) {
-            if (c + 2 < nchunks) stage_load(ra, v, beta, rec_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h, vb, lane);
             lds_barrier();
             if (c + 1 < nchunks) stage_store(L, 1, rb, lane, a.prologue);
+            if (c + 2 < nchunks) stage_load(ra, v, beta, rec_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h, vb, lane);
             lds_barrier();
             if (c + 1 >= nchunks) break;
-            if (c + 3 < nchunks) stage_load(rb, v, beta, rec_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h, vb, lane);
             lds_barrier();
             if (c + 2 < nchunks) stage_store(L, 0, ra, lane, a.prologue);
+            if (c + 3 < nchunks) stage_load(rb, v, beta, rec_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h, vb, lane);
             lds_barrier();
         }
         return;
