@@ -56,7 +56,7 @@ constexpr int kOffT = 48 * kTile;         // 8 tiles (row block rb, k-step kb): 
 constexpr int kOffM = 56 * kTile;         // 8 tiles
 constexpr int kOffGamma = 64 * kTile;     // 128 floats
 constexpr int kRecord = 64 * kTile + 512; // 66048 bytes (multiple of 256)
-constexpr int kWarmAhead = 6;             // chunks of L2 warm-up ahead of the state pass
+constexpr int kWarmAhead = 2;             // chunks of L2 warm-up ahead of the state pass (1, 2, 4 equal; 3, 6, 12 slower)
 
 __device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
