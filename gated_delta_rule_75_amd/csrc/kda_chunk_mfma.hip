@@ -31,6 +31,8 @@
 // reference is the block's 8th token; those factors are bounded by the decay of at
 // most 8 tokens.  Where that decay exceeds e^10 for some channel (beyond fp16), the
 // chunk's diagonal tiles are summed exactly in fp32 with per-pair exponentials instead.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -685,6 +687,8 @@ struct StageRegs {
     uint32_t g[2];
 };
 
+// Token half J (tokens 32 J .. 32 J + 31) of a chunk's staging; half 0 also takes gamma.
+template <int J>
 __device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* v, const uint16_t* beta,
                                            const unsigned char* rec, int64_t t0, int Lc, int H, int h, int vb,
                                            int lane) {
@@ -692,31 +696,30 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* v, cons
     const __amdgpu_buffer_rsrc_t vrs =
         make_rsrc(v + (t0 * H + h) * (int64_t)DV + vb * BV, (uint32_t)(((Lc - 1) * rowv + BV) * 2));
     const __amdgpu_buffer_rsrc_t brs = make_rsrc(beta + t0 * H + h, (uint32_t)(((Lc - 1) * H + 1) * 2));
-    const __amdgpu_buffer_rsrc_t grs = make_rsrc(rec + kOffGamma, DK * 4);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int tok = 32 * j + (lane >> 1);
-        r.v[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)((tok * rowv + 8 * (lane & 1)) * 2), 0, 0);
-        r.b[j] = __builtin_amdgcn_raw_buffer_load_b16(brs, tok * H * 2, 0, 0);
+    const int tok = 32 * J + (lane >> 1);
+    r.v[J] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)((tok * rowv + 8 * (lane & 1)) * 2), 0, 0);
+    r.b[J] = __builtin_amdgcn_raw_buffer_load_b16(brs, tok * H * 2, 0, 0);
+    if (J == 0) {
+        const __amdgpu_buffer_rsrc_t grs = make_rsrc(rec + kOffGamma, DK * 4);
+        r.g[0] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8, 0, 0);
+        r.g[1] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8 + 4, 0, 0);
     }
-    r.g[0] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8, 0, 0);
-    r.g[1] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8 + 4, 0, 0);
 }
 
+template <int J>
 __device__ __forceinline__ void stage_store(StateLds& L, int buf, const StageRegs& r, int lane, bool beta_logits) {
+    const int tok = 32 * J + (lane >> 1);
+    const float bt = beta_logits ? sigmoid(bf((uint16_t)r.b[J])) : bf((uint16_t)r.b[J]);
+    const uint32_t words[4] = {r.v[J].x, r.v[J].y, r.v[J].z, r.v[J].w};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int tok = 32 * j + (lane >> 1);
-        const float bt = beta_logits ? sigmoid(bf((uint16_t)r.b[j])) : bf((uint16_t)r.b[j]);
-        const uint32_t words[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint16_t bits = (uint16_t)((e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFF));
-            L.BVs[buf][8 * (lane & 1) + e][tok] = (_Float16)(bt * bf(bits));
-        }
+    for (int e = 0; e < 8; ++e) {
+        const uint16_t bits = (uint16_t)((e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFF));
+        L.BVs[buf][8 * (lane & 1) + e][tok] = (_Float16)(bt * bf(bits));
     }
-    L.gam[buf][2 * lane] = __uint_as_float(r.g[0]);
-    L.gam[buf][2 * lane + 1] = __uint_as_float(r.g[1]);
+    if (J == 0) {
+        L.gam[buf][2 * lane] = __uint_as_float(r.g[0]);
+        L.gam[buf][2 * lane + 1] = __uint_as_float(r.g[1]);
+    }
 }
 
 // Output rows of one chunk: the accumulator tile (lane = column, 4 rows) goes through LDS so
@@ -794,11 +797,10 @@ __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cu
     return O;
 }
 
-// Waves 0..3 compute.  Wave 4 only warms L2 ahead of them; wave 5 stages beta*V and gamma of
-// the next chunk in LDS.  Outstanding memory operations are counted per wave in issue order,
-// so the warm-up's long-latency loads and the staging loads stay out of the compute waves'
-// counters, and the per-CU address unit sees one wide load where each compute wave would
-// have issued several narrow ones.
+// Waves 0..3 compute.  Waves 4 and 5 stage beta*V of the next chunk in LDS, half the tokens
+// each (wave 5 also gamma), and wave 4 warms L2 ahead of the compute waves.  Outstanding memory
+// operations are counted per wave in issue order, so the warm-up's long-latency loads and the
+// staging loads stay out of the compute waves' counters.
 constexpr int kStateThreads = 384;
 
 __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, SeqMap sm) {
@@ -838,44 +840,46 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
         return (int)(t < C ? t : C);
     };
 
-    if (w == 4) {
-        // warm-up wave: touch chunks 1..kWarmAhead now, then one chunk per iteration between the
-        // two barriers, and take part in the compute waves' barriers (one before the loop, two
-        // per chunk)
+    if (w >= 4) {
+        // helper waves: chunk c+1's beta*V (wave 5 tokens 0..31 and gamma, wave 4 tokens 32..63)
+        // goes to LDS between the two barriers of chunk c, from registers loaded one chunk
+        // earlier; chunk c+2's loads are issued right after, away from the compute waves'
+        // operand loads before the first barrier.  Wave 4 also warms L2 with the record
+        // kWarmAhead chunks ahead.  Both take part in the compute waves' barriers (one before
+        // the loop, two per chunk).
         auto* dummy = reinterpret_cast<__attribute__((address_space(3))) void*>(
             reinterpret_cast<uintptr_t>(&L.warm_dummy[0]));
-        for (int64_t c = 1; c <= kWarmAhead && c < nchunks; ++c) warm_l2(rec_of(c), vb, lane, dummy);
-        lds_barrier();
-        for (int64_t c = 0; c < nchunks; ++c) {
+        const bool warm = w == 4;
+        auto run = [&](auto half) {
+            constexpr int J = decltype(half)::value;
+            StageRegs ra, rb;
+            if (warm)
+                for (int64_t c = 1; c <= kWarmAhead && c < nchunks; ++c) warm_l2(rec_of(c), vb, lane, dummy);
+            if (nchunks > 0) {
+                stage_load<J>(ra, v, beta, rec_of(0), bos, len_of(0), H, h, vb, lane);
+                stage_store<J>(L, 0, ra, lane, a.prologue);
+            }
+            if (nchunks > 1) stage_load<J>(rb, v, beta, rec_of(1), bos + C, len_of(1), H, h, vb, lane);
             lds_barrier();
-            if (c + 1 + kWarmAhead < nchunks) warm_l2(rec_of(c + 1 + kWarmAhead), vb, lane, dummy);
-            lds_barrier();
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS write may outlive the workgroup
-        return;
-    }
-    if (w == 5) {
-        // staging wave: chunk c+1's beta*V and gamma go to LDS between the two barriers of
-        // chunk c (from registers loaded one chunk earlier), and chunk c+2's loads are issued
-        // right after, away from the compute waves' operand loads before the first barrier
-        StageRegs ra, rb;
-        if (nchunks > 0) {
-            stage_load(ra, v, beta, rec_of(0), bos, len_of(0), H, h, vb, lane);
-            stage_store(L, 0, ra, lane, a.prologue);
-        }
-        if (nchunks > 1) stage_load(rb, v, beta, rec_of(1), bos + C, len_of(1), H, h, vb, lane);
-        lds_barrier();
-        for (int64_t c = 0; c < nchunks; c += 2) {
-            lds_barrier();
-            if (c + 1 < nchunks) stage_store(L, 1, rb, lane, a.prologue);
-            if (c + 2 < nchunks) stage_load(ra, v, beta, rec_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h, vb, lane);
-            lds_barrier();
-            if (c + 1 >= nchunks) break;
-            lds_barrier();
-            if (c + 2 < nchunks) stage_store(L, 0, ra, lane, a.prologue);
-            if (c + 3 < nchunks) stage_load(rb, v, beta, rec_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h, vb, lane);
-            lds_barrier();
-        }
+            for (int64_t c = 0; c < nchunks; c += 2) {
+                lds_barrier();
+                if (c + 1 < nchunks) stage_store<J>(L, 1, rb, lane, a.prologue);
+                if (c + 2 < nchunks)
+                    stage_load<J>(ra, v, beta, rec_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h, vb, lane);
+                if (warm && c + 1 + kWarmAhead < nchunks) warm_l2(rec_of(c + 1 + kWarmAhead), vb, lane, dummy);
+                lds_barrier();
+                if (c + 1 >= nchunks) break;
+                lds_barrier();
+                if (c + 2 < nchunks) stage_store<J>(L, 0, ra, lane, a.prologue);
+                if (c + 3 < nchunks)
+                    stage_load<J>(rb, v, beta, rec_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h, vb, lane);
+                if (warm && c + 2 + kWarmAhead < nchunks) warm_l2(rec_of(c + 2 + kWarmAhead), vb, lane, dummy);
+                lds_barrier();
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS write may outlive the workgroup
+        };
+        if (w == 4) run(std::integral_constant<int, 1>{});
+        else run(std::integral_constant<int, 0>{});
         return;
     }
 
