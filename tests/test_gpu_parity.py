@@ -45,6 +45,8 @@ def _run_prefill(w, B, T, with_state):
     ("f32", 128, 32, 1, 70, True),
     ("bf16", 64, 32, 2, 50, True),      # bf16 storage through the fp32 kernel
     ("bf16", 128, 64, 1, 64, False),    # one full chunk
+    ("bf16", 128, 64, 1, 128, True),    # two chunks: one pass of the two-chunk loop
+    ("bf16", 128, 64, 1, 130, True),    # three chunks, the last two tokens long
     ("bf16", 128, 64, 1, 1000, False),  # several chunks + ragged tail
     ("bf16", 128, 64, 2, 333, True),
     ("bf16", 128, 64, 1, 1, True),      # a single token
