@@ -637,11 +637,6 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
         pK.store(sKT, LT);
         pU.store(sU, kBV);
         pg.store(sg, DK);
-        fetch(c + 1 < nck ? c + 1 : c);
-        {  // W, U and K'^T (one contiguous range) of the chunk kWarm ahead
-            const float* wrec = a.ws + ((slot0 + (c + kWarm < nck ? c + kWarm : nck - 1)) * H + h) * R::kFloats;
-            warm_range<R::Kd>(wrec, 0, vb, NVB, dummy);
-        }
         for (int e = tid; e < DK * kBV; e += kThreads)
             rec[R::S0 + (e / kBV) * DV + vb * kBV + e % kBV] = sSt[(e % kBV) * LW + e / kBV];
         lds_barrier();
@@ -659,6 +654,13 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
             *reinterpret_cast<float4*>(sDt + lr * LT + 16 * rb + 4 * lg) = dv;
         }
         lds_barrier();
+        // the next chunk's operands and the L2 warm-up are requested here, after D: issued before
+        // it, their loads held up the product that the next barrier waits for
+        fetch(c + 1 < nck ? c + 1 : c);
+        {  // W, U and K'^T (one contiguous range) of the chunk kWarm ahead
+            const float* wrec = a.ws + ((slot0 + (c + kWarm < nck ? c + kWarm : nck - 1)) * H + h) * R::kFloats;
+            warm_range<R::Kd>(wrec, 0, vb, NVB, dummy);
+        }
         // S <- Diag(gamma) S + K'^T D
 #pragma unroll
         for (int cb = w; cb < DK / 16; cb += 4) {
@@ -736,11 +738,6 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
             const int e = tid + m * kThreads;
             if (e < C * kBV) sdOt[(e % kBV) * LT + e / kBV] = rdo[m];
         }
-        fetch(c > 0 ? c - 1 : c);
-        {  // K', Q+^T, W^T and M^T (one contiguous range) of the chunk kWarm behind
-            const float* wrec = a.ws + ((slot0 + (c >= kWarm ? c - kWarm : 0)) * H + h) * R::kFloats;
-            warm_range<R::T - R::Kd>(wrec, R::Kd, vb, NVB, dummy);
-        }
         for (int e = tid; e < DK * kBV; e += kThreads)
             rec[R::dS1 + (e / kBV) * DV + vb * kBV + e % kBV] = sdSt[(e % kBV) * LW + e / kBV];
         lds_barrier();
@@ -753,6 +750,13 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
             *reinterpret_cast<float4*>(sdDt + lr * LT + 16 * rb + 4 * lg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
         lds_barrier();
+        // the previous chunk's operands and the L2 warm-up are requested here, after dD (see
+        // fwd_chain)
+        fetch(c > 0 ? c - 1 : c);
+        {  // K', Q+^T, W^T and M^T (one contiguous range) of the chunk kWarm behind
+            const float* wrec = a.ws + ((slot0 + (c >= kWarm ? c - kWarm : 0)) * H + h) * R::kFloats;
+            warm_range<R::T - R::Kd>(wrec, R::Kd, vb, NVB, dummy);
+        }
         // dS <- Diag(gamma) dS + Q+^T dO - W^T dD
 #pragma unroll
         for (int cb = w; cb < DK / 16; cb += 4) {
