@@ -60,7 +60,7 @@ _MFMA_SHA = "46d248ca868e63c42c381d93c6569529d739263f0963389a289ac03f0cc9dd87"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
 _DECODE_SHA = "2994ede3f200b6caf1eb3a50f86a9e66dce4f573b9f983c576d7d490a90a2b4d"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
-_BWD_SHA = "14f6690038584df786cb954ead7ffa654108c4499cccaa27c71aaefa09dd4a81"
+_BWD_SHA = "8786058cb8a1138ef1c2d6bb948ce3ab30a8322623f3ac08012fc9d6ff0c903b"
 
 
 def _counted(fetch_kib, write_kib):
@@ -77,8 +77,8 @@ MEASURED_TRAFFIC = {
                    "bytes": _counted(267360.0, 528670.0)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
     "kda_backward": {"source": _BWD_SRC, "sha256": _BWD_SHA, "workload": "backward T=65536 H=32",
-                     "bytes": _counted(3553838.0 + 1604452.3 + 2780012.4 + 3788357.1 + 9377751.2,
-                                       7883223.0 + 3381520.5 + 3470729.5 + 3686914.2 + 4522764.3)},
+                     "bytes": _counted(3539131.8 + 1602078.2 + 2429950.4 + 3787802.2 + 9393159.3,
+                                       7881839.4 + 3381197.9 + 3390170.0 + 3686916.1 + 4522661.3)},
 }
 
 
