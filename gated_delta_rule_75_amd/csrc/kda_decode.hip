@@ -65,6 +65,12 @@ __global__ __launch_bounds__(1024) void decode_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         st[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sin + (int64_t)(rg + i * RG) * DV));
+    // v and beta of this thread's columns, needed only after the reductions, are requested now so
+    // that their latency overlaps the state loads instead of following the reductions
+    float vv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vv[j] = ld_in(v, nh * DV + 4 * c4 + j);
+    const float braw = ld_in(beta, nh);
     // alpha, k, q of every key row, one row per thread, shared through LDS
     float kt = 0.f, qt = 0.f;
     if (tid < DK) {
@@ -143,9 +149,9 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     }
 
     float d[4];
-    const float b = PROLOGUE ? sigmoid(ld_in(beta, nh)) : ld_in(beta, nh);
+    const float b = PROLOGUE ? sigmoid(braw) : braw;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d[j] = b * (ld_in(v, nh * DV + 4 * c4 + j) - uu[j]);
+    for (int j = 0; j < 4; ++j) d[j] = b * (vv[j] - uu[j]);
     if (rg == 0) {
         floatx4 ov;
 #pragma unroll
