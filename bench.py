@@ -58,7 +58,7 @@ _KIB = 1024
 _MFMA_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_mfma.hip"
 _MFMA_SHA = "46d248ca868e63c42c381d93c6569529d739263f0963389a289ac03f0cc9dd87"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
-_DECODE_SHA = "2994ede3f200b6caf1eb3a50f86a9e66dce4f573b9f983c576d7d490a90a2b4d"
+_DECODE_SHA = "0efe675059ee1ae0f51f5a31a1c1c41ff8e96536686270e3140e8030e17def42"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
 _BWD_SHA = "8786058cb8a1138ef1c2d6bb948ce3ab30a8322623f3ac08012fc9d6ff0c903b"
 
@@ -74,7 +74,7 @@ MEASURED_TRAFFIC = {
     "kda_state": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
                   "bytes": _counted(1337735.4, 1052835.1)},
     "kda_decode": {"source": _DECODE_SRC, "sha256": _DECODE_SHA, "workload": "decode N=256 H=32",
-                   "bytes": _counted(267360.0, 528670.0)},
+                   "bytes": _counted(267360.2, 528567.1)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
     "kda_backward": {"source": _BWD_SRC, "sha256": _BWD_SHA, "workload": "backward T=65536 H=32",
                      "bytes": _counted(3539131.8 + 1602078.2 + 2429950.4 + 3787802.2 + 9393159.3,
