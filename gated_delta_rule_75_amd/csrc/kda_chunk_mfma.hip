@@ -222,6 +222,15 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         kv[ks] = *reinterpret_cast<const uint4*>(k + rowk + c0);
         qv[ks] = *reinterpret_cast<const uint4*>(q + rowk + c0);
     }
+    // beta of this lane's token and of the accumulator rows 16w + 4lg + i, requested with the
+    // other inputs so that their latency does not open a later phase
+    const uint16_t beta_r = beta[(t0 + (valid ? r : Lc - 1)) * H + h];
+    uint16_t beta_q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * w + 4 * lg + i;
+        beta_q[i] = beta[(t0 + (rr < Lc ? rr : Lc - 1)) * H + h];
+    }
     // g as floats (zero past the chunk end); k, q stay packed bf16 until used
     float gl[4][8];
 #pragma unroll
@@ -285,7 +294,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
 
     // ---- operand tiles for this lane's token and 32 channels
     // beta of this lane's token (0 past the chunk end) for Diag(beta) K+
-    float brow_r = bf(beta[(t0 + (valid ? r : Lc - 1)) * H + h]);
+    float brow_r = bf(beta_r);
     brow_r = valid ? (PRO ? sigmoid(brow_r) : brow_r) : 0.f;
     // fused prologue: this token's key and query are scaled to unit length (its 128 channels
     // are spread over the 4 lanes lr, lr + 16, lr + 32, lr + 48)
@@ -405,7 +414,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int rr = 16 * w + 4 * lg + i;
-        const float bv = bf(beta[(t0 + (rr < Lc ? rr : Lc - 1)) * H + h]);
+        const float bv = bf(beta_q[i]);
         brow[i] = rr < Lc ? (PRO ? sigmoid(bv) : bv) : 0.f;
     }
     if (!EXACT) {  // the second pass has its exact tile in place already
