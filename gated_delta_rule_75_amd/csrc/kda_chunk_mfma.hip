@@ -122,7 +122,9 @@ __device__ __forceinline__ floatx4 mm16(const float* Ap, int lda, const float* B
 // ------------------------------------------------------------------------------------------
 // prep kernel: one workgroup (4 waves) per (slot, head); wave w owns token block w
 // ------------------------------------------------------------------------------------------
-struct PrepLds {
+// 16-byte aligned, so that the compiler may use 128-bit LDS accesses for the fragment and
+// table rows (with the 4-byte alignment of its members it splits every access into 32-bit ones)
+struct alignas(16) PrepLds {
     // per key channel, per 16-token block b (all fp32):
     float tot[4][DK];     // D_b = sum of g over block b
     float gmid[4][DK];    // within-block cumulative g at the block's 8th token
