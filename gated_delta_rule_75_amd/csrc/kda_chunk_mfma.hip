@@ -490,6 +490,15 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         __syncthreads();
     }
 
+    // ---- W's right-hand operand, Diag(beta) K+, staged transposed ([channel][token]) so that
+    //      each matrix-core B fragment (8 consecutive tokens of one channel) is one 16-byte read.
+    //      It shares the union with the inverse scratch, dead since the barrier above, and the
+    //      barrier after the tile write-out below makes it visible.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) L.u.bkT[32 * ks + 8 * lg + i][r] = BKp[ks][i];
+
     // ---- write T, M (8 tiles each) and K'^T (16 tiles) as fp16 operand tiles
     for (int t = w; t < 8; t += 4) {
         const int rb = t >> 1, kb = t & 1;
@@ -510,16 +519,9 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         const half8 kd = *reinterpret_cast<const half8*>(&L.o.kdT[16 * cb + lr][32 * ks + 8 * lg]);
         *reinterpret_cast<half8*>(rec + kOffKdT + t * kTile + lane * 16) = kd;
     }
-    __syncthreads();  // K'^T read out of the union; the inverse scratch is dead
+    __syncthreads();  // K'^T read out of its union (W overwrites it); Diag(beta) K+ staged
 
-    // ---- W = T Diag(beta) K+ (64 x 128): rows of token block w, all 8 channel blocks.  The
-    //      right-hand operand is staged transposed ([channel][token]) so that each matrix-core
-    //      B fragment (8 consecutive tokens of one channel) is one 16-byte read.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) L.u.bkT[32 * ks + 8 * lg + i][r] = BKp[ks][i];
-    __syncthreads();
+    // ---- W = T Diag(beta) K+ (64 x 128): rows of token block w, all 8 channel blocks
     {
         half8 ta[2];  // T rows of block w as matrix-core A operand, k-steps 0..1 (zero above the diagonal)
 #pragma unroll
