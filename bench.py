@@ -56,7 +56,7 @@ DECODE_BYTES_PER_SEQ_HEAD = 65536 + 65536 + 768 + 512 + 2 + 512         # 132866
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 _KIB = 1024
 _MFMA_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_mfma.hip"
-_MFMA_SHA = "b4c830a3a3aa4d8c8ab2031e2547686ad4491b453cc4c35fdfbaf82e40b554b8"
+_MFMA_SHA = "82df15bd320934547fe32a598f83e22a2b4bf160e4e56b607563d4f43466cf6b"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
 _DECODE_SHA = "0efe675059ee1ae0f51f5a31a1c1c41ff8e96536686270e3140e8030e17def42"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
@@ -70,9 +70,9 @@ def _counted(fetch_kib, write_kib):
 # kernel name -> where and on what it was measured, and HBM bytes per launch
 MEASURED_TRAFFIC = {
     "kda_prep": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                 "bytes": _counted(1065138.7, 2114565.9)},
+                 "bytes": _counted(1065139.0, 2114563.2)},
     "kda_state": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                  "bytes": _counted(1338010.8, 1052572.2)},
+                  "bytes": _counted(1337457.1, 1052735.4)},
     "kda_decode": {"source": _DECODE_SRC, "sha256": _DECODE_SHA, "workload": "decode N=256 H=32",
                    "bytes": _counted(267360.2, 528567.1)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
