@@ -105,10 +105,14 @@ def _options(gate, every=0, snapshots=None, snapshot_cu=None, gate_scale=None):
 
 
 def _workspace(nbytes, device, workspace):
+    """The caller's workspace (a contiguous uint8 tensor on `device`) when it is large enough,
+    else a new one."""
     if nbytes == 0:
         return None
-    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
-        return workspace
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, None, device)
+        if workspace.numel() >= nbytes:
+            return workspace
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
@@ -160,14 +164,17 @@ def prefill_chunked(q, k, v, g, beta, state=None, *, chunk=64, out=None, state_o
 
 
 def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=None, state_out=None,
-                   final_state=True, workspace=None, snapshot_every=0, prologue_gate_scale=None):
+                   final_state=True, workspace=None, snapshot_every=0, snapshots=None, prologue_gate_scale=None):
     """Append-prefill of N packed segments (token-major [T_total, H, d]) on carried states.
 
     cu_seqlens: int32 GPU tensor [N+1] (0, ..., T_total).  g [T_total,H,dk] or [T_total,H] (one
     decay per head).  state [N,H,dk,dv] float32 or None.
     Returns (o [T_total,H,dv] float32, S_T [N,H,dk,dv] float32 or None), plus, when
-    snapshot_every > 0, (snapshots [S,H,dk,dv], snapshot_cu int32 [N+1]): the state after every
-    snapshot_every chunks of each segment, segment n at rows snapshot_cu[n] .. snapshot_cu[n+1]-1."""
+    snapshot_every > 0, (snapshots [R,H,dk,dv], snapshot_cu int32 [N+1]): the state after every
+    snapshot_every chunks of each segment, segment n at rows snapshot_cu[n] .. snapshot_cu[n+1]-1.
+    snapshot_cu is computed on the device (no host synchronisation), so the row count is not
+    known here: snapshots (given, or allocated) has R = T_total // (snapshot_every * chunk) rows,
+    an upper bound of snapshot_cu[N]; rows from snapshot_cu[N] on are not written."""
     T, H, dk = q.shape
     dv = v.shape[-1]
     N = cu_seqlens.numel() - 1
@@ -183,14 +190,20 @@ def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=No
     _check(beta, "beta", dt, (T, H), dev)
     _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
     _check(state, "state", torch.float32, (N, H, dk, dv), dev)
-    snapshots = snapshot_cu = None
+    snapshot_cu = None
     if snapshot_every > 0:
-        # per-segment snapshot counts from the segment lengths (a host copy of cu_seqlens)
-        counts = torch.diff(cu_seqlens.to("cpu", torch.int64)) // (snapshot_every * chunk)
-        snapshot_cu = torch.zeros(N + 1, dtype=torch.int32)
-        snapshot_cu[1:] = torch.cumsum(counts, 0)
-        snapshot_cu = snapshot_cu.to(dev)
-        snapshots = torch.empty((int(counts.sum()), H, dk, dv), dtype=torch.float32, device=dev)
+        # per-segment snapshot counts from the segment lengths, on the device
+        counts = torch.diff(cu_seqlens.to(torch.int64)) // (snapshot_every * chunk)
+        snapshot_cu = torch.zeros(N + 1, dtype=torch.int32, device=dev)
+        snapshot_cu[1:] = torch.cumsum(counts, 0).to(torch.int32)
+        rows = T // (snapshot_every * chunk)
+        if snapshots is None:
+            snapshots = torch.empty((rows, H, dk, dv), dtype=torch.float32, device=dev)
+        _check(snapshots, "snapshots", torch.float32, None, dev)
+        if snapshots.dim() != 4 or tuple(snapshots.shape[1:]) != (H, dk, dv) or snapshots.shape[0] < rows:
+            raise ValueError(f"snapshots must be [>= {rows}, {H}, {dk}, {dv}], got {tuple(snapshots.shape)}")
+    elif snapshots is not None:
+        raise ValueError("snapshots given without snapshot_every")
     if out is None:
         out = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
     _check(out, "out", torch.float32, (T, H, dv), dev)

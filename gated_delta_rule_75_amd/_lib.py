@@ -22,7 +22,7 @@ KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
 # every symbol include/kda.h declares
 EXPORTS = ("kda_prefill_chunked", "kda_append_prefill", "kda_decode_step", "kda_prefill_chunked_ex",
            "kda_append_prefill_ex", "kda_decode_step_ex", "kda_chunked_backward", "kda_workspace_size",
-           "kda_is_supported",
+           "kda_is_supported", "kda_validate_cu_seqlens", "kda_validate_snapshot_cu", "kda_validate_gates",
            "kda_status_string", "kda_last_error", "kda_version", "kda_timing_begin", "kda_timing_end")
 KERNEL_NAMES = {1: "kda_prep", 2: "kda_state", 3: "kda_chunk_f32", 4: "kda_decode", 5: "kda_bwd_factors",
                 6: "kda_bwd_fwd_chain", 7: "kda_bwd_rev_chain", 8: "kda_bwd_grad_state", 9: "kda_bwd_grad_chunk"}
@@ -81,6 +81,12 @@ def load():
     L.kda_timing_begin.argtypes = []
     L.kda_timing_end.restype = ctypes.c_int
     L.kda_timing_end.argtypes = [vp, vp, i32]
+    L.kda_validate_cu_seqlens.restype = ctypes.c_int
+    L.kda_validate_cu_seqlens.argtypes = [vp, i32, i64]
+    L.kda_validate_snapshot_cu.restype = ctypes.c_int
+    L.kda_validate_snapshot_cu.argtypes = [vp, vp, i32, i32, i32]
+    L.kda_validate_gates.restype = ctypes.c_int
+    L.kda_validate_gates.argtypes = [vp, i64, vp, i64, i32]
     _LIB = L
     return L
 

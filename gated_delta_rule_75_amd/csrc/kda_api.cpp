@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -109,6 +110,58 @@ int check_hip(hipError_t e, hipStream_t s, const char* what) {
 // Host-side stand-in for a launch failure, for tests of the error path only.
 bool injected_launch_failure() { return env_flag("KDA_TEST_FAIL_LAUNCH"); }
 
+// ---------------------------------------------------------------------------------------
+// Debug checks of device-resident data (KDA_DEBUG_CHECK=1): the offsets and gates are
+// copied to the host, after the caller's stream has drained, and validated before any
+// launch.  Off by default: the calls then never synchronise.
+// ---------------------------------------------------------------------------------------
+bool debug_check() { return env_flag("KDA_DEBUG_CHECK"); }
+
+template <typename T>
+int fetch(const void* dev, size_t count, hipStream_t s, std::vector<T>& out, const char* name) {
+    out.resize(count);
+    if (!count) return KDA_OK;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipMemcpy(out.data(), dev, count * sizeof(T), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s (debug check): %s", name, hipGetErrorString(e));
+    return KDA_OK;
+}
+
+float bf16_bits_to_float(uint16_t b) {
+    const uint32_t u = static_cast<uint32_t>(b) << 16;
+    float f;
+    std::memcpy(&f, &u, sizeof(f));
+    return f;
+}
+
+// cu_seqlens (and snapshot_cu when every > 0) of an append or backward call
+int debug_check_offsets(const int32_t* cu, int32_t N, int64_t T_total, const int32_t* snap_cu, int32_t every,
+                        int32_t chunk, hipStream_t s, const char* name) {
+    std::vector<int32_t> h, hs;
+    if (int rc = fetch(cu, (size_t)N + 1, s, h, name)) return rc;
+    if (int rc = kda_validate_cu_seqlens(h.data(), N, T_total)) return rc;
+    if (every > 0 && snap_cu) {
+        if (int rc = fetch(snap_cu, (size_t)N + 1, s, hs, name)) return rc;
+        if (int rc = kda_validate_snapshot_cu(h.data(), hs.data(), N, every, chunk)) return rc;
+    }
+    return KDA_OK;
+}
+
+// g (ng floats) and beta (nb values of dtype); raw prologue inputs are only checked to be finite
+int debug_check_gates(const float* g, size_t ng, const void* beta, size_t nb, int32_t dtype, bool prologue,
+                      hipStream_t s, const char* name) {
+    std::vector<float> hg, hb(nb);
+    if (int rc = fetch(g, ng, s, hg, name)) return rc;
+    if (dtype == KDA_BF16) {
+        std::vector<uint16_t> raw;
+        if (int rc = fetch(beta, nb, s, raw, name)) return rc;
+        for (size_t i = 0; i < nb; ++i) hb[i] = bf16_bits_to_float(raw[i]);
+    } else if (int rc = fetch(beta, nb, s, hb, name)) {
+        return rc;
+    }
+    return kda_validate_gates(hg.data(), (int64_t)ng, hb.data(), (int64_t)nb, prologue ? 1 : 0);
+}
+
 bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
 
 // Which chunked implementation serves (dtype, dk, dv, chunk): 2 = matrix cores, 1 = fp32, 0 = none.
@@ -194,7 +247,51 @@ int read_options(const kda_options* o, int op, const char* name, Opts& out) {
 
 extern "C" {
 
-const char* kda_version(void) { return "kda-mi355x 0.1.0 (gfx950)"; }
+int kda_validate_cu_seqlens(const int32_t* cu, int32_t N, int64_t T_total) {
+    if (!cu || N < 0) return fail(KDA_ERR_INVALID_ARG, "kda_validate_cu_seqlens: cu must be non-NULL and N >= 0");
+    if (cu[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    for (int32_t n = 0; n < N; ++n)
+        if (cu[n + 1] < cu[n])
+            return fail(KDA_ERR_INVALID_ARG, "cu_seqlens decreases at %d: %d > %d", n, cu[n], cu[n + 1]);
+    if ((int64_t)cu[N] != T_total)
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[%d] = %d, expected T_total = %lld", N, cu[N], (long long)T_total);
+    return ok();
+}
+
+int kda_validate_snapshot_cu(const int32_t* cu, const int32_t* snapshot_cu, int32_t N, int32_t snapshot_every,
+                             int32_t chunk) {
+    if (!cu || !snapshot_cu || N < 0 || snapshot_every <= 0 || chunk <= 0)
+        return fail(KDA_ERR_INVALID_ARG, "kda_validate_snapshot_cu: bad arguments");
+    if (snapshot_cu[0] != 0) return fail(KDA_ERR_INVALID_ARG, "snapshot_cu[0] = %d, expected 0", snapshot_cu[0]);
+    const int64_t interval = (int64_t)snapshot_every * chunk;
+    for (int32_t n = 0; n < N; ++n) {
+        const int64_t want = ((int64_t)cu[n + 1] - cu[n]) / interval;
+        if ((int64_t)snapshot_cu[n + 1] - snapshot_cu[n] != want)
+            return fail(KDA_ERR_INVALID_ARG, "snapshot_cu[%d] - snapshot_cu[%d] = %d, expected %lld", n + 1, n,
+                        snapshot_cu[n + 1] - snapshot_cu[n], (long long)want);
+    }
+    return ok();
+}
+
+int kda_validate_gates(const float* g, int64_t n_g, const float* beta, int64_t n_beta, int32_t raw) {
+    if ((n_g > 0 && !g) || (n_beta > 0 && !beta) || n_g < 0 || n_beta < 0)
+        return fail(KDA_ERR_INVALID_ARG, "kda_validate_gates: bad arguments");
+    for (int64_t i = 0; i < n_g; ++i) {
+        const float x = g[i];
+        if (!std::isfinite(x) || (!raw && x > 0.f))
+            return fail(KDA_ERR_INVALID_ARG, "g[%lld] = %g: %s", (long long)i, (double)x,
+                        raw ? "not finite" : "a log-decay must be finite and <= 0");
+    }
+    for (int64_t i = 0; i < n_beta; ++i) {
+        const float x = beta[i];
+        if (!std::isfinite(x) || (!raw && (x < 0.f || x > 1.f)))
+            return fail(KDA_ERR_INVALID_ARG, "beta[%lld] = %g: %s", (long long)i, (double)x,
+                        raw ? "not finite" : "must lie in [0, 1]");
+    }
+    return ok();
+}
+
+const char* kda_version(void) { return "kda-mi355x 0.2.0 (gfx950)"; }
 
 int kda_timing_begin(void) {
     g_timing.on = true;
@@ -289,6 +386,16 @@ int kda_prefill_chunked_ex(const void* q, const void* k, const void* v, const fl
     if (need && (!workspace || workspace_bytes < need))
         return fail(KDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name, need,
                     workspace ? workspace_bytes : (size_t)0);
+    const Span wsp{workspace, need};
+    for (const Span& in : ins)
+        if (overlap(wsp, in)) return fail(KDA_ERR_ALIAS, "%s: the workspace overlaps an input", name);
+    if (overlap(wsp, o) || overlap(wsp, sout) || overlap(wsp, snp))
+        return fail(KDA_ERR_ALIAS, "%s: the workspace overlaps out, state_out or snapshots", name);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (debug_check())
+        if (int rc = debug_check_gates(g, tokens * H * (op.gate_head ? 1 : d_k), beta, tokens * H, dtype, op.prologue,
+                                       stream, name))
+            return rc;
     kda::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s0 = state_in; a.o = out; a.sT = state_out;
@@ -298,7 +405,7 @@ int kda_prefill_chunked_ex(const void* q, const void* k, const void* v, const fl
     a.gate_head = op.gate_head; a.snap = snap_per_seq > 0 ? op.snaps : nullptr; a.snap_every = op.every;
     a.snap_cu = nullptr; a.snap_per_seq = snap_per_seq;
     a.prologue = op.prologue; a.gate_scale = op.gate_scale;
-    return run_prefill(a, dtype, static_cast<hipStream_t>(hip_stream), name);
+    return run_prefill(a, dtype, stream, name);
 }
 
 int kda_prefill_chunked(const void* q, const void* k, const void* v, const float* g, const void* beta,
@@ -346,6 +453,18 @@ int kda_append_prefill_ex(const void* q, const void* k, const void* v, const flo
     if (need && (!workspace || workspace_bytes < need))
         return fail(KDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name, need,
                     workspace ? workspace_bytes : (size_t)0);
+    const Span wsp{workspace, need};
+    for (const Span& in : ins)
+        if (overlap(wsp, in)) return fail(KDA_ERR_ALIAS, "%s: the workspace overlaps an input", name);
+    if (overlap(wsp, o) || overlap(wsp, sout) || overlap(wsp, snp))
+        return fail(KDA_ERR_ALIAS, "%s: the workspace overlaps out, state_out or snapshots", name);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (debug_check()) {
+        if (int rc = debug_check_offsets(cu_seqlens, N, T_total, op.snap_cu, op.every, chunk, stream, name)) return rc;
+        if (int rc = debug_check_gates(g, tokens * H * (op.gate_head ? 1 : d_k), beta, tokens * H, dtype, op.prologue,
+                                       stream, name))
+            return rc;
+    }
     kda::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s0 = state_in; a.o = out; a.sT = state_out;
@@ -355,7 +474,7 @@ int kda_append_prefill_ex(const void* q, const void* k, const void* v, const flo
     a.gate_head = op.gate_head; a.snap = op.snaps; a.snap_every = op.every; a.snap_cu = op.snap_cu;
     a.snap_per_seq = 0;
     a.prologue = op.prologue; a.gate_scale = op.gate_scale;
-    return run_prefill(a, dtype, static_cast<hipStream_t>(hip_stream), name);
+    return run_prefill(a, dtype, stream, name);
 }
 
 int kda_append_prefill(const void* q, const void* k, const void* v, const float* g, const void* beta,
@@ -415,6 +534,11 @@ int kda_chunked_backward(const void* q, const void* k, const void* v, const floa
     if (need && (!workspace || workspace_bytes < need))
         return fail(KDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name, need,
                     workspace ? workspace_bytes : (size_t)0);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (debug_check()) {
+        if (int rc = debug_check_offsets(cu_seqlens, N, T_total, nullptr, 0, chunk, s, name)) return rc;
+        if (int rc = debug_check_gates(g, tokens * H * gk, beta, tokens * H, dtype, false, s, name)) return rc;
+    }
     if (injected_launch_failure()) return fail(KDA_ERR_HIP, "%s: injected launch failure (KDA_TEST_FAIL_LAUNCH)", name);
     kda::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
@@ -423,7 +547,6 @@ int kda_chunked_backward(const void* q, const void* k, const void* v, const floa
     a.s0 = state_in; a.dO = d_out; a.dsT = d_state_out;
     a.gq = dq; a.gk = dk; a.gv = dv; a.gg = dg; a.gbeta = dbeta; a.gs0 = d_state_in;
     a.ws = static_cast<float*>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
     return check_hip(kda::launch_chunk_bwd(a, s), s, name);
 }
 
@@ -452,13 +575,17 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const float*
     if (overlap(o, sout)) return fail(KDA_ERR_ALIAS, "%s: out overlaps state_out", name);
     if (overlap(sin, sout) && state_in != state_out)
         return fail(KDA_ERR_ALIAS, "%s: state_out partially overlaps state_in", name);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (debug_check())
+        if (int rc = debug_check_gates(g, (size_t)N * H * (op.gate_head ? 1 : d_k), beta, (size_t)N * H, dtype,
+                                       op.prologue, s, name))
+            return rc;
     if (injected_launch_failure()) return fail(KDA_ERR_HIP, "%s: injected launch failure (KDA_TEST_FAIL_LAUNCH)", name);
     kda::DecodeArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s_in = state_in; a.s_out = state_out; a.o = out;
     a.N = N; a.H = H; a.dk = d_k; a.dv = d_v; a.bf16 = dtype == KDA_BF16; a.gate_head = op.gate_head;
     a.prologue = op.prologue; a.gate_scale = op.gate_scale;
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
     return check_hip(kda::launch_decode(a, s), s, name);
 }
 

@@ -20,7 +20,9 @@
 //
 // One workgroup per (sequence, head, block of 16 value columns); value columns
 // never interact, so blocks of them are independent chains.  With one forget gate
-// per head (Gated DeltaNet) every key channel takes the same log-decay.
+// per head (Gated DeltaNet) every key channel takes the same log-decay.  The same
+// kernel redoes, in fp32, the chains of the matrix-core path that met values beyond
+// the fp16 range (PrefillArgs::redo).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(PrefillArgs a) {
     const int h = (blockIdx.x / NVB) % H;
     const int64_t n = blockIdx.x / NVB / H;
     const int tid = threadIdx.x;
+    if (a.redo && a.redo[blockIdx.x] == 0) return;  // uniform over the workgroup
     const int64_t bos = a.cu ? (int64_t)a.cu[n] : n * a.T_fixed;
     const int64_t eos = a.cu ? (int64_t)a.cu[n + 1] : bos + a.T_fixed;
     const int64_t sbase = (n * H + h) * (int64_t)DK * DV + vb * kBV;

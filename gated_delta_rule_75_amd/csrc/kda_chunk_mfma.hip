@@ -31,6 +31,12 @@
 // reference is the block's 8th token; those factors are bounded by the decay of at
 // most 8 tokens.  Where that decay exceeds e^10 for some channel (beyond fp16), the
 // chunk's diagonal tiles are summed exactly in fp32 with per-pair exponentials instead.
+//
+// Magnitudes beyond fp16: every value that is rounded to an fp16 operand is checked against
+// the fp16 range first (q and k entries, M, T, W in prep; beta*V, the corrections D and the
+// state in the state pass; a NaN or Inf fails the check too).  A (sequence, head, value
+// block) chain that meets such a value is not finished here: its final state is left
+// unwritten, and a third pass recomputes the whole chain with the fp32 chunked kernel.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -145,7 +151,16 @@ struct alignas(16) PrepLds {
         _Float16 bkT[DK][C + 8];   // Diag(beta) K+ as [channel][token]: B operand of W
     } u;
     int exact_diag;  // some channel's 8-token decay is beyond the fp16 factors
+    int range_bad;   // some value rounded to an fp16 operand is beyond the fp16 range
 };
+
+// |x| within the fp16 range (false for NaN and Inf)
+__device__ __forceinline__ bool f16_ok(float x) { return __builtin_fabsf(x) < 65504.f; }
+
+// per-unit flag word written by prep: bit 0 = exact diagonal tiles needed (redone by the
+// second prep pass), bit 1 = a value beyond the fp16 range (the chain is redone in fp32)
+constexpr int kFlagExact = 1;
+constexpr int kFlagRange = 2;
 
 __device__ __forceinline__ float dpp_row_shr(float x, int d) {
     // lanes whose source is outside their 16-lane row read 0 (bound_ctrl)
@@ -194,7 +209,10 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
     const uint16_t* k = static_cast<const uint16_t*>(a.k);
     const uint16_t* beta = static_cast<const uint16_t*>(a.beta);
 
-    if (threadIdx.x == 0) L.exact_diag = 0;
+    if (threadIdx.x == 0) {
+        L.exact_diag = 0;
+        L.range_bad = 0;
+    }
 
     // ---- this lane: token r = 16w + lr, channels 32*ks + 8*lg + i (the matrix-core operand
     //      layout); rows past the chunk end load a clamped row and are zeroed
@@ -292,7 +310,6 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         if (bad) L.exact_diag = 1;  // benign race: every writer stores 1
     }
     __syncthreads();
-    if (!EXACT && threadIdx.x == 0) *flag = L.exact_diag;
 
     // ---- operand tiles for this lane's token and 32 channels
     // beta of this lane's token (0 past the chunk end) for Diag(beta) K+
@@ -369,6 +386,9 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
     }
     half8 KR[4], QR[4], BKp[4];
     floatx4 diagA = {0.f, 0.f, 0.f, 0.f}, diagM = {0.f, 0.f, 0.f, 0.f};  // tile (w, w)
+    // largest |q|, |k| entry of this lane: the decay-folded operands are bounded by it (times
+    // e^10 for the diagonal-tile factors, whose overflow shows up in M and T below)
+    float qkmax = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         half8 kp, qp, kc, krd, qrd, kcd;
@@ -381,6 +401,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
             const uint32_t kb16 = (i & 1) ? (kw[i >> 1] >> 16) : (kw[i >> 1] & 0xFFFF);
             const uint32_t qb16 = (i & 1) ? (qw[i >> 1] >> 16) : (qw[i >> 1] & 0xFFFF);
             const float kk = valid ? bf(kb16) * inv_k : 0.f, qq = valid ? bf(qb16) * inv_q : 0.f;
+            qkmax = fmaxf(qkmax, fmaxf(__builtin_fabsf(kk), __builtin_fabsf(qq)));
             const float eloc = fast_exp(gloc);              // exp(G_r - P_w)          <= 1
             const float ecol = fast_exp(L.tot[w][ch] - gloc);  // exp(P_{w+1} - G_r)   <= 1
             const float ep = L.eP[w][ch];
@@ -419,6 +440,8 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         const float bv = bf(beta_q[i]);
         brow[i] = rr < Lc ? (PRO ? sigmoid(bv) : bv) : 0.f;
     }
+    // NaN-safe: a NaN entry fails the comparison
+    bool rbad = !(qkmax < 32768.f);
     if (!EXACT) {  // the second pass has its exact tile in place already
         const floatx4 accA = diagA, accM = diagM;
         // accumulator: column s = lr of block j, rows 4*lg + i of block w
@@ -426,8 +449,13 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         for (int i = 0; i < 4; ++i) {
             const int rr = 16 * w + 4 * lg + i, ss = 16 * w + lr;
             L.AT[rr][ss] = (ss < rr) ? brow[i] * accA[i] : 0.f;
-            L.M[rr][ss] = (_Float16)((ss <= rr) ? accM[i] : 0.f);
+            const float mv = (ss <= rr) ? accM[i] : 0.f;
+            rbad |= !f16_ok(mv);
+            L.M[rr][ss] = (_Float16)mv;
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rbad |= !f16_ok((float)L.M[r][16 * w + 4 * lg + j]);
     }
     for (int j = w + 1; j < 4; ++j)
 #pragma unroll
@@ -450,6 +478,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         for (int i = 0; i < 4; ++i) {
             const int rr = 16 * w + 4 * lg + i, ss = 16 * j + lr;
             L.AT[rr][ss] = brow[i] * accA[i];
+            rbad |= !f16_ok(accM[i]);
             L.M[rr][ss] = (_Float16)accM[i];
         }
     }
@@ -508,6 +537,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
             const int col = 32 * kb + 8 * lg + i, cb = col >> 4;
             float val = 0.f;
             if (cb <= rb) val = t_block(L, rb, cb)[lr * (C + 1) + (col & 15)];
+            rbad |= !f16_ok(val);
             tv[i] = (_Float16)val;
         }
         *reinterpret_cast<half8*>(rec + kOffT + t * kTile + lane * 16) = tv;
@@ -538,10 +568,15 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
                 acc = mfma16x16x32(ta[kb], *reinterpret_cast<const half8*>(&L.u.bkT[16 * cb + lr][32 * kb + 8 * lg]),
                                    acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) L.o.W[16 * w + 4 * lg + i][16 * cb + lr] = (_Float16)acc[i];
+            for (int i = 0; i < 4; ++i) {
+                rbad |= !f16_ok(acc[i]);
+                L.o.W[16 * w + 4 * lg + i][16 * cb + lr] = (_Float16)acc[i];
+            }
         }
     }
+    if (rbad) L.range_bad = 1;  // benign race: every writer stores 1
     __syncthreads();
+    if (threadIdx.x == 0) *flag = (L.exact_diag ? kFlagExact : 0) | (L.range_bad ? kFlagRange : 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
         *reinterpret_cast<half8*>(rec + kOffW + (w * 4 + ks) * kTile + lane * 16) =
@@ -564,7 +599,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm, 
 }
 
 // Second pass: workgroup b reads the flags of units 64b .. 64b + 63 (unit = slot * H + head) and
-// redoes the flagged ones in turn.  A flag of a slot that no chunk uses is never written and
+// redoes the ones flagged for exact diagonal tiles in turn (each rewrites its own flag word).  A flag of a slot that no chunk uses is never written and
 // may hold anything; such a unit returns at once.
 template <bool PRO>
 __global__ __launch_bounds__(256, 2) void prep_exact_kernel(PrefillArgs a, SeqMap sm, int32_t* exact_flags,
@@ -572,7 +607,7 @@ __global__ __launch_bounds__(256, 2) void prep_exact_kernel(PrefillArgs a, SeqMa
     __shared__ PrepLds L;
     const int64_t u0 = (int64_t)blockIdx.x * 64;
     const int64_t u = u0 + (threadIdx.x & 63);
-    const bool set = u < units && exact_flags[u] != 0;
+    const bool set = u < units && (exact_flags[u] & kFlagExact) != 0;
     uint64_t todo = __ballot(set);  // the same mask in every wave
     while (todo) {
         const int bit = __builtin_ctzll(todo);
@@ -689,6 +724,7 @@ struct StateLds {
     alignas(16) float gam[2][DK];            // gamma, double-buffered by chunk parity
     alignas(16) float Ost[4][16][20];        // per-wave output tile, transposed to token rows
     alignas(16) float warm_dummy[64];        // sink of the L2 warm-up loads (never read)
+    int bad[8];                              // per wave: met a value beyond the fp16 range
 };
 
 // v, beta and gamma of one chunk as loaded by the staging wave: lane l covers token
@@ -698,13 +734,14 @@ struct StageRegs {
     u32x4 v[2];
     uint32_t b[2];
     uint32_t g[2];
+    uint32_t f;  // the chunk's prep flag word (half 0)
 };
 
 // Token half J (tokens 32 J .. 32 J + 31) of a chunk's staging; half 0 also takes gamma.
 template <int J>
 __device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* v, const uint16_t* beta,
-                                           const unsigned char* rec, int64_t t0, int Lc, int H, int h, int vb,
-                                           int lane) {
+                                           const unsigned char* rec, const int32_t* flag, int64_t t0, int Lc, int H,
+                                           int h, int vb, int lane) {
     const int64_t rowv = (int64_t)H * DV;
     const __amdgpu_buffer_rsrc_t vrs =
         make_rsrc(v + (t0 * H + h) * (int64_t)DV + vb * BV, (uint32_t)(((Lc - 1) * rowv + BV) * 2));
@@ -716,23 +753,32 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* v, cons
         const __amdgpu_buffer_rsrc_t grs = make_rsrc(rec + kOffGamma, DK * 4);
         r.g[0] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8, 0, 0);
         r.g[1] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8 + 4, 0, 0);
+        r.f = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(flag, 4), 0, 0, 0);
     }
 }
 
+// Also records in the wave's flag slot a beta*V value beyond the fp16 range, or (half 0) a
+// prep flag of the chunk that says so of one of its operands.
 template <int J>
-__device__ __forceinline__ void stage_store(StateLds& L, int buf, const StageRegs& r, int lane, bool beta_logits) {
+__device__ __forceinline__ void stage_store(StateLds& L, int buf, const StageRegs& r, int w, int lane,
+                                            bool beta_logits) {
     const int tok = 32 * J + (lane >> 1);
     const float bt = beta_logits ? sigmoid(bf((uint16_t)r.b[J])) : bf((uint16_t)r.b[J]);
     const uint32_t words[4] = {r.v[J].x, r.v[J].y, r.v[J].z, r.v[J].w};
+    bool bad = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const uint16_t bits = (uint16_t)((e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFF));
-        L.BVs[buf][8 * (lane & 1) + e][tok] = (_Float16)(bt * bf(bits));
+        const float x = bt * bf(bits);
+        bad |= !f16_ok(x);
+        L.BVs[buf][8 * (lane & 1) + e][tok] = (_Float16)x;
     }
     if (J == 0) {
         L.gam[buf][2 * lane] = __uint_as_float(r.g[0]);
         L.gam[buf][2 * lane + 1] = __uint_as_float(r.g[1]);
+        bad |= (r.f & kFlagRange) != 0;
     }
+    if (bad) L.bad[w] = 1;  // benign race: every writer stores 1
 }
 
 // Output rows of one chunk: the accumulator tile (lane = column, 4 rows) goes through LDS so
@@ -755,6 +801,7 @@ __device__ __forceinline__ void store_o(StateLds& L, floatx4 O, float* obase, in
 __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cur, ChunkFrags& nxt,
                                                const unsigned char* nrec, bool has_next, int buf, floatx4 (&Sf)[2],
                                                int w, int lane) {
+    bool bad = false;
     const int lr = lane & 15, lg = lane >> 4;
     const __amdgpu_buffer_rsrc_t nr = make_rsrc(nrec, kRecord);  // a valid record even when !has_next
     if (has_next) load_group(nxt, nr, 0, w, lane);
@@ -779,7 +826,11 @@ __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cu
     __builtin_amdgcn_sched_barrier(0);
     half4 dh;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dh[i] = (_Float16)(U[i] - X[i]);
+    for (int i = 0; i < 4; ++i) {
+        const float d = U[i] - X[i];
+        bad |= !f16_ok(d);
+        dh[i] = (_Float16)d;
+    }
     *reinterpret_cast<half4*>(&L.D[lr][16 * w + 4 * lg]) = dh;
     lds_barrier();
 
@@ -799,13 +850,17 @@ __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cu
         Sf[t] = acc;
         half4 hv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = (_Float16)acc[i];
+        for (int i = 0; i < 4; ++i) {
+            bad |= !f16_ok(acc[i]);
+            hv[i] = (_Float16)acc[i];
+        }
         *reinterpret_cast<half4*>(&L.S[lr][16 * (2 * w + t) + 4 * lg]) = hv;
     }
     // O = Q+ S0 + M D
     floatx4 O = Y;
     O = mfma16x16x32(cur.mm[0], db[0], O);
     if (w >= 2) O = mfma16x16x32(cur.mm[1], db[1], O);
+    if (bad) L.bad[w] = 1;  // benign race: every writer stores 1
     lds_barrier();
     return O;
 }
@@ -816,12 +871,18 @@ __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cu
 // staging loads stay out of the compute waves' counters.
 constexpr int kStateThreads = 384;
 
-__global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, SeqMap sm) {
+// uflags: prep's flag word per (slot, head); redo: one word per chain (sequence, head, value
+// block), set to 1 when the chain met a value beyond the fp16 range (its final state is then not
+// written, so that an in-place state_in survives for the fp32 redo), else 0.
+__global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, SeqMap sm, const int32_t* uflags,
+                                                              int32_t* redo) {
     __shared__ StateLds L;
     // wave index, wave-uniform (readfirstlane lets the compiler keep it in a scalar register)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int H = a.H;
+    // this wave's fp16-range flag; every later write of 1 follows it in the wave's program order
+    if (lane == 0) L.bad[w] = 0;
 
     // workgroup -> (sequence, head, value block); the 8 value blocks of a (sequence, head)
     // land on one XCD (workgroups are dealt to the 8 XCDs round-robin) so they share its L2
@@ -848,6 +909,7 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
     const int64_t sbase = nh * (int64_t)DK * DV + vb * BV;
     const unsigned char* ws = static_cast<const unsigned char*>(a.ws);
     auto rec_of = [&](int64_t c) { return ws + ((slot0 + c) * H + h) * (int64_t)kRecord; };
+    auto flag_of = [&](int64_t c) { return uflags + (slot0 + c) * H + h; };
     auto len_of = [&](int64_t c) {
         const int64_t t = eos - (bos + c * C);
         return (int)(t < C ? t : C);
@@ -869,23 +931,25 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
             if (warm)
                 for (int64_t c = 1; c <= kWarmAhead && c < nchunks; ++c) warm_l2(rec_of(c), vb, lane, dummy);
             if (nchunks > 0) {
-                stage_load<J>(ra, v, beta, rec_of(0), bos, len_of(0), H, h, vb, lane);
-                stage_store<J>(L, 0, ra, lane, a.prologue);
+                stage_load<J>(ra, v, beta, rec_of(0), flag_of(0), bos, len_of(0), H, h, vb, lane);
+                stage_store<J>(L, 0, ra, w, lane, a.prologue);
             }
-            if (nchunks > 1) stage_load<J>(rb, v, beta, rec_of(1), bos + C, len_of(1), H, h, vb, lane);
+            if (nchunks > 1) stage_load<J>(rb, v, beta, rec_of(1), flag_of(1), bos + C, len_of(1), H, h, vb, lane);
             lds_barrier();
             for (int64_t c = 0; c < nchunks; c += 2) {
                 lds_barrier();
-                if (c + 1 < nchunks) stage_store<J>(L, 1, rb, lane, a.prologue);
+                if (c + 1 < nchunks) stage_store<J>(L, 1, rb, w, lane, a.prologue);
                 if (c + 2 < nchunks)
-                    stage_load<J>(ra, v, beta, rec_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h, vb, lane);
+                    stage_load<J>(ra, v, beta, rec_of(c + 2), flag_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h,
+                                  vb, lane);
                 if (warm && c + 1 + kWarmAhead < nchunks) warm_l2(rec_of(c + 1 + kWarmAhead), vb, lane, dummy);
                 lds_barrier();
                 if (c + 1 >= nchunks) break;
                 lds_barrier();
-                if (c + 2 < nchunks) stage_store<J>(L, 0, ra, lane, a.prologue);
+                if (c + 2 < nchunks) stage_store<J>(L, 0, ra, w, lane, a.prologue);
                 if (c + 3 < nchunks)
-                    stage_load<J>(rb, v, beta, rec_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h, vb, lane);
+                    stage_load<J>(rb, v, beta, rec_of(c + 3), flag_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h,
+                                  vb, lane);
                 if (warm && c + 2 + kWarmAhead < nchunks) warm_l2(rec_of(c + 2 + kWarmAhead), vb, lane, dummy);
                 lds_barrier();
             }
@@ -904,13 +968,18 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
 #pragma unroll
             for (int i = 0; i < 4; ++i) Sf[t][i] = a.s0[sbase + (int64_t)(16 * (2 * w + t) + 4 * lg + i) * DV + lr];
     }
+    bool s0bad = false;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         half4 hv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = (_Float16)Sf[t][i];
+        for (int i = 0; i < 4; ++i) {
+            s0bad |= !f16_ok(Sf[t][i]);
+            hv[i] = (_Float16)Sf[t][i];
+        }
         *reinterpret_cast<half4*>(&L.S[lr][16 * (2 * w + t) + 4 * lg]) = hv;
     }
+    if (s0bad) L.bad[w] = 1;  // benign race: every writer stores 1
 
     // Two chunks per iteration with alternating operand registers: chunk c reads fa and loads
     // chunk c+1 into fb, chunk c+1 reads fb and loads chunk c+2 into fa, so no registers are
@@ -953,6 +1022,12 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
     }
     if (nchunks > 0) store_o(L, Oprev, obase0 + (nchunks - 1) * ostep, len_of(nchunks - 1), H, w, lane);
 
+    // Every wave wrote its flag slot before the last barrier it took part in (the helper waves'
+    // last staging precedes the last chunk's barriers), so the slots are final here.  A chain
+    // that met a value beyond the fp16 range leaves its final state to the fp32 redo.
+    const bool any_bad = (L.bad[0] | L.bad[1] | L.bad[2] | L.bad[3] | L.bad[4] | L.bad[5]) != 0;
+    if (w == 0 && lane == 0) redo[nh * NVB + vb] = any_bad ? 1 : 0;
+    if (any_bad) return;
     if (a.sT) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -981,11 +1056,15 @@ bool chunk_mfma_supported(int bf16, int dk, int dv, int chunk) {
     return bf16 && dk == DK && dv == DV && chunk == C;
 }
 
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Workspace layout: the records (one per slot and head), one prep flag word per record, one redo
+// word per state chain (sequence, head, value block); each part rounded up to 256 bytes.
 size_t chunk_mfma_workspace(int64_t N, int64_t T_fixed, int64_t T_total, bool fixed, int H, int chunk) {
     (void)chunk;
     const size_t units = (size_t)num_slots(N, T_fixed, T_total, fixed) * (size_t)H;
-    // the records, then one flag word per record (rounded up to 256 bytes)
-    return units * (size_t)kRecord + ((units * sizeof(int32_t) + 255) / 256) * 256;
+    return units * (size_t)kRecord + round256(units * sizeof(int32_t)) +
+           round256((size_t)N * (size_t)H * NVB * sizeof(int32_t));
 }
 
 hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
@@ -996,10 +1075,11 @@ hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
     // (sequence, head)
     if (slots * (int64_t)a.H > INT32_MAX || a.N * (int64_t)a.H * NVB > INT32_MAX) return hipErrorInvalidConfiguration;
     const bool timed = timing_on();
+    const int64_t units = slots * (int64_t)a.H;
+    int32_t* flags = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) + units * kRecord);
+    int32_t* redo = reinterpret_cast<int32_t*>(reinterpret_cast<unsigned char*>(flags) +
+                                               round256((size_t)units * sizeof(int32_t)));
     if (slots > 0 && a.T_total > 0) {
-        int32_t* flags = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) +
-                                                    slots * (int64_t)a.H * kRecord);
-        const int64_t units = slots * (int64_t)a.H;
         const dim3 grid((unsigned)units);
         const dim3 grid2((unsigned)((units + 63) / 64));
         if (timed) timed_begin(kKernelPrep, s);
@@ -1016,10 +1096,19 @@ hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
         if (timed) timed_end(s);
     }
     if (timed) timed_begin(kKernelState, s);
-    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(a.N * a.H * NVB)), dim3(kStateThreads), 0, s, a, sm);
+    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(a.N * a.H * NVB)), dim3(kStateThreads), 0, s, a, sm, flags,
+                       redo);
     hipError_t e = hipGetLastError();
     if (timed) timed_end(s);
-    return e;
+    if (e != hipSuccess) return e;
+    // the chains that met a value beyond the fp16 range, recomputed in fp32 (64-token chunks as
+    // two 32-token ones, so snapshots fall every 2 * snap_every of them); the other chains'
+    // workgroups return at once
+    PrefillArgs r = a;
+    r.chunk = 32;
+    r.snap_every = a.snap_every * 2;
+    r.redo = redo;
+    return launch_chunk_f32(r, s);
 }
 
 }  // namespace kda

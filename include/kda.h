@@ -25,23 +25,40 @@
  *     every other pointer its element size.
  *   - q, k, v and beta have the storage type `dtype` (KDA_F32: float,
  *     KDA_BF16: bfloat16).  g = log(alpha) is always float (fp32, values <= 0
- *     expected, not checked), states and outputs are always float.
+ *     expected), states and outputs are always float.
  *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
- *     stream).  The library never synchronises (unless KDA_DEBUG_SYNC=1 is set
- *     in the environment), never allocates or frees device memory, and keeps
- *     no pointer after returning.  The caller keeps every buffer alive until
- *     the stream has drained.
+ *     stream).  The library never synchronises (unless KDA_DEBUG_SYNC=1 or
+ *     KDA_DEBUG_CHECK=1 is set in the environment), never allocates or frees
+ *     device memory, and keeps no pointer after returning.  The caller keeps
+ *     every buffer alive until the stream has drained.
  *   - Return value: KDA_OK or a negative kda_status.  Arguments are validated
  *     on the host before any device work; a failed call launches nothing.
- *     Device-resident data (cu_seqlens contents, gate ranges, NaN/Inf) is not
- *     inspected.  kda_last_error() gives a message for the calling thread.
- *   - bfloat16 path numerics: products inside a chunk use fp16 matrix-core
- *     operands with fp32 accumulation; the state, the decays and all outputs are
- *     fp32.  Values of v, of the state and of the intermediate corrections must
- *     stay within fp16 range (|x| < 6e4).  Decays of any strength are exact up
- *     to rounding: a chunk in which some channel decays by more than e^10 over 8
- *     tokens sums its diagonal 16x16 Gram tiles in fp32 with one exponential per
- *     token pair, which costs that chunk extra time.  The fp32 path has no such
+ *     kda_last_error() gives a message for the calling thread.
+ *   - Device-resident data (cu_seqlens and snapshot_cu contents, gate ranges)
+ *     is a caller contract and is not inspected by default.  With
+ *     KDA_DEBUG_CHECK=1 in the environment every call first waits for its
+ *     stream, copies those arrays to the host and checks them with the
+ *     kda_validate_* functions below (cu_seqlens: cu[0] = 0, non-decreasing,
+ *     cu[N] = T_total; snapshot_cu: consistent with cu_seqlens; g finite and
+ *     <= 0, beta in [0, 1]; with the fused prologue, g and beta finite).  A
+ *     violation returns KDA_ERR_INVALID_ARG before any launch.  Without the
+ *     check, offsets that break the contract make the kernels read and write
+ *     outside the caller's buffers.
+ *   - bfloat16 path numerics (d_k = d_v = 128, chunk 64): products inside a
+ *     chunk use fp16 matrix-core operands with fp32 accumulation; the state,
+ *     the decays and all outputs are fp32.  Every value rounded to an fp16
+ *     operand is first checked against the fp16 range (|x| < 65504; NaN and
+ *     Inf fail too): q and k entries (which must not exceed 32768; unit-length
+ *     q and k, as the DeltaNet family uses them, are far inside), the gated
+ *     Gram matrix M, the UT transform T and the WY factor W per chunk, and
+ *     beta*v, the per-token corrections and the state per chain.  A (sequence,
+ *     head, 16-column value block) chain that meets a value outside the range
+ *     is recomputed by the fp32 chunked kernel in the same call (same results
+ *     to the fp32 tolerance, at that kernel's speed), so there is no range
+ *     limit beyond fp32's.  Decays of any strength are exact up to rounding: a
+ *     chunk in which some channel decays by more than e^10 over 8 tokens sums
+ *     its diagonal 16x16 Gram tiles in fp32 with one exponential per token
+ *     pair, which costs that chunk extra time.  The fp32 path has no such
  *     limits.
  */
 #ifndef KDA_H_
@@ -80,7 +97,8 @@ typedef enum { KDA_OP_PREFILL = 0, KDA_OP_APPEND = 1, KDA_OP_DECODE = 2, KDA_OP_
  *              must not partially overlap it
  *   chunk      tokens per chunk: 16, 32 or 64 (64 for the bfloat16 d=128 path)
  *   workspace  device scratch of at least kda_workspace_size(KDA_OP_PREFILL, B, T, ...)
- *              bytes (NULL allowed when that size is 0); contents need no
+ *              bytes (NULL allowed when that size is 0), 256-byte aligned,
+ *              overlapping no other argument (KDA_ERR_ALIAS); contents need no
  *              initialisation and are clobbered.
  * T = 0 copies state_in to state_out (zeros when state_in is NULL).
  */
@@ -95,7 +113,8 @@ int kda_prefill_chunked(const void* q, const void* k, const void* v, const float
  * top of a kept history).
  *   q, k, g    [T_total, H, d_k]; v [T_total, H, d_v]; beta [T_total, H]
  *   cu_seqlens DEVICE int32 [N + 1]: cu[0] = 0, non-decreasing, cu[N] = T_total
- *              (segment n is tokens cu[n] .. cu[n+1]-1; not checked on device)
+ *              (segment n is tokens cu[n] .. cu[n+1]-1; checked only with
+ *              KDA_DEBUG_CHECK=1, see Conventions)
  *   state_in   [N, H, d_k, d_v] float or NULL (zeros); state_out as in prefill
  *   out        [T_total, H, d_v] float
  * Empty segments pass their state through unchanged.
@@ -224,6 +243,28 @@ int kda_chunked_backward(const void* q, const void* k, const void* v, const floa
                          float* dg, float* dbeta, float* d_state_in, int32_t H, int32_t d_k, int32_t d_v,
                          int32_t dtype, int32_t chunk, void* workspace, size_t workspace_bytes,
                          const kda_options* options, void* hip_stream);
+
+/*
+ * Host-side validators of the device-resident contract (the checks that
+ * KDA_DEBUG_CHECK=1 applies to a call's data after copying it to the host).
+ * Every pointer here is a HOST pointer; nothing is launched.  Each returns
+ * KDA_OK, or KDA_ERR_INVALID_ARG with a message in kda_last_error().
+ *   kda_validate_cu_seqlens   cu [N + 1]: cu[0] = 0, cu[n] <= cu[n+1],
+ *                             cu[N] = T_total (the append-prefill layout).
+ *   kda_validate_snapshot_cu  snapshot_cu [N + 1]: snapshot_cu[0] = 0 and
+ *                             snapshot_cu[n+1] - snapshot_cu[n] =
+ *                             (cu[n+1] - cu[n]) / (snapshot_every * chunk).
+ *   kda_validate_gates        g [n_g] finite and <= 0 (alpha = exp(g) in
+ *                             (0, 1]); beta [n_beta] finite and in [0, 1]
+ *                             ("Kimi K3, explained", "How Kimi Delta
+ *                             Attention works, step by step": both gates lie
+ *                             in (0, 1)).  raw = 1 (fused prologue inputs):
+ *                             finite only.  beta is given as float.
+ */
+int kda_validate_cu_seqlens(const int32_t* cu, int32_t N, int64_t T_total);
+int kda_validate_snapshot_cu(const int32_t* cu, const int32_t* snapshot_cu, int32_t N, int32_t snapshot_every,
+                             int32_t chunk);
+int kda_validate_gates(const float* g, int64_t n_g, const float* beta, int64_t n_beta, int32_t raw);
 
 /* Workspace bytes an op needs (B_or_N sequences, T tokens per sequence for
  * KDA_OP_PREFILL or T_total for KDA_OP_APPEND and KDA_OP_BACKWARD).  0 for

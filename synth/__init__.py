@@ -138,6 +138,7 @@ class Workload:
     s0_std: float = 0.0  # 0 -> no initial state (zeros)
     gate: Gate = field(default_factory=Gate)
     q_unit: bool = True
+    v_std: float = 1.0  # v ~ N(0, v_std^2)
     decode_steps: int = 0
     decode_N: int = 0
 
@@ -152,7 +153,7 @@ def gen_tokens(w: Workload, T: int, *, offset_tokens: int = 0, q_unit: bool | No
     else:
         q = fill(K_NORMAL, w.seed, TID_Q, (T, H, dk), dt, offset=off_k, p0=1.0, threads=threads)
     k = fill(K_UNIT_ROWS, w.seed, TID_K, (T, H, dk), dt, offset=off_k, row_len=dk, threads=threads)
-    v = fill(K_NORMAL, w.seed, TID_V, (T, H, dv), dt, offset=off_v, p0=1.0, threads=threads)
+    v = fill(K_NORMAL, w.seed, TID_V, (T, H, dv), dt, offset=off_v, p0=w.v_std, threads=threads)
     beta = fill(K_SIGMOID_NORMAL, w.seed, TID_BETA, (T, H), dt, offset=off_h, threads=threads)
     if w.gate.kind == "softplus":
         g = fill(K_LOGDECAY_SOFTPLUS, w.seed, TID_G, (T, H, dk), "f32", offset=off_k, p0=w.gate.scale,

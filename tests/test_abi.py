@@ -43,7 +43,9 @@ def test_supported_and_workspace():
     assert L.kda_is_supported(2, 1, 128, 128, 0) == 1
     assert L.kda_workspace_size(2, 4, 0, 32, 128, 128, 1, 64) == 0
     ws = L.kda_workspace_size(0, 1, 8192, 32, 128, 128, 1, 64)
-    assert ws == 128 * 32 * 66048 + 128 * 32 * 4  # records, then one flag word per record
+    # records, one flag word per record, one redo word per (sequence, head, 16-column block),
+    # each part rounded up to 256 bytes
+    assert ws == 128 * 32 * 66048 + 128 * 32 * 4 + 1 * 32 * 8 * 4
     assert L.kda_workspace_size(0, 1, 8192, 32, 96, 128, 1, 64) == 2 ** 64 - 1
 
 
@@ -181,3 +183,86 @@ def test_backward_call_is_validated():
     assert call(opts=snap) == _l.KDA_ERR_UNSUPPORTED and b"snapshots" in L.kda_last_error()
     pro = ctypes.byref(_l.Options(0, 0, None, None, 1, 1.0))
     assert call(opts=pro) == _l.KDA_ERR_UNSUPPORTED
+
+
+def test_workspace_may_not_overlap_arguments():
+    """Prefill and append reject a workspace that overlaps an input or an output (the prep pass
+    writes its records while other workgroups still read the inputs)."""
+    _l, L = _lib()
+    base = 1 << 40
+    p = [base + i * (1 << 30) for i in range(12)]  # valid, non-overlapping fake buffers
+    B, T, H, d, C = 1, 64, 2, 128, 64
+    need = L.kda_workspace_size(_l.KDA_OP_PREFILL, B, T, H, d, d, _l.KDA_BF16, C)
+    need_a = L.kda_workspace_size(_l.KDA_OP_APPEND, 1, T, H, d, d, _l.KDA_BF16, C)
+    assert need > 0 and need_a > 0
+
+    def prefill(ws, s_in=None, s_out=None):
+        return L.kda_prefill_chunked(p[0], p[1], p[2], p[3], p[4], s_in, p[5], s_out, B, T, H, d, d, _l.KDA_BF16, C,
+                                     ws, need, None)
+
+    def append(ws, s_in=None, s_out=None):
+        return L.kda_append_prefill(p[0], p[1], p[2], p[3], p[4], p[6], 1, T, s_in, p[5], s_out, H, d, d,
+                                    _l.KDA_BF16, C, ws, need_a, None)
+
+    for call in (prefill, append):
+        assert call(p[0]) == _l.KDA_ERR_ALIAS and b"workspace" in L.kda_last_error()  # on q
+        assert call(p[3] + 256) == _l.KDA_ERR_ALIAS  # inside g
+        assert call(p[5]) == _l.KDA_ERR_ALIAS  # on out
+        assert call(p[8], s_in=p[7], s_out=p[8]) == _l.KDA_ERR_ALIAS  # on state_out
+        assert call(p[7], s_in=p[7]) == _l.KDA_ERR_ALIAS  # on state_in
+    assert append(p[6]) == _l.KDA_ERR_ALIAS  # on cu_seqlens
+    assert prefill(p[0] - need + 256) == _l.KDA_ERR_ALIAS  # ends inside q
+
+
+def test_host_validators_reject_malformed_offsets_and_gates():
+    """kda_validate_*: the checks KDA_DEBUG_CHECK=1 applies to device-resident data, on host arrays."""
+    import numpy as np
+
+    _l, L = _lib()
+
+    def cu_ok(cu, T):
+        a = np.ascontiguousarray(cu, dtype=np.int32)
+        return L.kda_validate_cu_seqlens(a.ctypes.data, len(a) - 1, T)
+
+    assert cu_ok([0, 5, 5, 12], 12) == 0
+    assert cu_ok([0], 0) == 0
+    assert cu_ok([1, 5, 12], 12) == _l.KDA_ERR_INVALID_ARG and b"[0]" in L.kda_last_error()
+    assert cu_ok([0, 7, 5, 12], 12) == _l.KDA_ERR_INVALID_ARG and b"decreases" in L.kda_last_error()
+    assert cu_ok([0, 5, 11], 12) == _l.KDA_ERR_INVALID_ARG and b"T_total" in L.kda_last_error()
+    assert cu_ok([0, 5, 13], 12) == _l.KDA_ERR_INVALID_ARG
+    assert L.kda_validate_cu_seqlens(None, 1, 0) == _l.KDA_ERR_INVALID_ARG
+
+    def snap_ok(cu, scu, every, chunk):
+        a = np.ascontiguousarray(cu, dtype=np.int32)
+        b = np.ascontiguousarray(scu, dtype=np.int32)
+        return L.kda_validate_snapshot_cu(a.ctypes.data, b.ctypes.data, len(a) - 1, every, chunk)
+
+    cu = [0, 200, 200, 263]  # lengths 200, 0, 63 with snapshots every 64 tokens: 3, 0, 0
+    assert snap_ok(cu, [0, 3, 3, 3], 1, 64) == 0
+    assert snap_ok(cu, [0, 3, 3, 4], 1, 64) == _l.KDA_ERR_INVALID_ARG
+    assert snap_ok(cu, [1, 4, 4, 4], 1, 64) == _l.KDA_ERR_INVALID_ARG
+    assert snap_ok(cu, [0, 1, 1, 1], 2, 64) == 0  # every 128 tokens: 1, 0, 0
+
+    def gates_ok(g, b, raw=0):
+        ga = np.ascontiguousarray(g, dtype=np.float32)
+        ba = np.ascontiguousarray(b, dtype=np.float32)
+        return L.kda_validate_gates(ga.ctypes.data, ga.size, ba.ctypes.data, ba.size, raw)
+
+    assert gates_ok([0.0, -0.1, -30.0], [0.0, 0.5, 1.0]) == 0
+    assert gates_ok([0.0, 0.25], [0.5]) == _l.KDA_ERR_INVALID_ARG and b"g[1]" in L.kda_last_error()
+    assert gates_ok([-np.inf], [0.5]) == _l.KDA_ERR_INVALID_ARG
+    assert gates_ok([np.nan], [0.5]) == _l.KDA_ERR_INVALID_ARG
+    assert gates_ok([-1.0], [1.5]) == _l.KDA_ERR_INVALID_ARG and b"beta[0]" in L.kda_last_error()
+    assert gates_ok([-1.0], [-0.01]) == _l.KDA_ERR_INVALID_ARG
+    assert gates_ok([2.0, -3.0], [-4.0, 7.0], raw=1) == 0  # raw prologue inputs: any finite value
+    assert gates_ok([np.inf], [0.0], raw=1) == _l.KDA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_a_host_workspace():
+    """The binding checks a caller's workspace like every other tensor before passing its pointer."""
+    import torch
+
+    import gated_delta_rule_75_amd as kda
+
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda._workspace(1024, torch.device("cuda:0"), torch.empty(4096, dtype=torch.uint8))

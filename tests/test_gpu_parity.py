@@ -317,8 +317,9 @@ def test_snapshots_match_oracle(dtype, d, chunk, every):
     assert_close(host(snaps).reshape(-1, 2, d, d), sref, TOL[dtype], None, "prefill snapshots")
     _, sTref, srefa = oracle.recurrence(*widea, cu, s0a, snapshot_every=E)
     assert list(snap_cu.cpu().numpy()) == list(np.concatenate([[0], np.cumsum([n // E for n in lens])]))
-    assert snapsa.shape[0] == srefa.shape[0] == 3 + 0 + 0 + 1 + 1
-    assert_close(host(snapsa), srefa, TOL[dtype], None, "append snapshots")
+    assert srefa.shape[0] == 3 + 0 + 0 + 1 + 1
+    assert snapsa.shape[0] == Ta // E >= srefa.shape[0]  # an upper bound: the rows are counted on the device
+    assert_close(host(snapsa[:srefa.shape[0]]), srefa, TOL[dtype], None, "append snapshots")
     assert_close(host(sTa), sTref, TOL[dtype], None, "append S_T")
 
 
