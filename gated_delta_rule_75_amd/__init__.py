@@ -164,7 +164,8 @@ def prefill_chunked(q, k, v, g, beta, state=None, *, chunk=64, out=None, state_o
 
 
 def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=None, state_out=None,
-                   final_state=True, workspace=None, snapshot_every=0, snapshots=None, prologue_gate_scale=None):
+                   final_state=True, workspace=None, snapshot_every=0, snapshots=None, prologue_gate_scale=None,
+                   no_alloc=False):
     """Append-prefill of N packed segments (token-major [T_total, H, d]) on carried states.
 
     cu_seqlens: int32 GPU tensor [N+1] (0, ..., T_total).  g [T_total,H,dk] or [T_total,H] (one
@@ -174,7 +175,11 @@ def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=No
     snapshot_every chunks of each segment, segment n at rows snapshot_cu[n] .. snapshot_cu[n+1]-1.
     snapshot_cu is computed on the device (no host synchronisation), so the row count is not
     known here: snapshots (given, or allocated) has R = T_total // (snapshot_every * chunk) rows,
-    an upper bound of snapshot_cu[N]; rows from snapshot_cu[N] on are not written."""
+    an upper bound of snapshot_cu[N]; rows from snapshot_cu[N] on are not written.
+
+    no_alloc=True calls kda_append_prefill_noalloc: the library's fixed device scratch replaces
+    the workspace (no workspace argument; calls needing more than KDA_NOALLOC_SCRATCH_BYTES of
+    scratch raise).  Outputs not given are still allocated here."""
     T, H, dk = q.shape
     dv = v.shape[-1]
     N = cu_seqlens.numel() - 1
@@ -210,14 +215,22 @@ def append_prefill(q, k, v, g, beta, cu_seqlens, state=None, *, chunk=64, out=No
     if state_out is None and final_state:
         state_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(state_out, "state_out", torch.float32, (N, H, dk, dv), dev)
+    L = _lib.load()
+    opts = _options(gate, snapshot_every, snapshots, snapshot_cu, prologue_gate_scale)
+    if no_alloc:
+        if workspace is not None:
+            raise ValueError("no_alloc takes no workspace")
+        _lib.check(L.kda_append_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+                                                _ptr(state), _ptr(out), _ptr(state_out), H, dk, dv, _DT[dt], chunk,
+                                                opts, _stream(dev)))
+        if snapshot_every > 0:
+            return out, state_out, snapshots, snapshot_cu
+        return out, state_out
     ws_bytes = workspace_size(_lib.KDA_OP_APPEND, N, T, H, dk, dv, dt, chunk)
     ws = _workspace(ws_bytes, dev, workspace)
-    L = _lib.load()
     _lib.check(L.kda_append_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
                                        _ptr(state), _ptr(out), _ptr(state_out), H, dk, dv, _DT[dt], chunk,
-                                       _ptr(ws), ws_bytes,
-                                       _options(gate, snapshot_every, snapshots, snapshot_cu, prologue_gate_scale),
-                                       _stream(dev)))
+                                       _ptr(ws), ws_bytes, opts, _stream(dev)))
     if snapshot_every > 0:
         return out, state_out, snapshots, snapshot_cu
     return out, state_out

@@ -18,10 +18,11 @@ KDA_ERR_ALIAS, KDA_ERR_WORKSPACE, KDA_ERR_HIP = -4, -5, -6
 KDA_F32, KDA_BF16 = 0, 1
 KDA_OP_PREFILL, KDA_OP_APPEND, KDA_OP_DECODE, KDA_OP_BACKWARD = 0, 1, 2, 3
 KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
+KDA_NOALLOC_SCRATCH_BYTES = 128 << 20  # the fixed device scratch of kda_append_prefill_noalloc
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_prefill_chunked", "kda_append_prefill", "kda_decode_step", "kda_prefill_chunked_ex",
-           "kda_append_prefill_ex", "kda_decode_step_ex", "kda_chunked_backward", "kda_workspace_size",
+           "kda_append_prefill_ex", "kda_decode_step_ex", "kda_append_prefill_noalloc", "kda_chunked_backward", "kda_workspace_size",
            "kda_is_supported", "kda_validate_cu_seqlens", "kda_validate_snapshot_cu", "kda_validate_gates",
            "kda_status_string", "kda_last_error", "kda_version", "kda_timing_begin", "kda_timing_end")
 KERNEL_NAMES = {1: "kda_prep", 2: "kda_state", 3: "kda_chunk_f32", 4: "kda_decode", 5: "kda_bwd_factors",
@@ -64,6 +65,8 @@ def load():
     L.kda_append_prefill_ex.argtypes = L.kda_append_prefill.argtypes[:-1] + [op, vp]
     L.kda_decode_step_ex.restype = ctypes.c_int
     L.kda_decode_step_ex.argtypes = L.kda_decode_step.argtypes[:-1] + [op, vp]
+    L.kda_append_prefill_noalloc.restype = ctypes.c_int
+    L.kda_append_prefill_noalloc.argtypes = L.kda_append_prefill.argtypes[:-3] + [op, vp]
     L.kda_workspace_size.restype = sz
     L.kda_chunked_backward.restype = ctypes.c_int
     L.kda_chunked_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,

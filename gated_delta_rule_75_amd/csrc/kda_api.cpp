@@ -416,11 +416,17 @@ int kda_prefill_chunked(const void* q, const void* k, const void* v, const float
                                   workspace, workspace_bytes, nullptr, hip_stream);
 }
 
-int kda_append_prefill_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,
-                          const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in, float* out,
-                          float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
-                          void* workspace, size_t workspace_bytes, const kda_options* options, void* hip_stream) {
-    static const char* name = "kda_append_prefill";
+}  // extern "C"
+
+namespace {
+
+// Append-prefill with a caller workspace (noalloc = false), or with the library's fixed device
+// scratch in place of one (noalloc = true: workspace must be NULL and 0).
+int append_impl(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in, float* out,
+                float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk, void* workspace,
+                size_t workspace_bytes, const kda_options* options, void* hip_stream, bool noalloc) {
+    const char* name = noalloc ? "kda_append_prefill_noalloc" : "kda_append_prefill";
     Opts op;
     if (int rc = read_options(options, KDA_OP_APPEND, name, op)) return rc;
     if (N < 0 || T_total < 0) return fail(KDA_ERR_INVALID_ARG, "%s: N and T_total must be >= 0", name);
@@ -450,15 +456,29 @@ int kda_append_prefill_ex(const void* q, const void* k, const void* v, const flo
     if (overlap(sin, sout) && state_in != state_out)
         return fail(KDA_ERR_ALIAS, "%s: state_out partially overlaps state_in", name);
     const size_t need = ws_size(KDA_OP_APPEND, N, T_total, H, d_k, d_v, dtype, chunk);
-    if (need && (!workspace || workspace_bytes < need))
-        return fail(KDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name, need,
-                    workspace ? workspace_bytes : (size_t)0);
-    const Span wsp{workspace, need};
-    for (const Span& in : ins)
-        if (overlap(wsp, in)) return fail(KDA_ERR_ALIAS, "%s: the workspace overlaps an input", name);
-    if (overlap(wsp, o) || overlap(wsp, sout) || overlap(wsp, snp))
-        return fail(KDA_ERR_ALIAS, "%s: the workspace overlaps out, state_out or snapshots", name);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (noalloc) {
+        // the library's own scratch; it overlaps no caller buffer
+        if (need > kda::noalloc_scratch_bytes())
+            return fail(KDA_ERR_WORKSPACE, "%s: this call needs %zu bytes of scratch, beyond the fixed maximum of %zu",
+                        name, need, kda::noalloc_scratch_bytes());
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need) {
+            hipError_t e = kda::noalloc_scratch(stream, &workspace);
+            if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: scratch address: %s", name, hipGetErrorString(e));
+            workspace_bytes = kda::noalloc_scratch_bytes();
+        }
+    } else {
+        if (need && (!workspace || workspace_bytes < need))
+            return fail(KDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        const Span wsp{workspace, need};
+        for (const Span& in : ins)
+            if (overlap(wsp, in)) return fail(KDA_ERR_ALIAS, "%s: the workspace overlaps an input", name);
+        if (overlap(wsp, o) || overlap(wsp, sout) || overlap(wsp, snp))
+            return fail(KDA_ERR_ALIAS, "%s: the workspace overlaps out, state_out or snapshots", name);
+    }
     if (debug_check()) {
         if (int rc = debug_check_offsets(cu_seqlens, N, T_total, op.snap_cu, op.every, chunk, stream, name)) return rc;
         if (int rc = debug_check_gates(g, tokens * H * (op.gate_head ? 1 : d_k), beta, tokens * H, dtype, op.prologue,
@@ -475,6 +495,26 @@ int kda_append_prefill_ex(const void* q, const void* k, const void* v, const flo
     a.snap_per_seq = 0;
     a.prologue = op.prologue; a.gate_scale = op.gate_scale;
     return run_prefill(a, dtype, stream, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_append_prefill_ex(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                          const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in, float* out,
+                          float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                          void* workspace, size_t workspace_bytes, const kda_options* options, void* hip_stream) {
+    return append_impl(q, k, v, g, beta, cu_seqlens, N, T_total, state_in, out, state_out, H, d_k, d_v, dtype, chunk,
+                       workspace, workspace_bytes, options, hip_stream, false);
+}
+
+int kda_append_prefill_noalloc(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                               const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in,
+                               float* out, float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                               int32_t chunk, const kda_options* options, void* hip_stream) {
+    return append_impl(q, k, v, g, beta, cu_seqlens, N, T_total, state_in, out, state_out, H, d_k, d_v, dtype, chunk,
+                       nullptr, 0, options, hip_stream, true);
 }
 
 int kda_append_prefill(const void* q, const void* k, const void* v, const float* g, const void* beta,

@@ -37,8 +37,11 @@
 // state in the state pass; a NaN or Inf fails the check too).  A (sequence, head, value
 // block) chain that meets such a value is not finished here: its final state is left
 // unwritten, and a third pass recomputes the whole chain with the fp32 chunked kernel.
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
+#include "kda.h"
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -1065,6 +1068,49 @@ size_t chunk_mfma_workspace(int64_t N, int64_t T_fixed, int64_t T_total, bool fi
     const size_t units = (size_t)num_slots(N, T_fixed, T_total, fixed) * (size_t)H;
     return units * (size_t)kRecord + round256(units * sizeof(int32_t)) +
            round256((size_t)N * (size_t)H * NVB * sizeof(int32_t));
+}
+
+// ------------------------------------------------------------------------------------------
+// Fixed scratch for the entry point that allocates nothing (kda_append_prefill_noalloc): the
+// records, flags and redo words of one call live in this array instead of a caller workspace.
+// Each GPU the library runs on holds its own copy from the code object's load until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it is a stand-in, not
+// a device address): it takes the per-device address from hipGetSymbolAddress once per device.
+// ------------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = KDA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+size_t noalloc_scratch_bytes() { return kScratchBytes; }
+
+hipError_t noalloc_scratch(hipStream_t s, void** out) {
+    static std::mutex mu;
+    static std::vector<void*> addr;  // per device, filled on the first call on that device
+    int dev = 0, cur = 0;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr.empty()) {
+        int n = 0;
+        if ((e = hipGetDeviceCount(&n)) != hipSuccess) return e;
+        addr.assign((size_t)n, nullptr);
+    }
+    if (dev < 0 || (size_t)dev >= addr.size()) return hipErrorInvalidDevice;
+    if (!addr[dev]) {
+        // the symbol's address on `dev`, with `dev` current
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {

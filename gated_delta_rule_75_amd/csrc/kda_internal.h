@@ -109,6 +109,10 @@ hipError_t launch_chunk_f32(const PrefillArgs& a, hipStream_t s);
 bool chunk_mfma_supported(int bf16, int dk, int dv, int chunk);
 size_t chunk_mfma_workspace(int64_t N, int64_t T_fixed, int64_t T_total, bool fixed, int H, int chunk);
 hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s);
+// the fixed device scratch of the entry point that allocates nothing: its size, and its address
+// on the device of stream s (resolved once per device)
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(hipStream_t s, void** out);
 
 // decode step
 bool decode_supported(int dk, int dv);

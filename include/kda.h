@@ -207,6 +207,37 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const float*
                        int32_t d_k, int32_t d_v, int32_t dtype, const kda_options* options, void* hip_stream);
 
 /*
+ * kda_append_prefill_noalloc — kda_append_prefill_ex without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results and errors as kda_append_prefill_ex with a workspace (the same
+ * kernels), except:
+ *   - The scratch the matrix-core path needs (kda_workspace_size(KDA_OP_APPEND,
+ *     ...) bytes) comes from a fixed array of KDA_NOALLOC_SCRATCH_BYTES bytes
+ *     in device memory that the library holds on each GPU it runs on, from
+ *     its first use there until the process ends.  A call that needs more
+ *     returns KDA_ERR_WORKSPACE before any launch; 128 MiB covers, e.g.,
+ *     H = 32 with T_total / 64 + N <= 62 (one segment of up to 3,904 tokens).
+ *     Shapes served by the fp32 kernel need no scratch.
+ *   - The call allocates and frees nothing (no hipMalloc, hipFree or
+ *     allocating library routine).  Its first call on a device looks up the
+ *     array's address on that device once (hipGetSymbolAddress).
+ *   - Every call on one GPU shares that GPU's array, which keeps the previous
+ *     call's contents (nothing in it needs clearing: every word a call reads
+ *     it has written first).  Calls that overlap in time on one GPU (several
+ *     streams, or several host threads) race on it: serialise them, e.g. on
+ *     one stream.
+ *   - KDA_DEBUG_CHECK=1 (see Conventions) synchronises and copies through host
+ *     memory, so it is for debugging only, not for the callers above.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+int kda_append_prefill_noalloc(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                               const int32_t* cu_seqlens, int32_t N, int64_t T_total, const float* state_in,
+                               float* out, float* state_out, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                               int32_t chunk, const kda_options* options, void* hip_stream);
+
+/*
  * kda_chunked_backward — gradients of the chunked prefill (training).
  *
  * "Kimi K3, explained" ("How is KDA trained efficiently if it is a
