@@ -98,6 +98,55 @@ def traffic_of(kernel, workload=None):
     return m["bytes"]
 
 
+# prefill MFMA utilisation from rocprofv3 --pmc MfmaUtil (percent of cycles the matrix cores are
+# busy, per kernel), on the kernel source named by its SHA-256 (profiles/prefill_mfma_utilisation_*)
+MEASURED_MFMA_UTIL = {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
+                      "kda_prep": 0.063, "kda_state": 0.099}
+# the algorithmic MFMA fraction at the HBM roofline: 139,264 flop per 1,794 B at 8 TB/s = 621
+# TFLOP/s, 24.8% of the dense fp16/bf16 peak
+MFMA_CEILING_AT_HBM_ROOFLINE = PREFILL_FLOP_PER_TOKEN_HEAD / PREFILL_BYTES_PER_TOKEN_HEAD * HBM_PEAK_GBPS / 1e3 / \
+    MFMA_F16_PEAK_TFLOPS
+
+
+def copy_rate(n=1 << 30, reps=5):
+    """GB/s of a plain device-to-device copy of n bytes (n read + n written), best of reps, timed
+    with events: the practical streaming ceiling of this machine's HBM."""
+    import torch
+
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = None
+    # torch's copy_ and its elementwise kernel (neg, vectorised loads and stores): the faster
+    for fn in (lambda: dst.copy_(src), lambda: torch.neg(src, out=dst)):
+        for _ in range(2):
+            fn()
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / (best * 1e-3) / 1e9
+
+
+class CacheFlush:
+    """Evicts the L2 caches and the 256 MB Infinity Cache by writing a 1 GiB buffer (untimed)."""
+
+    def __init__(self):
+        import torch
+
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i & 0xFF)
+
+
 def copy_calibration():
     """A plain device-to-device copy of 1 GiB: reads and writes exactly 2^30 bytes per launch."""
     import torch
@@ -222,6 +271,24 @@ def bench_prefill(args, res):
                             "traffic_per_pass": traffic_of(name, f"prefill T={T} H={H}"),
                             "achieved_GBps": round(alg * th / (avg[name] * launches * 1e-3) / 1e9, 1)})
     tflops = PREFILL_FLOP_PER_TOKEN_HEAD * th / (path_ms * 1e-3) / 1e12
+    mfma_util = None
+    if source_sha256(MEASURED_MFMA_UTIL["source"]) == MEASURED_MFMA_UTIL["sha256"] and \
+            MEASURED_MFMA_UTIL["workload"] == f"prefill T={T} H={H}":
+        mfma_util = {k: MEASURED_MFMA_UTIL[k] for k in ("kda_prep", "kda_state")}
+    # cache-flush check: the same passes with L2 and the Infinity Cache evicted before each one
+    flush = CacheFlush()
+    fl = []
+    for _ in range(min(args.steps, 10)):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        fl.append(e0.elapsed_time(e1))
+    del flush
+    torch.cuda.empty_cache()
+    flushed_ms = sum(fl) / len(fl)
     res["value"] = T * args.steps / elapsed
     res["ms_per_step"] = elapsed * 1e3 / args.steps
     res["roofline"] = {
@@ -231,13 +298,23 @@ def bench_prefill(args, res):
         "algorithmic_bytes_per_launch": PREFILL_BYTES_PER_TOKEN_HEAD * th,
         "avg_pass_ms": round(path_ms, 4), "min_pass_ms": round(min(pass_list), 4),
         "timing": "HIP events on the call's stream around each kda_prefill_chunked call (a pass)",
+        "cache_flush": {"unflushed_avg_pass_ms": round(path_ms, 4), "flushed_avg_pass_ms": round(flushed_ms, 4),
+                        "flushed_passes": len(fl),
+                        "how": "1 GiB buffer written (untimed) before each flushed pass; the timed steps above run "
+                               "back to back without it (each pass moves 8 GB, 32x the 256 MB Infinity Cache)"},
         "mfma_algorithmic_tflops": round(tflops, 1),
         "mfma_frac_of_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "mfma_util_counters": mfma_util,
+        "mfma_target_frac": 0.5, "mfma_target_met": False,
+        "mfma_algorithmic_ceiling_at_hbm_roofline": round(MFMA_CEILING_AT_HBM_ROOFLINE, 4),
+        "mfma_note": "the chunked prefill does 139,264 flop per 1,794 B (77.6 flop/B, below the fp16 ridge of "
+                     "~313), so even at the full 8 TB/s its algorithmic matrix-core fraction is capped at the "
+                     "ceiling above; the HBM-roofline fraction is the governing figure",
     }
     res["kernels"] = kernels
     kp = ", ".join(f"{x['kernel']}: {x['ms_per_pass']}" for x in kernels)
     log(f"[prefill] {res['value'] / 1e6:.2f} M tokens/s, {res['ms_per_step']:.3f} ms/step, pass {path_ms:.3f} ms "
-        f"(events), kernel time per pass {{{kp}}}")
+        f"(events), kernel time per pass {{{kp}}}; with a cache flush before each pass {flushed_ms:.3f} ms")
 
     # the next rows on the same inputs: one gate per head (Gated DeltaNet: the first channel's
     # log-decay of each token) and state snapshots every 16 chunks
@@ -306,12 +383,87 @@ def oracle_sample(args, res, out, wide_all):
     o_ref, t = run(Ts)
     o_gpu = out[0, :Ts].detach().cpu().numpy().astype(np.float64)
     err = slice_err(o_gpu, o_ref)
+    # one host thread, on a smaller sample of the same tokens
+    T1 = 256
+    ins1 = [synth.to_f64(q[:T1], "bf16"), synth.to_f64(k[:T1], "bf16"), synth.to_f64(v[:T1], "bf16"),
+            g[:T1].astype(np.float64), synth.to_f64(b[:T1], "bf16")]
+    t0 = time.perf_counter()
+    oracle.recurrence(*ins1, threads=1)
+    t1 = time.perf_counter() - t0
     res["cpu_baseline"] = {"value": round(Ts / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                            "sample": f"first {Ts} tokens x {H} heads of the T={q.shape[0]} prefill workload "
-                                     f"(fp64 token recurrence, {t:.1f} s)"}
+                                     f"(fp64 token recurrence, {t:.1f} s)",
+                           "threads": threads, "host_cores": host_cores(), "os_cpu_count": os.cpu_count(),
+                           "threads_note": "the oracle runs on at most 16 threads, the host CPU share of one GPU "
+                                           "on this machine; host_cores is what the process may run on",
+                           "single_core": {"value": round(T1 / t1, 2), "unit": "tokens/s", "threads": 1,
+                                           "sample": f"first {T1} tokens x {H} heads, {t1:.2f} s"}}
     res["parity"] = {"prefill_tokens_checked": Ts, "heads": H, "max_slice_rel_err": err, "tol": 2e-3,
                      "ok": bool(err <= 2e-3)}
     log(f"[oracle] {Ts / t:.1f} tokens/s; parity max err {err:.2e}")
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def oracle_rates(args, res):
+    """The oracle's rate on the other workloads' own inputs (bounded samples, every head), on the
+    same host threads and on one thread: the prefill workload (T=8192), the varlen append workload
+    (the first tokens of each of its 8 segments, from their carried states) and the long-context
+    workload (its first tokens; and its decode tail, one token per step on all heads)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    threads = oracle.default_threads()
+
+    def timed(ins, cu=None, s0=None, th=threads):
+        t0 = time.perf_counter()
+        o, sT = oracle.recurrence(*ins, cu, s0, threads=th)
+        return time.perf_counter() - t0, sT
+
+    def widen(x):
+        q, k, v, g, b = x
+        return [synth.to_f64(q, "bf16"), synth.to_f64(k, "bf16"), synth.to_f64(v, "bf16"), g.astype(np.float64),
+                synth.to_f64(b, "bf16")]
+
+    out = {}
+    for name, n_all, n_one in (("prefill", 2048, 256), ("long", 2048, 256)):
+        w = synth.workload(name)
+        ins = widen(synth.gen_tokens(w, n_all))
+        t_all, sT = timed(ins)
+        t_one, _ = timed([x[:n_one] for x in ins], th=1)
+        out[name] = {"tokens_per_s": round(n_all / t_all, 1), "threads": threads,
+                     "single_core_tokens_per_s": round(n_one / t_one, 1),
+                     "sample": f"first {n_all} tokens x {w.H} heads ({n_one} on one thread) of T={w.T}"}
+        if name == "long":
+            steps = 256
+            dins = widen(synth.gen_tokens(w, steps, offset_tokens=n_all))
+            # one sequence, one token per decode step, in order from the sample's final state
+            t_dec, _ = timed(dins, None, sT, th=1)
+            out["long_decode_tail"] = {"steps_per_s": round(steps / t_dec, 1), "threads": 1,
+                                       "sample": f"{steps} decode steps (B=1, {w.H} heads) from the state after "
+                                                 f"the first {n_all} tokens"}
+    w = synth.workload("varlen")
+    s0 = synth.gen_state(w, len(w.lengths))
+    rates = []
+    for n_seg, th in ((512, threads), (32, 1)):
+        parts = [synth.gen_tokens(w, min(L, n_seg), offset_tokens=int(o))
+                 for L, o in zip(w.lengths, synth.cu_seqlens(w.lengths)[:-1])]
+        ins = widen([np.concatenate([p[i] for p in parts]) for i in range(5)])
+        cu = synth.cu_seqlens([min(L, n_seg) for L in w.lengths])
+        t, _ = timed(ins, cu, s0, th=th)
+        rates.append(round(int(cu[-1]) / t, 1))
+    out["varlen"] = {"tokens_per_s": rates[0], "threads": threads, "single_core_tokens_per_s": rates[1],
+                     "sample": f"first 512 tokens (32 on one thread) of each of the {len(w.lengths)} segments x "
+                               f"{w.H} heads, from their carried states"}
+    res.setdefault("cpu_baseline", {})["per_workload"] = out
+    log(f"[oracle] per workload: {out}")
 
 
 def bench_backward(args, res, wide_all):
@@ -443,15 +595,42 @@ def bench_decode(args, res):
     bytes_step = DECODE_BYTES_PER_SEQ_HEAD * N * H
     gbps_wall = steps * bytes_step / elapsed / 1e9
     gbps_kernel = bytes_step / (avg * 1e-3) / 1e9
+    # cache-flush check: steps with L2 and the Infinity Cache evicted before each one (the 512 MiB
+    # state is only twice the Infinity Cache, so the unflushed loop could read part of it from
+    # there).  Out of place into a second state and output buffer (the same bytes moved), so that
+    # the timed run's in-place state and last output, which the parity check below follows, are
+    # left as they are.
+    flush = CacheFlush()
+    S2, out2 = torch.empty_like(S), torch.empty_like(out)
+    sp2, op2 = S2.data_ptr(), out2.data_ptr()
+    fl = []
+    for i in range(args.decode_warmup, min(total, args.decode_warmup + 50)):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = L.kda_decode_step(*args_list[i], sp, sp2, op2, N, H, dk, dv, _lib.KDA_BF16, stream)
+        e1.record()
+        if rc:
+            _lib.check(rc)
+        torch.cuda.synchronize()
+        fl.append(e0.elapsed_time(e1))
+    del flush, S2, out2
+    torch.cuda.empty_cache()
+    flushed = sum(fl) / len(fl)
     res["decode"] = {"workload": f"decode step, {N} sequences x {H} heads, d={dk}, in-place fp32 state",
                      "steps": steps, "steps_per_s": round(steps / elapsed, 1),
                      "ms_per_step": round(elapsed * 1e3 / steps, 4), "hbm_GBps": round(gbps_wall, 1),
-                     "kernel_avg_ms": round(avg, 4)}
+                     "kernel_avg_ms": round(avg, 4),
+                     "cache_flush": {"flushed_step_ms": round(flushed, 4), "flushed_steps": len(fl),
+                                     "flushed_GBps": round(bytes_step / (flushed * 1e-3) / 1e9, 1),
+                                     "how": "1 GiB buffer written (untimed) before each flushed step (out of place, "
+                                            "the same bytes), timed with events around the step; the 1000 timed "
+                                            "steps run back to back in place"}}
     res["roofline_decode"] = {"bound": "hbm", "kernel": "kda_decode", "achieved": round(gbps_kernel, 1),
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps_kernel / HBM_PEAK_GBPS, 4),
                               "traffic": traffic_of("kda_decode", f"decode N={N} H={H}"), "algorithmic_bytes_per_launch": bytes_step}
     log(f"[decode] {steps / elapsed:.1f} steps/s, {gbps_wall:.1f} GB/s wall, kernel avg {avg * 1e3:.1f} us "
-        f"({gbps_kernel:.1f} GB/s)")
+        f"({gbps_kernel:.1f} GB/s); flushed step {flushed * 1e3:.1f} us")
 
     if args.no_cpu_baseline:
         return
@@ -648,11 +827,17 @@ def main():
                                "fp32 log-decay/state/output; plus decode 256 seq x 32 heads x 1000 steps",
                    "global_batch": 1, "seq_len": args.T, "heads": 32, "head_dim": 128, "chunk": 64},
     }
+    res["copy_GBps"] = round(copy_rate(), 1)
+    res["copy_note"] = "best of 5 plain 1 GiB device-to-device streams (1 GiB read + 1 GiB written; torch copy_ " \
+                       "and torch.neg), events: this box's practical HBM streaming rate; the roofline peak stays " \
+                       "the 8 TB/s spec"
+    log(f"[copy] {res['copy_GBps']} GB/s")
     out = None
     if not args.skip_prefill:
         out, sT, wide_all = bench_prefill(args, res)
         if not args.no_cpu_baseline:
             oracle_sample(args, res, out, wide_all)
+            oracle_rates(args, res)
         del out, sT
         torch.cuda.empty_cache()
         if not args.skip_backward:

@@ -34,14 +34,15 @@
 //
 // Magnitudes beyond fp16: every value that is rounded to an fp16 operand is checked against
 // the fp16 range first (q and k entries, M, T, W in prep; beta*V, the corrections D and the
-// state in the state pass; a NaN or Inf fails the check too).  A (sequence, head, value
-// block) chain that meets such a value is not finished here: its final state is left
-// unwritten, and a third pass recomputes the whole chain with the fp32 chunked kernel.
+// state in the state pass).  A (sequence, head, value block) chain that meets such a value is
+// recomputed at the end of its state workgroup by the fp32 chunked evaluation, before any of its
+// final state is written.
 #include <mutex>
 #include <type_traits>
 #include <vector>
 
 #include "kda.h"
+#include "kda_chunk_f32.h"
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -157,11 +158,8 @@ struct alignas(16) PrepLds {
     int range_bad;   // some value rounded to an fp16 operand is beyond the fp16 range
 };
 
-// |x| within the fp16 range (false for NaN and Inf)
-__device__ __forceinline__ bool f16_ok(float x) { return __builtin_fabsf(x) < 65504.f; }
-
-// per-unit flag word written by prep: bit 0 = exact diagonal tiles needed (redone by the
-// second prep pass), bit 1 = a value beyond the fp16 range (the chain is redone in fp32)
+// per-unit flag word written by prep: bit 0 = exact diagonal tiles needed (the unit's second
+// pass), bit 1 = a value beyond the fp16 range (the chains through the chunk are redone in fp32)
 constexpr int kFlagExact = 1;
 constexpr int kFlagRange = 2;
 
@@ -189,19 +187,21 @@ __device__ __forceinline__ uint32_t bf_elem(const uint4& v, int i) {
 
 // PRO: fused input prologue (raw q, k, beta logits, raw gate inputs); a template parameter so
 // that the plain kernel carries none of its code.
-// EXACT: the second pass, which redoes the chunks that the first pass flagged (one word per
-// slot and head in `exact_flags`) with exact diagonal Gram tiles.  The first pass writes every
-// flag and leaves the records of flagged chunks to the second.
-// One (slot, head) unit; the whole workgroup calls it with the same arguments.
+// EXACT: the second pass over a unit whose first pass found a decay beyond the fp16 factors; it
+// rewrites the record with exact diagonal Gram tiles.  Both passes write the unit's flag word
+// (`exact_flags`, one per slot and head).
+// One (slot, head) unit; the whole workgroup calls it with the same arguments.  Returns whether
+// the unit needs the second pass (always false for the second pass itself, and for a slot that
+// no chunk uses).
 template <bool PRO, bool EXACT>
-__device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm, int64_t slot, int h,
+__device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm, int64_t slot, int h,
                                           int32_t* exact_flags, PrepLds& L) {
     // wave index, wave-uniform (readfirstlane lets the compiler keep it in a scalar register)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int H = a.H;
     int64_t n, c;
-    if (!sm.locate(slot, n, c)) return;  // uniform over the workgroup
+    if (!sm.locate(slot, n, c)) return false;  // uniform over the workgroup
     int32_t* flag = exact_flags + slot * H + h;
     int64_t bos, eos;
     sm.bounds(n, bos, eos);
@@ -443,8 +443,9 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         const float bv = bf(beta_q[i]);
         brow[i] = rr < Lc ? (PRO ? sigmoid(bv) : bv) : 0.f;
     }
-    // NaN-safe: a NaN entry fails the comparison
-    bool rbad = !(qkmax < 32768.f);
+    // largest magnitude among the M, T and W values this lane rounds to fp16 (a running maximum;
+    // a NaN leaves it unchanged and stays NaN in every result, as on the fp32 path)
+    float pmax = 0.f;
     if (!EXACT) {  // the second pass has its exact tile in place already
         const floatx4 accA = diagA, accM = diagM;
         // accumulator: column s = lr of block j, rows 4*lg + i of block w
@@ -453,12 +454,12 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
             const int rr = 16 * w + 4 * lg + i, ss = 16 * w + lr;
             L.AT[rr][ss] = (ss < rr) ? brow[i] * accA[i] : 0.f;
             const float mv = (ss <= rr) ? accM[i] : 0.f;
-            rbad |= !f16_ok(mv);
+            pmax = fmaxf(pmax, __builtin_fabsf(mv));
             L.M[rr][ss] = (_Float16)mv;
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rbad |= !f16_ok((float)L.M[r][16 * w + 4 * lg + j]);
+        for (int j = 0; j < 4; ++j) pmax = fmaxf(pmax, __builtin_fabsf((float)L.M[r][16 * w + 4 * lg + j]));
     }
     for (int j = w + 1; j < 4; ++j)
 #pragma unroll
@@ -481,7 +482,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         for (int i = 0; i < 4; ++i) {
             const int rr = 16 * w + 4 * lg + i, ss = 16 * j + lr;
             L.AT[rr][ss] = brow[i] * accA[i];
-            rbad |= !f16_ok(accM[i]);
+            pmax = fmaxf(pmax, __builtin_fabsf(accM[i]));
             L.M[rr][ss] = (_Float16)accM[i];
         }
     }
@@ -540,7 +541,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
             const int col = 32 * kb + 8 * lg + i, cb = col >> 4;
             float val = 0.f;
             if (cb <= rb) val = t_block(L, rb, cb)[lr * (C + 1) + (col & 15)];
-            rbad |= !f16_ok(val);
+            pmax = fmaxf(pmax, __builtin_fabsf(val));
             tv[i] = (_Float16)val;
         }
         *reinterpret_cast<half8*>(rec + kOffT + t * kTile + lane * 16) = tv;
@@ -572,12 +573,12 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
                                    acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                rbad |= !f16_ok(acc[i]);
+                pmax = fmaxf(pmax, __builtin_fabsf(acc[i]));
                 L.o.W[16 * w + 4 * lg + i][16 * cb + lr] = (_Float16)acc[i];
             }
         }
     }
-    if (rbad) L.range_bad = 1;  // benign race: every writer stores 1
+    if (!(qkmax < 32768.f) || !(pmax < 65504.f)) L.range_bad = 1;  // benign race: every writer stores 1
     __syncthreads();
     if (threadIdx.x == 0) *flag = (L.exact_diag ? kFlagExact : 0) | (L.range_bad ? kFlagRange : 0);
 #pragma unroll
@@ -590,34 +591,20 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, const SeqMap& sm
         for (int ch = lane; ch < DK; ch += 64)
             gam[ch] = fast_exp(L.tot[0][ch] + L.tot[1][ch] + L.tot[2][ch] + L.tot[3][ch]);
     }
+    return !EXACT && L.exact_diag != 0;  // final since the factor tables' barrier
 }
 
-// First pass: one workgroup (4 waves) per (slot, head), heads fastest: workgroups that run at
-// the same time read neighbouring token rows and write neighbouring records.
+// One workgroup (4 waves) per (slot, head), heads fastest: workgroups that run at the same time
+// read neighbouring token rows and write neighbouring records.  A unit that needs exact diagonal
+// tiles takes its second pass in the same workgroup.
 template <bool PRO>
 __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm, int32_t* exact_flags) {
     __shared__ PrepLds L;
-    const int64_t unit = blockIdx.x;
-    prep_unit<PRO, false>(a, sm, unit / a.H, (int)(unit % a.H), exact_flags, L);
-}
-
-// Second pass: workgroup b reads the flags of units 64b .. 64b + 63 (unit = slot * H + head) and
-// redoes the ones flagged for exact diagonal tiles in turn (each rewrites its own flag word).  A flag of a slot that no chunk uses is never written and
-// may hold anything; such a unit returns at once.
-template <bool PRO>
-__global__ __launch_bounds__(256, 2) void prep_exact_kernel(PrefillArgs a, SeqMap sm, int32_t* exact_flags,
-                                                            int64_t units) {
-    __shared__ PrepLds L;
-    const int64_t u0 = (int64_t)blockIdx.x * 64;
-    const int64_t u = u0 + (threadIdx.x & 63);
-    const bool set = u < units && (exact_flags[u] & kFlagExact) != 0;
-    uint64_t todo = __ballot(set);  // the same mask in every wave
-    while (todo) {
-        const int bit = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const int64_t unit = u0 + bit;
-        prep_unit<PRO, true>(a, sm, unit / a.H, (int)(unit % a.H), exact_flags, L);
-        __syncthreads();  // the next unit rewrites the LDS this one still reads at its end
+    const int64_t unit = blockIdx.x, slot = unit / a.H;
+    const int h = (int)(unit % a.H);
+    if (prep_unit<PRO, false>(a, sm, slot, h, exact_flags, L)) {  // uniform over the workgroup
+        __syncthreads();  // the second pass rewrites the LDS the first still reads at its end
+        prep_unit<PRO, true>(a, sm, slot, h, exact_flags, L);
     }
 }
 
@@ -737,14 +724,13 @@ struct StageRegs {
     u32x4 v[2];
     uint32_t b[2];
     uint32_t g[2];
-    uint32_t f;  // the chunk's prep flag word (half 0)
 };
 
 // Token half J (tokens 32 J .. 32 J + 31) of a chunk's staging; half 0 also takes gamma.
 template <int J>
 __device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* v, const uint16_t* beta,
-                                           const unsigned char* rec, const int32_t* flag, int64_t t0, int Lc, int H,
-                                           int h, int vb, int lane) {
+                                           const unsigned char* rec, int64_t t0, int Lc, int H, int h, int vb,
+                                           int lane) {
     const int64_t rowv = (int64_t)H * DV;
     const __amdgpu_buffer_rsrc_t vrs =
         make_rsrc(v + (t0 * H + h) * (int64_t)DV + vb * BV, (uint32_t)(((Lc - 1) * rowv + BV) * 2));
@@ -756,32 +742,28 @@ __device__ __forceinline__ void stage_load(StageRegs& r, const uint16_t* v, cons
         const __amdgpu_buffer_rsrc_t grs = make_rsrc(rec + kOffGamma, DK * 4);
         r.g[0] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8, 0, 0);
         r.g[1] = __builtin_amdgcn_raw_buffer_load_b32(grs, lane * 8 + 4, 0, 0);
-        r.f = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(flag, 4), 0, 0, 0);
     }
 }
 
-// Also records in the wave's flag slot a beta*V value beyond the fp16 range, or (half 0) a
-// prep flag of the chunk that says so of one of its operands.
+// amax: the largest |beta*v| staged so far by this lane (a running maximum; a NaN leaves it
+// unchanged and stays NaN in every result, as on the fp32 path)
 template <int J>
-__device__ __forceinline__ void stage_store(StateLds& L, int buf, const StageRegs& r, int w, int lane,
-                                            bool beta_logits) {
+__device__ __forceinline__ void stage_store(StateLds& L, int buf, const StageRegs& r, int lane, bool beta_logits,
+                                            float& amax) {
     const int tok = 32 * J + (lane >> 1);
     const float bt = beta_logits ? sigmoid(bf((uint16_t)r.b[J])) : bf((uint16_t)r.b[J]);
     const uint32_t words[4] = {r.v[J].x, r.v[J].y, r.v[J].z, r.v[J].w};
-    bool bad = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const uint16_t bits = (uint16_t)((e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFF));
         const float x = bt * bf(bits);
-        bad |= !f16_ok(x);
+        amax = fmaxf(amax, __builtin_fabsf(x));
         L.BVs[buf][8 * (lane & 1) + e][tok] = (_Float16)x;
     }
     if (J == 0) {
         L.gam[buf][2 * lane] = __uint_as_float(r.g[0]);
         L.gam[buf][2 * lane + 1] = __uint_as_float(r.g[1]);
-        bad |= (r.f & kFlagRange) != 0;
     }
-    if (bad) L.bad[w] = 1;  // benign race: every writer stores 1
 }
 
 // Output rows of one chunk: the accumulator tile (lane = column, 4 rows) goes through LDS so
@@ -801,10 +783,10 @@ __device__ __forceinline__ void store_o(StateLds& L, floatx4 O, float* obase, in
 // One chunk: operands `cur` (the next chunk's are already requested).  Returns this wave's
 // output rows; the caller stores them after issuing the following prefetch (loads and stores
 // share one in-order counter, so an early store would delay every later operand wait).
+// amax: running maximum of |D| and |S1| over this lane's values (see stage_store)
 __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cur, ChunkFrags& nxt,
                                                const unsigned char* nrec, bool has_next, int buf, floatx4 (&Sf)[2],
-                                               int w, int lane) {
-    bool bad = false;
+                                               int w, int lane, float& amax) {
     const int lr = lane & 15, lg = lane >> 4;
     const __amdgpu_buffer_rsrc_t nr = make_rsrc(nrec, kRecord);  // a valid record even when !has_next
     if (has_next) load_group(nxt, nr, 0, w, lane);
@@ -831,7 +813,7 @@ __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cu
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float d = U[i] - X[i];
-        bad |= !f16_ok(d);
+        amax = fmaxf(amax, __builtin_fabsf(d));
         dh[i] = (_Float16)d;
     }
     *reinterpret_cast<half4*>(&L.D[lr][16 * w + 4 * lg]) = dh;
@@ -854,7 +836,7 @@ __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cu
         half4 hv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            bad |= !f16_ok(acc[i]);
+            amax = fmaxf(amax, __builtin_fabsf(acc[i]));
             hv[i] = (_Float16)acc[i];
         }
         *reinterpret_cast<half4*>(&L.S[lr][16 * (2 * w + t) + 4 * lg]) = hv;
@@ -863,7 +845,6 @@ __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cu
     floatx4 O = Y;
     O = mfma16x16x32(cur.mm[0], db[0], O);
     if (w >= 2) O = mfma16x16x32(cur.mm[1], db[1], O);
-    if (bad) L.bad[w] = 1;  // benign race: every writer stores 1
     lds_barrier();
     return O;
 }
@@ -874,18 +855,20 @@ __device__ __forceinline__ floatx4 state_chunk(StateLds& L, const ChunkFrags& cu
 // staging loads stay out of the compute waves' counters.
 constexpr int kStateThreads = 384;
 
-// uflags: prep's flag word per (slot, head); redo: one word per chain (sequence, head, value
-// block), set to 1 when the chain met a value beyond the fp16 range (its final state is then not
-// written, so that an in-place state_in survives for the fp32 redo), else 0.
-__global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, SeqMap sm, const int32_t* uflags,
-                                                              int32_t* redo) {
+// uflags: prep's flag word per (slot, head).  A chain that met a value beyond the fp16 range is
+// recomputed from its inputs by the fp32 chunked evaluation (f32_chain, 32-token chunks) in the
+// same workgroup, before any of its final state is written (so an in-place state_in is intact);
+// its LDS is the kernel's dynamic shared memory.
+constexpr int kRedoChunk = 32;
+
+__global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, SeqMap sm, const int32_t* uflags) {
     __shared__ StateLds L;
+    extern __shared__ float redo_lds[];
     // wave index, wave-uniform (readfirstlane lets the compiler keep it in a scalar register)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int H = a.H;
-    // this wave's fp16-range flag; every later write of 1 follows it in the wave's program order
-    if (lane == 0) L.bad[w] = 0;
+    float amax = 0.f;  // largest magnitude this lane rounds to fp16 (beta*v; corrections, state)
 
     // workgroup -> (sequence, head, value block); the 8 value blocks of a (sequence, head)
     // land on one XCD (workgroups are dealt to the 8 XCDs round-robin) so they share its L2
@@ -912,7 +895,14 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
     const int64_t sbase = nh * (int64_t)DK * DV + vb * BV;
     const unsigned char* ws = static_cast<const unsigned char*>(a.ws);
     auto rec_of = [&](int64_t c) { return ws + ((slot0 + c) * H + h) * (int64_t)kRecord; };
-    auto flag_of = [&](int64_t c) { return uflags + (slot0 + c) * H + h; };
+    // After every chunk: each wave publishes whether it met a value beyond the fp16 range (and
+    // the compute waves whether prep flagged one of this chain's chunks), one barrier, then the
+    // compute waves take the decision together.
+    auto publish_flag = [&](bool bad) {
+        const bool any = __ballot(bad) != 0;
+        if (lane == 0) L.bad[w] = any ? 1 : 0;
+        lds_barrier();
+    };
     auto len_of = [&](int64_t c) {
         const int64_t t = eos - (bos + c * C);
         return (int)(t < C ? t : C);
@@ -934,32 +924,36 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
             if (warm)
                 for (int64_t c = 1; c <= kWarmAhead && c < nchunks; ++c) warm_l2(rec_of(c), vb, lane, dummy);
             if (nchunks > 0) {
-                stage_load<J>(ra, v, beta, rec_of(0), flag_of(0), bos, len_of(0), H, h, vb, lane);
-                stage_store<J>(L, 0, ra, w, lane, a.prologue);
+                stage_load<J>(ra, v, beta, rec_of(0), bos, len_of(0), H, h, vb, lane);
+                stage_store<J>(L, 0, ra, lane, a.prologue, amax);
             }
-            if (nchunks > 1) stage_load<J>(rb, v, beta, rec_of(1), flag_of(1), bos + C, len_of(1), H, h, vb, lane);
+            if (nchunks > 1) stage_load<J>(rb, v, beta, rec_of(1), bos + C, len_of(1), H, h, vb, lane);
             lds_barrier();
             for (int64_t c = 0; c < nchunks; c += 2) {
                 lds_barrier();
-                if (c + 1 < nchunks) stage_store<J>(L, 1, rb, w, lane, a.prologue);
+                if (c + 1 < nchunks) stage_store<J>(L, 1, rb, lane, a.prologue, amax);
                 if (c + 2 < nchunks)
-                    stage_load<J>(ra, v, beta, rec_of(c + 2), flag_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h,
-                                  vb, lane);
+                    stage_load<J>(ra, v, beta, rec_of(c + 2), bos + (c + 2) * C, len_of(c + 2), H, h, vb, lane);
                 if (warm && c + 1 + kWarmAhead < nchunks) warm_l2(rec_of(c + 1 + kWarmAhead), vb, lane, dummy);
                 lds_barrier();
                 if (c + 1 >= nchunks) break;
                 lds_barrier();
-                if (c + 2 < nchunks) stage_store<J>(L, 0, ra, w, lane, a.prologue);
+                if (c + 2 < nchunks) stage_store<J>(L, 0, ra, lane, a.prologue, amax);
                 if (c + 3 < nchunks)
-                    stage_load<J>(rb, v, beta, rec_of(c + 3), flag_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h,
-                                  vb, lane);
+                    stage_load<J>(rb, v, beta, rec_of(c + 3), bos + (c + 3) * C, len_of(c + 3), H, h, vb, lane);
                 if (warm && c + 2 + kWarmAhead < nchunks) warm_l2(rec_of(c + 2 + kWarmAhead), vb, lane, dummy);
                 lds_barrier();
             }
             __builtin_amdgcn_s_waitcnt(0);  // no direct-to-LDS write may outlive the workgroup
+            publish_flag(!(amax < 65504.f));
         };
         if (w == 4) run(std::integral_constant<int, 1>{});
         else run(std::integral_constant<int, 0>{});
+        if (L.bad[0] | L.bad[1] | L.bad[2] | L.bad[3] | L.bad[4] | L.bad[5]) {
+            PrefillArgs r = a;  // 64-token snapshot intervals are twice as many 32-token chunks
+            r.snap_every = a.snap_every * (C / kRedoChunk);
+            f32_chain<DK, DV, kRedoChunk, kStateThreads, uint16_t>(r, n, h, vb, redo_lds);
+        }
         return;
     }
 
@@ -971,18 +965,16 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
 #pragma unroll
             for (int i = 0; i < 4; ++i) Sf[t][i] = a.s0[sbase + (int64_t)(16 * (2 * w + t) + 4 * lg + i) * DV + lr];
     }
-    bool s0bad = false;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         half4 hv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s0bad |= !f16_ok(Sf[t][i]);
+            amax = fmaxf(amax, __builtin_fabsf(Sf[t][i]));
             hv[i] = (_Float16)Sf[t][i];
         }
         *reinterpret_cast<half4*>(&L.S[lr][16 * (2 * w + t) + 4 * lg]) = hv;
     }
-    if (s0bad) L.bad[w] = 1;  // benign race: every writer stores 1
 
     // Two chunks per iteration with alternating operand registers: chunk c reads fa and loads
     // chunk c+1 into fb, chunk c+1 reads fb and loads chunk c+2 into fa, so no registers are
@@ -1014,23 +1006,29 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(PrefillArgs a, Seq
         __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0), expcnt/lgkmcnt at max
         if (c > 0) store_o(L, Oprev, obase0 + (c - 1) * ostep, len_of(c - 1), H, w, lane);
         const bool has_next = c + 1 < nchunks;
-        Oprev = state_chunk(L, fa, fb, rec_of(has_next ? c + 1 : c), has_next, 0, Sf, w, lane);
+        Oprev = state_chunk(L, fa, fb, rec_of(has_next ? c + 1 : c), has_next, 0, Sf, w, lane, amax);
         snapshot(c);
         if (!has_next) break;
         __builtin_amdgcn_s_waitcnt(0x0F70);
         store_o(L, Oprev, obase0 + c * ostep, len_of(c), H, w, lane);
         const bool has_next2 = c + 2 < nchunks;
-        Oprev = state_chunk(L, fb, fa, rec_of(has_next2 ? c + 2 : c + 1), has_next2, 1, Sf, w, lane);
+        Oprev = state_chunk(L, fb, fa, rec_of(has_next2 ? c + 2 : c + 1), has_next2, 1, Sf, w, lane, amax);
         snapshot(c + 1);
     }
     if (nchunks > 0) store_o(L, Oprev, obase0 + (nchunks - 1) * ostep, len_of(nchunks - 1), H, w, lane);
 
-    // Every wave wrote its flag slot before the last barrier it took part in (the helper waves'
-    // last staging precedes the last chunk's barriers), so the slots are final here.  A chain
-    // that met a value beyond the fp16 range leaves its final state to the fp32 redo.
-    const bool any_bad = (L.bad[0] | L.bad[1] | L.bad[2] | L.bad[3] | L.bad[4] | L.bad[5]) != 0;
-    if (w == 0 && lane == 0) redo[nh * NVB + vb] = any_bad ? 1 : 0;
-    if (any_bad) return;
+    // prep's range flags of this chain's chunks, a quarter per compute wave
+    bool pbad = false;
+#pragma unroll 4
+    for (int64_t c = 64 * w + lane; c < nchunks; c += 256) pbad |= (uflags[(slot0 + c) * H + h] & kFlagRange) != 0;
+    publish_flag(pbad || !(amax < 65504.f));
+    // the same decision in all six waves (the helper waves read the same slots)
+    if (L.bad[0] | L.bad[1] | L.bad[2] | L.bad[3] | L.bad[4] | L.bad[5]) {
+        PrefillArgs r = a;
+        r.snap_every = a.snap_every * (C / kRedoChunk);
+        f32_chain<DK, DV, kRedoChunk, kStateThreads, uint16_t>(r, n, h, vb, redo_lds);
+        return;
+    }
     if (a.sT) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -1061,18 +1059,18 @@ bool chunk_mfma_supported(int bf16, int dk, int dv, int chunk) {
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Workspace layout: the records (one per slot and head), one prep flag word per record, one redo
-// word per state chain (sequence, head, value block); each part rounded up to 256 bytes.
+// Workspace layout: the records (one per slot and head), then one prep flag word per record
+// (rounded up to 256 bytes).
 size_t chunk_mfma_workspace(int64_t N, int64_t T_fixed, int64_t T_total, bool fixed, int H, int chunk) {
     (void)chunk;
+    (void)N;
     const size_t units = (size_t)num_slots(N, T_fixed, T_total, fixed) * (size_t)H;
-    return units * (size_t)kRecord + round256(units * sizeof(int32_t)) +
-           round256((size_t)N * (size_t)H * NVB * sizeof(int32_t));
+    return units * (size_t)kRecord + round256(units * sizeof(int32_t));
 }
 
 // ------------------------------------------------------------------------------------------
 // Fixed scratch for the entry point that allocates nothing (kda_append_prefill_noalloc): the
-// records, flags and redo words of one call live in this array instead of a caller workspace.
+// records and flags of one call live in this array instead of a caller workspace.
 // Each GPU the library runs on holds its own copy from the code object's load until the process
 // ends.  Host code never passes the array's name to a kernel (on the host it is a stand-in, not
 // a device address): it takes the per-device address from hipGetSymbolAddress once per device.
@@ -1123,38 +1121,28 @@ hipError_t launch_chunk_mfma(const PrefillArgs& a, hipStream_t s) {
     const bool timed = timing_on();
     const int64_t units = slots * (int64_t)a.H;
     int32_t* flags = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) + units * kRecord);
-    int32_t* redo = reinterpret_cast<int32_t*>(reinterpret_cast<unsigned char*>(flags) +
-                                               round256((size_t)units * sizeof(int32_t)));
     if (slots > 0 && a.T_total > 0) {
         const dim3 grid((unsigned)units);
-        const dim3 grid2((unsigned)((units + 63) / 64));
         if (timed) timed_begin(kKernelPrep, s);
-        // first pass over every chunk, then the chunks it flagged for exact diagonal tiles
-        if (a.prologue) {
+        if (a.prologue)
             hipLaunchKernelGGL(prep_kernel<true>, grid, dim3(256), 0, s, a, sm, flags);
-            hipLaunchKernelGGL(prep_exact_kernel<true>, grid2, dim3(256), 0, s, a, sm, flags, units);
-        } else {
+        else
             hipLaunchKernelGGL(prep_kernel<false>, grid, dim3(256), 0, s, a, sm, flags);
-            hipLaunchKernelGGL(prep_exact_kernel<false>, grid2, dim3(256), 0, s, a, sm, flags, units);
-        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (timed) timed_end(s);
     }
+    // the fp32 evaluation of flagged chains needs more LDS than the default dynamic limit
+    constexpr size_t redo_bytes = F32Lds<DK, kRedoChunk>::kBytes;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(state_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)redo_bytes);
+    if (attr != hipSuccess) return attr;
     if (timed) timed_begin(kKernelState, s);
-    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(a.N * a.H * NVB)), dim3(kStateThreads), 0, s, a, sm, flags,
-                       redo);
+    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(a.N * a.H * NVB)), dim3(kStateThreads), redo_bytes, s, a, sm,
+                       flags);
     hipError_t e = hipGetLastError();
     if (timed) timed_end(s);
-    if (e != hipSuccess) return e;
-    // the chains that met a value beyond the fp16 range, recomputed in fp32 (64-token chunks as
-    // two 32-token ones, so snapshots fall every 2 * snap_every of them); the other chains'
-    // workgroups return at once
-    PrefillArgs r = a;
-    r.chunk = 32;
-    r.snap_every = a.snap_every * 2;
-    r.redo = redo;
-    return launch_chunk_f32(r, s);
+    return e;
 }
 
 }  // namespace kda

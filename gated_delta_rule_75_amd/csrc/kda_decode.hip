@@ -19,6 +19,11 @@
 // read-once/write-once HBM stream needs (measured on MI355X at N = 256, H = 32, d = 128:
 // 1024 threads x 4 rows beat 256 x 16, 512 x 8 and column-sliced workgroups).  The column
 // reductions over key rows go through wave shuffles, then a small LDS table.
+//
+// Small batches: value columns never interact (each column of S is its own chain), so when
+// there are few (sequence, head) pairs each one is split over DV / 16 workgroups of 16 columns
+// (512 threads, one row each).  A single sequence with 32 heads then launches 256 workgroups
+// instead of 32, one per CU.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -27,29 +32,32 @@ namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-template <int DK, int DV>
+// DVB: value columns per workgroup (DV, or 16 for the column-split variant)
+template <int DK, int DVB>
 struct DecodeShape {
-    static constexpr int kColThreads = DV / 4;                    // threads per row
+    static constexpr int kColThreads = DVB / 4;                   // threads per row
     static constexpr int kRowGroups = DK < 1024 / kColThreads ? DK : 1024 / kColThreads;
     static constexpr int kThreads = kColThreads * kRowGroups;
     static constexpr int kWaves = kThreads / 64;
     static constexpr int kRowsPerThread = DK / kRowGroups;
-    static_assert(DV % 4 == 0 && kThreads % 64 == 0, "shape");
+    static_assert(DVB % 4 == 0 && kThreads % 64 == 0, "shape");
     static_assert(DK % kRowGroups == 0, "rows must split evenly");
     static_assert(kThreads >= DK, "one thread per key row stages alpha, k, q");
 };
 
-template <int DK, int DV, typename TI, bool PROLOGUE>
+template <int DK, int DV, int DVB, typename TI, bool PROLOGUE>
 __global__ __launch_bounds__(1024) void decode_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v, const float* __restrict__ g,
     const TI* __restrict__ beta, const float* s_in, float* s_out, float* __restrict__ o, int gate_head,
     float gate_scale) {
-    using Sh = DecodeShape<DK, DV>;
+    using Sh = DecodeShape<DK, DVB>;
     constexpr int CT = Sh::kColThreads, RG = Sh::kRowGroups, RPT = Sh::kRowsPerThread;
     constexpr int NW = Sh::kWaves;
-    const int64_t nh = blockIdx.x;  // sequence * H + head
+    constexpr int NCB = DV / DVB;   // workgroups per (sequence, head)
+    const int64_t nh = blockIdx.x / NCB;  // sequence * H + head
+    const int col0 = (int)(blockIdx.x % NCB) * DVB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c4 = tid % CT;  // owns columns 4*c4 .. 4*c4+3
+    const int c4 = tid % CT;  // owns columns col0 + 4*c4 .. +3
     const int rg = tid / CT;  // owns rows rg, rg + RG, ...
 
     __shared__ floatx4 s_red[NW][2][CT];  // per wave: partial u and p of each column group
@@ -57,8 +65,8 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     __shared__ float s_a[DK], s_k[DK], s_q[DK];
     __shared__ float s_nrm[2][DK / 64 > 0 ? DK / 64 : 1];
 
-    const float* Sin = s_in + nh * (int64_t)DK * DV + 4 * c4;
-    float* Sout = s_out + nh * (int64_t)DK * DV + 4 * c4;
+    const float* Sin = s_in + nh * (int64_t)DK * DV + col0 + 4 * c4;
+    float* Sout = s_out + nh * (int64_t)DK * DV + col0 + 4 * c4;
 
     // the state loads first: they are the bulk of the traffic
     floatx4 st[RPT];
@@ -69,7 +77,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     // that their latency overlaps the state loads instead of following the reductions
     float vv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vv[j] = ld_in(v, nh * DV + 4 * c4 + j);
+    for (int j = 0; j < 4; ++j) vv[j] = ld_in(v, nh * DV + col0 + 4 * c4 + j);
     const float braw = ld_in(beta, nh);
     // alpha, k, q of every key row, one row per thread, shared through LDS
     float kt = 0.f, qt = 0.f;
@@ -156,7 +164,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(
         floatx4 ov;
 #pragma unroll
         for (int j = 0; j < 4; ++j) ov[j] = pp[j] + kqt * d[j];
-        *reinterpret_cast<floatx4*>(o + nh * DV + 4 * c4) = ov;
+        *reinterpret_cast<floatx4*>(o + nh * DV + col0 + 4 * c4) = ov;
     }
 
 #pragma unroll
@@ -168,30 +176,38 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     }
 }
 
-template <int DK, int DV, typename TI>
-void launch_typed(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+template <int DK, int DV, int DVB, typename TI>
+void launch_typed(const DecodeArgs& a, hipStream_t s) {
+    using Sh = DecodeShape<DK, DVB>;
+    const dim3 grid(static_cast<unsigned>(a.N * a.H * (DV / DVB))), block(Sh::kThreads);
     const TI* q = static_cast<const TI*>(a.q);
     const TI* k = static_cast<const TI*>(a.k);
     const TI* v = static_cast<const TI*>(a.v);
     const TI* b = static_cast<const TI*>(a.beta);
     if (a.prologue)
-        hipLaunchKernelGGL((decode_kernel<DK, DV, TI, true>), grid, block, 0, s, q, k, v, a.g, b, a.s_in, a.s_out,
-                           a.o, a.gate_head, a.gate_scale);
+        hipLaunchKernelGGL((decode_kernel<DK, DV, DVB, TI, true>), grid, block, 0, s, q, k, v, a.g, b, a.s_in,
+                           a.s_out, a.o, a.gate_head, a.gate_scale);
     else
-        hipLaunchKernelGGL((decode_kernel<DK, DV, TI, false>), grid, block, 0, s, q, k, v, a.g, b, a.s_in, a.s_out,
-                           a.o, a.gate_head, a.gate_scale);
+        hipLaunchKernelGGL((decode_kernel<DK, DV, DVB, TI, false>), grid, block, 0, s, q, k, v, a.g, b, a.s_in,
+                           a.s_out, a.o, a.gate_head, a.gate_scale);
 }
+
+// (sequence, head) pairs below which each pair is split over 16-column workgroups: with fewer
+// than two workgroups per CU the whole-row layout leaves most of the chip idle
+constexpr int64_t kSplitBelow = 512;
 
 template <int DK, int DV>
 hipError_t launch_shape(const DecodeArgs& a, hipStream_t s) {
-    using Sh = DecodeShape<DK, DV>;
-    const dim3 grid(static_cast<unsigned>(a.N * a.H));
     const bool timed = timing_on();
     if (timed) timed_begin(kKernelDecode, s);
-    if (a.bf16)
-        launch_typed<DK, DV, uint16_t>(a, grid, dim3(Sh::kThreads), s);
-    else
-        launch_typed<DK, DV, float>(a, grid, dim3(Sh::kThreads), s);
+    const bool split = DV > 16 && a.N * a.H < kSplitBelow;
+    if (a.bf16) {
+        if (split) launch_typed<DK, DV, 16, uint16_t>(a, s);
+        else launch_typed<DK, DV, DV, uint16_t>(a, s);
+    } else {
+        if (split) launch_typed<DK, DV, 16, float>(a, s);
+        else launch_typed<DK, DV, DV, float>(a, s);
+    }
     hipError_t e = hipGetLastError();
     if (timed) timed_end(s);
     return e;

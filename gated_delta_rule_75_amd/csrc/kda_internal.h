@@ -50,9 +50,6 @@ struct PrefillArgs {
     int64_t snap_per_seq;   // fixed length: snapshots per sequence
     int prologue;           // raw inputs: normalise q, k; beta = sigmoid(beta); g = -gate_scale * softplus(g)
     float gate_scale;
-    // fp32 chunked kernel only: when set, one word per (sequence, head, 16-column value block);
-    // only the blocks whose word is non-zero are computed
-    const int32_t* redo;
 };
 
 struct DecodeArgs {

@@ -53,9 +53,9 @@
  *     Gram matrix M, the UT transform T and the WY factor W per chunk, and
  *     beta*v, the per-token corrections and the state per chain.  A (sequence,
  *     head, 16-column value block) chain that meets a value outside the range
- *     is recomputed by the fp32 chunked kernel in the same call (same results
- *     to the fp32 tolerance, at that kernel's speed), so there is no range
- *     limit beyond fp32's.  Decays of any strength are exact up to rounding: a
+ *     is recomputed in the same call by the fp32 chunked evaluation (fp32
+ *     accuracy, at that path's speed), so there is no range limit beyond
+ *     fp32's.  Decays of any strength are exact up to rounding: a
  *     chunk in which some channel decays by more than e^10 over 8 tokens sums
  *     its diagonal 16x16 Gram tiles in fp32 with one exponential per token
  *     pair, which costs that chunk extra time.  The fp32 path has no such

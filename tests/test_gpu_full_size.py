@@ -6,10 +6,11 @@ max|gpu - oracle| / max|oracle| <= 2e-3 (bfloat16 storage, fp32 state).
 
 Workloads (seeded, see synth.workload):
   prefill  B=1, H=32, T=8192, d=128, chunk 64, zero initial state   (every head checked)
-  metric   the same at T=65,536 (the headline prefill)              (4 heads checked)
-  decode   256 sequences x 32 heads, 1000 in-place steps            (8 pairs, every step)
-  varlen   8 carried states, segments of 1K..32K tokens, packed     (4 heads, every segment)
-  long     B=1, H=32, T=2^20, per-channel rates, then 4096 decode steps (1 head, every token)
+  metric   the same at T=65,536 (the headline prefill)              (every head checked)
+  decode   256 sequences x 32 heads, 1000 in-place steps            (every pair at the first step;
+                                                                     8 pairs at every step)
+  varlen   8 carried states, segments of 1K..32K tokens, packed     (every head, every segment)
+  long     B=1, H=32, T=2^20, per-channel rates, then 4096 decode steps (4 heads, every token)
 """
 import numpy as np
 import pytest
@@ -63,7 +64,7 @@ def test_prefill_workload_all_heads():
 
 def test_metric_prefill_sampled_heads():
     w = synth.workload("metric")
-    heads = [0, 9, 22, 31]
+    heads = list(range(w.H))
     _, o, sT, og, sg, oref, sref = _prefill_full(w, w.T, heads)
     assert_close(og, oref, TOL, None, "o")
     assert_close(sg, sref, TOL, None, "S_T")
@@ -84,6 +85,17 @@ def test_decode_workload_1000_steps():
     ph = torch.tensor([p[1] for p in pairs], device="cuda")
     outs = torch.empty((steps, len(pairs), w.dv), device="cuda")
     out = torch.empty((N, H, w.dv), device="cuda")
+    # the first step on every (sequence, head) pair, out of place, against the oracle's step
+    S1 = torch.empty_like(S)
+    kda.decode_step(tq[0], tk[0], tv[0], tg[0], tb[0], S, out=out, state_out=S1)
+    torch.cuda.synchronize()
+    wide0 = (_wide(q[:N], "bf16"), _wide(k[:N], "bf16"), _wide(v[:N], "bf16"), g[:N].astype(np.float64),
+             _wide(b[:N], "bf16"))
+    print("[decode] oracle step 0 on all pairs", flush=True)
+    o0, s1 = oracle.decode_step(*wide0, s0.astype(np.float64))
+    assert_close(host(out), o0, TOL, np.arange(N + 1), "o step 0, all pairs")
+    assert_close(host(S1), s1, TOL, None, "S step 0, all pairs")
+    del S1, s1
     print("[decode] gpu steps", flush=True)
     for t in range(steps):
         kda.decode_step(tq[t], tk[t], tv[t], tg[t], tb[t], S, out=out)
@@ -113,7 +125,7 @@ def test_varlen_append_workload():
     o, sT = kda.append_prefill(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(g, "f32"), dev(b, "bf16"),
                                torch.from_numpy(cu).cuda(), dev(s0, "f32"))
     torch.cuda.synchronize()
-    heads = [0, 5, 18, 31]
+    heads = list(range(w.H))
     print(f"[varlen] oracle on heads {heads}", flush=True)
     oref, sref = oracle.recurrence(*_heads(st, heads, "bf16"), cu, s0[:, heads], vcols=32)
     assert_close(host(o[:, heads]), oref, TOL, cu, "o")
@@ -125,7 +137,7 @@ def test_varlen_append_workload():
 def test_long_context_prefill_then_decode():
     w = synth.workload("long")
     T, H, steps = w.T, w.H, w.decode_steps
-    heads = [11]
+    heads = [0, 11, 20, 31]
     st, o, sT, og, sg, oref, sref = _prefill_full(w, T, heads)
     assert_close(og, oref, TOL, None, "o (1M prefill)")
     assert_close(sg, sref, TOL, None, "S_T (1M prefill)")
@@ -141,7 +153,7 @@ def test_long_context_prefill_then_decode():
     for t in range(steps):
         outs[t] = kda.decode_step(tq[t:t + 1], tk[t:t + 1], tv[t:t + 1], tg[t:t + 1], tb[t:t + 1], S)[0]
     torch.cuda.synchronize()
-    oref2, sref2 = oracle.recurrence(*_heads((dq, dk_, dv_, dg, db), heads, "bf16"), None, sref, vcols=8)
+    oref2, sref2 = oracle.recurrence(*_heads((dq, dk_, dv_, dg, db), heads, "bf16"), None, sref, vcols=32)
     assert_close(host(outs[:, heads]), oref2, TOL, None, "o (decode tail)")
     assert_close(host(S[:, heads]), sref2, TOL, None, "S (decode tail)")
 

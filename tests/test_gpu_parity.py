@@ -90,12 +90,17 @@ def test_tiny_workload_exact_shape():
     assert_close(s, sref, 1e-5, None, "S_T")
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("f32", 16), ("bf16", 64), ("f32", 32)])
-def test_decode_steps_match_oracle(dtype, d):
-    print(f"decode dtype={dtype} d={d}", flush=True)
+@pytest.mark.parametrize("dtype,d,N", [
+    ("bf16", 128, 6), ("f32", 128, 6), ("f32", 16, 6), ("bf16", 64, 6), ("f32", 32, 6),
+    # 130 x 4 = 520 (sequence, head) pairs: one workgroup per pair (the large-batch layout); the
+    # cases above split each pair over 16-column workgroups
+    ("bf16", 128, 130), ("f32", 64, 130),
+])
+def test_decode_steps_match_oracle(dtype, d, N):
+    print(f"decode dtype={dtype} d={d} N={N}", flush=True)
     w = _w(dtype, H=4, d=d, seed=5, s0_std=0.02)
     w.q_unit = False
-    N, steps = 6, 5
+    steps = 5
     s0 = synth.gen_state(w, N)
     S = dev(s0, "f32")
     sref = s0.astype(np.float64)
