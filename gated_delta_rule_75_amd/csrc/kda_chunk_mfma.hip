@@ -64,11 +64,15 @@ constexpr int kTile = 1024;
 constexpr int kOffW = 0;                  // 16 tiles (token block tb, k-step ks): tb*4+ks
 constexpr int kOffQp = 16 * kTile;        // 16 tiles
 constexpr int kOffKdT = 32 * kTile;       // 16 tiles (channel block cb, k-step ks): cb*2+ks
-constexpr int kOffT = 48 * kTile;         // 8 tiles (row block rb, k-step kb): rb*2+kb
-constexpr int kOffM = 56 * kTile;         // 8 tiles
-constexpr int kOffGamma = 64 * kTile;     // 128 floats
-constexpr int kRecord = 64 * kTile + 512; // 66048 bytes (multiple of 256)
+constexpr int kOffT = 48 * kTile;         // 6 tiles (row block rb, k-step kb): t6(rb, kb)
+constexpr int kOffM = 54 * kTile;         // 6 tiles
+constexpr int kOffGamma = 60 * kTile;     // 128 floats
+constexpr int kRecord = 60 * kTile + 512; // 61952 bytes (multiple of 256)
 constexpr int kWarmAhead = 2;             // chunks of L2 warm-up ahead of the state pass (1, 2, 4 equal; 3, 6, 12 slower)
+
+// T and M are lower triangular: row blocks 0 and 1 have no entries in tokens 32..63 (k-step 1),
+// so those two tiles of each are not stored.  Tile index of row block rb, k-step kb:
+__host__ __device__ constexpr int t6(int rb, int kb) { return rb < 2 ? rb : 2 * rb - 2 + kb; }
 
 __device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -535,6 +539,7 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
     // ---- write T, M (8 tiles each) and K'^T (16 tiles) as fp16 operand tiles
     for (int t = w; t < 8; t += 4) {
         const int rb = t >> 1, kb = t & 1;
+        if (rb < 2 && kb == 1) continue;  // all zero, not stored
         half8 tv;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -544,8 +549,8 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
             pmax = fmaxf(pmax, __builtin_fabsf(val));
             tv[i] = (_Float16)val;
         }
-        *reinterpret_cast<half8*>(rec + kOffT + t * kTile + lane * 16) = tv;
-        *reinterpret_cast<half8*>(rec + kOffM + t * kTile + lane * 16) =
+        *reinterpret_cast<half8*>(rec + kOffT + t6(rb, kb) * kTile + lane * 16) = tv;
+        *reinterpret_cast<half8*>(rec + kOffM + t6(rb, kb) * kTile + lane * 16) =
             *reinterpret_cast<const half8*>(&L.M[16 * rb + lr][32 * kb + 8 * lg]);
     }
     for (int t = w; t < 16; t += 4) {
@@ -666,11 +671,11 @@ __device__ __forceinline__ void load_group(ChunkFrags& f, __amdgpu_buffer_rsrc_t
                 f.kd[t][ks] = as_half8(
                     __builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffKdT + ((2 * w + t) * 2 + ks) * kTile, 0));
     } else {
-        f.tt[0] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffT + (w * 2) * kTile, 0));
-        f.mm[0] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffM + (w * 2) * kTile, 0));
-        if (w >= 2) {  // rows of token blocks 0, 1 have no entries in tokens 32..63
-            f.tt[1] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffT + (w * 2 + 1) * kTile, 0));
-            f.mm[1] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffM + (w * 2 + 1) * kTile, 0));
+        f.tt[0] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffT + t6(w, 0) * kTile, 0));
+        f.mm[0] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffM + t6(w, 0) * kTile, 0));
+        if (w >= 2) {  // rows of token blocks 0, 1 have no entries in tokens 32..63 (not stored)
+            f.tt[1] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffT + t6(w, 1) * kTile, 0));
+            f.mm[1] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rr, lo, kOffM + t6(w, 1) * kTile, 0));
         }
     }
 }

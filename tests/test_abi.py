@@ -43,7 +43,7 @@ def test_supported_and_workspace():
     assert L.kda_is_supported(2, 1, 128, 128, 0) == 1
     assert L.kda_workspace_size(2, 4, 0, 32, 128, 128, 1, 64) == 0
     ws = L.kda_workspace_size(0, 1, 8192, 32, 128, 128, 1, 64)
-    assert ws == 128 * 32 * 66048 + 128 * 32 * 4  # records, then one flag word per record
+    assert ws == 128 * 32 * 61952 + 128 * 32 * 4  # records, then one flag word per record
     assert L.kda_workspace_size(0, 1, 8192, 32, 96, 128, 1, 64) == 2 ** 64 - 1
 
 
