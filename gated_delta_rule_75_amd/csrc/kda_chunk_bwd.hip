@@ -32,6 +32,8 @@
 // exp(G_r - G_m) exp(G_m - G_s), and the two factors scale the two operands.  Across blocks both
 // exponents are <= 0.  Inside a block one factor can exceed 1; where a block's 16-token decay
 // exceeds e^64 those pairs take their own exponentials on the vector ALUs instead.
+#include <cstdlib>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -132,21 +134,36 @@ struct Rec {
     static constexpr int64_t kFloats = (dgam + DK + 63) / 64 * 64;  // records stay 256-byte aligned
 };
 
-// Sequences (device cu_seqlens) and chunk slots: sequence n owns slots base(n) .. base(n) + chunks - 1.
+// Sequences (device cu_seqlens) and chunk slots.  One pass over every chunk (wlen = 0): sequence n
+// owns slots base(n) .. base(n) + chunks - 1.  A window (wlen > 0): only chunks wlo .. wlo + wlen - 1
+// of every sequence, sequence n owning slots n * wlen .. n * wlen + wlen - 1 (slot = base(n) + c).
 template <int C>
 struct Map {
     const int32_t* cu;
     int64_t N;
-    __device__ __forceinline__ int64_t base(int64_t n) const { return (int64_t)cu[n] / C + n; }
+    int64_t wlo, wlen;
+    __device__ __forceinline__ int64_t base(int64_t n) const { return wlen ? n * wlen - wlo : (int64_t)cu[n] / C + n; }
+    // this launch's chunks [c0, c1) of sequence n
+    __device__ __forceinline__ void range(int64_t n, int64_t& c0, int64_t& c1) const {
+        const int64_t nck = ((int64_t)cu[n + 1] - cu[n] + C - 1) / C;
+        c0 = wlen ? (wlo < nck ? wlo : nck) : 0;
+        c1 = wlen ? (wlo + wlen < nck ? wlo + wlen : nck) : nck;
+    }
     __device__ __forceinline__ bool locate(int64_t slot, int64_t& n, int64_t& c, int64_t& t0, int& L) const {
-        if (N <= 0 || base(0) > slot) return false;
-        int64_t lo = 0, hi = N - 1;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi + 1) >> 1;
-            if (base(mid) <= slot) lo = mid; else hi = mid - 1;
+        if (wlen) {
+            n = slot / wlen;
+            c = wlo + slot % wlen;
+            if (n >= N) return false;
+        } else {
+            if (N <= 0 || base(0) > slot) return false;
+            int64_t lo = 0, hi = N - 1;
+            while (lo < hi) {
+                const int64_t mid = (lo + hi + 1) >> 1;
+                if (base(mid) <= slot) lo = mid; else hi = mid - 1;
+            }
+            n = lo;
+            c = slot - base(n);
         }
-        n = lo;
-        c = slot - base(n);
         const int64_t bos = cu[n], eos = cu[n + 1];
         t0 = bos + c * C;
         if (t0 >= eos) return false;
@@ -615,9 +632,15 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
         const int i = e / kBV, j = e % kBV;
         sSt[j * LW + i] = a.s0 ? a.s0[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] : 0.f;
     }
-    const int64_t bos = mp.cu[n], eos = mp.cu[n + 1];
-    const int64_t nck = (eos - bos + C - 1) / C, slot0 = mp.base(n);
-    if (nck == 0) return;  // uniform
+    const int64_t slot0 = mp.base(n);
+    int64_t c0, c1;
+    mp.range(n, c0, c1);
+    float* s_fin = a.s_fin ? a.s_fin + ((n * H + h) * DK) * (int64_t)DV + vb * kBV : nullptr;
+    if (c0 >= c1) {  // uniform: no chunk here, the state passes through (each thread its own elements)
+        if (s_fin)
+            for (int e = tid; e < DK * kBV; e += kThreads) s_fin[(e / kBV) * DV + e % kBV] = sSt[(e % kBV) * LW + e / kBV];
+        return;
+    }
     Stage<C, DK> pW;
     Stage<DK, C> pK;
     Stage<C, kBV> pU;
@@ -629,8 +652,8 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
         pU.load(rec + R::U + vb * kBV, DV);
         pg.load(rec + R::gam, DK);
     };
-    fetch(0);
-    for (int64_t c = 0; c < nck; ++c) {
+    fetch(c0);
+    for (int64_t c = c0; c < c1; ++c) {
         float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
         lds_barrier();  // the previous chunk is done with the LDS operands; sSt is its final state
         pW.store(sW, LW);
@@ -656,9 +679,9 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
         lds_barrier();
         // the next chunk's operands and the L2 warm-up are requested here, after D: issued before
         // it, their loads held up the product that the next barrier waits for
-        fetch(c + 1 < nck ? c + 1 : c);
+        fetch(c + 1 < c1 ? c + 1 : c);
         {  // W, U and K'^T (one contiguous range) of the chunk kWarm ahead
-            const float* wrec = a.ws + ((slot0 + (c + kWarm < nck ? c + kWarm : nck - 1)) * H + h) * R::kFloats;
+            const float* wrec = a.ws + ((slot0 + (c + kWarm < c1 ? c + kWarm : c1 - 1)) * H + h) * R::kFloats;
             warm_range<R::Kd>(wrec, 0, vb, NVB, dummy);
         }
         // S <- Diag(gamma) S + K'^T D
@@ -670,6 +693,10 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
             acc = mma_k4<C / 16>(sKT + 16 * cb * LT, LT, sDt, LT, acc, lane);
             *reinterpret_cast<float4*>(sSt + lr * LW + i0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
+    }
+    if (s_fin) {  // the state after the last chunk (a checkpoint for a later window)
+        lds_barrier();
+        for (int e = tid; e < DK * kBV; e += kThreads) s_fin[(e / kBV) * DV + e % kBV] = sSt[(e % kBV) * LW + e / kBV];
     }
 }
 
@@ -703,7 +730,9 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
         sdSt[j * LW + i] = a.dsT ? a.dsT[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] : 0.f;
     }
     const int64_t bos = mp.cu[n], eos = mp.cu[n + 1];
-    const int64_t nck = (eos - bos + C - 1) / C, slot0 = mp.base(n);
+    const int64_t slot0 = mp.base(n);
+    int64_t c0, c1;
+    mp.range(n, c0, c1);
     Stage<C, DK> pK;
     Stage<C, C> pM;
     Stage<DK, C> pQ, pW;
@@ -724,8 +753,8 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
             rdo[m] = (e < C * kBV && t0 + r < eos) ? a.dO[((t0 + r) * H + h) * (int64_t)DV + vb * kBV + j] : 0.f;
         }
     };
-    if (nck > 0) fetch(nck - 1);
-    for (int64_t c = nck - 1; c >= 0; --c) {
+    if (c1 > c0) fetch(c1 - 1);
+    for (int64_t c = c1 - 1; c >= c0; --c) {
         float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
         lds_barrier();  // the previous chunk is done with the LDS operands; sdSt is its result
         pK.store(sKd, LW);
@@ -752,9 +781,9 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
         lds_barrier();
         // the previous chunk's operands and the L2 warm-up are requested here, after dD (see
         // fwd_chain)
-        fetch(c > 0 ? c - 1 : c);
+        fetch(c > c0 ? c - 1 : c);
         {  // K', Q+^T, W^T and M^T (one contiguous range) of the chunk kWarm behind
-            const float* wrec = a.ws + ((slot0 + (c >= kWarm ? c - kWarm : 0)) * H + h) * R::kFloats;
+            const float* wrec = a.ws + ((slot0 + (c - kWarm >= c0 ? c - kWarm : c0)) * H + h) * R::kFloats;
             warm_range<R::T - R::Kd>(wrec, R::Kd, vb, NVB, dummy);
         }
         // dS <- Diag(gamma) dS + Q+^T dO - W^T dD
@@ -1329,39 +1358,125 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 int64_t num_slots(int64_t N, int64_t T_total, int C) { return T_total / C + N + 1; }
 
+// Workspace plan.  One pass keeps a record for every chunk (its bytes grow with T).  When that
+// exceeds the cap, the chunks are taken in windows of wlen chunks of every sequence: a forward
+// sweep over the windows keeps only the states at window boundaries (checkpoints), then a
+// reverse sweep recomputes each window's records from its checkpoint and runs the reverse
+// chain, carrying the state gradient from one window to the one before it.  That costs a second
+// evaluation of the factors and the forward chain; the workspace is then the records of one
+// window plus the checkpoints and the carried gradient.
+struct BwdPlan {
+    bool windowed;
+    int64_t wlen, W;
+    size_t records, ckpt, carry;  // bytes
+    size_t total() const { return records + ckpt + carry; }
+};
+
+size_t workspace_cap() {
+    // default 20 GiB; KDA_BWD_WORKSPACE_CAP (bytes) overrides it, e.g. to take the windowed path
+    // at small sizes
+    const char* v = std::getenv("KDA_BWD_WORKSPACE_CAP");
+    if (v && v[0]) {
+        const unsigned long long x = std::strtoull(v, nullptr, 10);
+        if (x > 0) return (size_t)x;
+    }
+    return size_t(20) << 30;
+}
+
+BwdPlan plan_bwd(int64_t N, int64_t T_total, int H, int DK, int DV, int C, size_t rec_floats) {
+    BwdPlan p{};
+    const size_t rec = rec_floats * sizeof(float);
+    const size_t full = (size_t)num_slots(N, T_total, C) * (size_t)H * rec;
+    const size_t cap = workspace_cap();
+    if (full <= cap || N * (int64_t)H == 0 || T_total == 0) {
+        p.windowed = false;
+        p.records = full;
+        return p;
+    }
+    const size_t state = (size_t)N * H * DK * DV * sizeof(float);
+    const size_t per_chunk = (size_t)N * H * rec;  // one window chunk of every sequence
+    const int64_t nck_max = (T_total + C - 1) / C;
+    int64_t wlen = (int64_t)(cap / per_chunk);
+    if (wlen < 1) wlen = 1;
+    int64_t W = (nck_max + wlen - 1) / wlen;
+    // room for the checkpoints (one per window boundary) and the carried gradient
+    const size_t extra = (size_t)W * state;
+    if (cap > extra + per_chunk) {
+        wlen = (int64_t)((cap - extra) / per_chunk);
+        W = (nck_max + wlen - 1) / wlen;
+    }
+    p.windowed = true;
+    p.wlen = wlen;
+    p.W = W;
+    p.records = (size_t)wlen * per_chunk;
+    p.ckpt = (size_t)(W - 1) * state;
+    p.carry = state;
+    return p;
+}
+
 template <int DK, int DV, int C, typename TI>
 hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
-    const Map<C> mp{a.cu, a.N};
-    const int64_t slots = num_slots(a.N, a.T_total, C);
-    const dim3 per_chunk((unsigned)slots, (unsigned)a.H), chains((unsigned)(a.N * a.H * (DV / kBV)));
     const bool timed = timing_on();
     hipError_t e;
     constexpr size_t f_lds = FactorsLds<DK, DV, C>::kBytes, c_lds = ChunkLds<DK, DV, C>::kBytes;
     if ((e = set_lds(factors_kernel<DK, DV, C, TI>, f_lds)) != hipSuccess) return e;
     if ((e = set_lds(grad_chunk_kernel<DK, DV, C, TI>, c_lds)) != hipSuccess) return e;
-    if (a.T_total > 0) {
+    const dim3 chains((unsigned)(a.N * a.H * (DV / kBV)));
+    // the five kernels (or the first two) over the chunks that `mp` selects
+    auto run = [&](const BwdArgs& x, const Map<C>& mp, int64_t slots, bool forward_only) -> hipError_t {
+        const dim3 per_chunk((unsigned)slots, (unsigned)x.H);
         if (timed) timed_begin(kKernelBwdFactors, s);
-        hipLaunchKernelGGL((factors_kernel<DK, DV, C, TI>), per_chunk, dim3(kThreads), f_lds, s, a, mp);
+        hipLaunchKernelGGL((factors_kernel<DK, DV, C, TI>), per_chunk, dim3(kThreads), f_lds, s, x, mp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (timed) timed_end(s);
         if (timed) timed_begin(kKernelBwdFwdChain, s);
-        hipLaunchKernelGGL((fwd_chain_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, a, mp);
+        hipLaunchKernelGGL((fwd_chain_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, x, mp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (timed) timed_end(s);
-    }
-    if (timed) timed_begin(kKernelBwdRevChain, s);
-    hipLaunchKernelGGL((rev_chain_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, a, mp);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (timed) timed_end(s);
-    if (a.T_total > 0) {
+        if (forward_only) return hipSuccess;
+        if (timed) timed_begin(kKernelBwdRevChain, s);
+        hipLaunchKernelGGL((rev_chain_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, x, mp);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (timed) timed_end(s);
         if (timed) timed_begin(kKernelBwdGradState, s);
-        hipLaunchKernelGGL((grad_state_kernel<DK, DV, C>), per_chunk, dim3(kThreads), 0, s, a, mp);
+        hipLaunchKernelGGL((grad_state_kernel<DK, DV, C>), per_chunk, dim3(kThreads), 0, s, x, mp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (timed) timed_end(s);
         if (timed) timed_begin(kKernelBwdGradChunk, s);
-        hipLaunchKernelGGL((grad_chunk_kernel<DK, DV, C, TI>), per_chunk, dim3(kThreads), c_lds, s, a, mp);
+        hipLaunchKernelGGL((grad_chunk_kernel<DK, DV, C, TI>), per_chunk, dim3(kThreads), c_lds, s, x, mp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (timed) timed_end(s);
+        return hipSuccess;
+    };
+    const BwdPlan p = plan_bwd(a.N, a.T_total, a.H, DK, DV, C, Rec<DK, DV, C>::kFloats);
+    if (!p.windowed) {
+        const Map<C> mp{a.cu, a.N, 0, 0};
+        if (a.T_total > 0) return run(a, mp, num_slots(a.N, a.T_total, C), false);
+        // no tokens: only the reverse chain, which passes dL/dS_T through to dL/dS_0
+        if (timed) timed_begin(kKernelBwdRevChain, s);
+        hipLaunchKernelGGL((rev_chain_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, a, mp);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (timed) timed_end(s);
+        return hipSuccess;
+    }
+    const int64_t state = a.N * a.H * (int64_t)DK * DV;  // floats
+    float* ckpt = a.ws + p.records / sizeof(float);       // state entering window j (j >= 1) at j - 1
+    float* carry = ckpt + p.ckpt / sizeof(float);
+    auto ckpt_of = [&](int64_t j) -> const float* { return j == 0 ? a.s0 : ckpt + (j - 1) * state; };
+    const int64_t slots = a.N * p.wlen;
+    for (int64_t j = 0; j + 1 < p.W; ++j) {  // forward sweep: the checkpoints
+        BwdArgs x = a;
+        x.s0 = ckpt_of(j);
+        x.s_fin = ckpt + j * state;
+        if ((e = run(x, Map<C>{a.cu, a.N, j * p.wlen, p.wlen}, slots, true)) != hipSuccess) return e;
+    }
+    for (int64_t j = p.W - 1; j >= 0; --j) {  // reverse sweep
+        BwdArgs x = a;
+        x.s0 = ckpt_of(j);
+        x.s_fin = nullptr;
+        x.dsT = j == p.W - 1 ? a.dsT : carry;  // read at the start of each chain, then
+        x.gs0 = j == 0 ? a.gs0 : carry;        // written at its end by the same workgroup
+        if ((e = run(x, Map<C>{a.cu, a.N, j * p.wlen, p.wlen}, slots, false)) != hipSuccess) return e;
     }
     return hipSuccess;
 }
@@ -1386,7 +1501,7 @@ size_t chunk_bwd_workspace(int64_t N, int64_t T_total, int H, int dk, int dv, in
 #define KDA_BWD_DV(DK_) KDA_BWD_C(DK_, DK_)
     KDA_BWD_DV(16) KDA_BWD_DV(32) KDA_BWD_DV(64) KDA_BWD_DV(128)
 #undef KDA_BWD
-    return (size_t)num_slots(N, T_total, chunk) * (size_t)H * (size_t)per * sizeof(float);
+    return plan_bwd(N, T_total, H, dk, dv, chunk, (size_t)per).total();
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s) {

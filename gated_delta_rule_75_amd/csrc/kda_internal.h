@@ -92,6 +92,7 @@ struct BwdArgs {
     float* gbeta;      // [T_total, H]
     float* gs0;        // [N, H, dk, dv] or nullptr
     float* ws;
+    float* s_fin;      // windowed passes: the forward chain's state after the window [N, H, dk, dv], or nullptr
 };
 
 bool chunk_bwd_supported(int dk, int dv, int chunk);

@@ -264,6 +264,15 @@ int kda_append_prefill_noalloc(const void* q, const void* k, const void* v, cons
  * kda_workspace_size(KDA_OP_BACKWARD, N, T_total, H, d_k, d_v, dtype, chunk)
  * bytes, 256-byte aligned, overlapping no argument; it holds the per-chunk
  * factors, the states entering each chunk and the state gradients leaving it.
+ * That grows with T_total (about 545 KB per chunk and head at d = 128, chunk
+ * 64); when it would exceed 20 GiB (or the byte count in the environment
+ * variable KDA_BWD_WORKSPACE_CAP, read by both kda_workspace_size and the
+ * call, which must agree), the chunks are taken in windows of a fixed number
+ * of chunks of every sequence: the factors and the forward state chain run
+ * twice (a forward sweep keeping the states at window boundaries, then a
+ * reverse sweep that rebuilds each window from its checkpoint), and the
+ * workspace is one window's records plus the checkpoints.  The results are
+ * bitwise those of the one-pass evaluation.
  * The gradient outputs must not overlap one another either (KDA_ERR_ALIAS).
  * Repeated calls on the same inputs give bitwise equal results (no atomics).
  * Asynchronous on hip_stream; errors as for the other calls.

@@ -112,3 +112,29 @@ def test_backward_strong_decay(dtype, d, chunk):
     def g_of(T, H, dk):
         return -np.linspace(0.01, 8.0, dk, dtype=np.float32)[None, None, :]
     _run(dtype, d, chunk, [200, 77], True, True, g_override=g_of)
+
+
+@pytest.mark.parametrize("dtype,d,chunk,lengths,cap_chunks,head_gate", [
+    ("bf16", 128, 64, [1000, 0, 130, 700], 3, False),  # windows of a few chunks; empty and short segments
+    ("f32", 32, 16, [333, 17, 250], 5, True),           # the per-head gate through the windows
+])
+def test_backward_in_windows_equals_one_pass(monkeypatch, dtype, d, chunk, lengths, cap_chunks, head_gate):
+    """With the workspace cap lowered (KDA_BWD_WORKSPACE_CAP), the backward runs in windows of a few
+    chunks of every sequence: a forward sweep keeps the window-boundary states, a reverse sweep
+    recomputes each window from its checkpoint and carries dL/dS backwards.  Checkpoints and the
+    carried gradient are exact fp32 copies, so every gradient is bitwise the one-pass result, and
+    within the tolerance of the oracle."""
+    H = 3
+    got1, ref = _run(dtype, d, chunk, lengths, True, True, head_gate=head_gate, seed=13, H=H)
+    from gated_delta_rule_75_amd import _lib
+
+    T, N = sum(lengths), len(lengths)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    one_pass = kda.workspace_size(_lib.KDA_OP_BACKWARD, N, T, H, d, d, dt, chunk)
+    rec = one_pass // ((T // chunk + N + 1) * H)
+    monkeypatch.setenv("KDA_BWD_WORKSPACE_CAP", str(cap_chunks * N * H * rec + 1))
+    windowed = kda.workspace_size(_lib.KDA_OP_BACKWARD, N, T, H, d, d, dt, chunk)
+    assert windowed < one_pass
+    got2, _ = _run(dtype, d, chunk, lengths, True, True, head_gate=head_gate, seed=13, H=H)
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got1, got2):
+        np.testing.assert_array_equal(x, y, err_msg=name)

@@ -10,7 +10,8 @@ Workloads (seeded, see synth.workload):
   decode   256 sequences x 32 heads, 1000 in-place steps            (every pair at the first step;
                                                                      8 pairs at every step)
   varlen   8 carried states, segments of 1K..32K tokens, packed     (every head, every segment)
-  long     B=1, H=32, T=2^20, per-channel rates, then 4096 decode steps (4 heads, every token)
+  long     B=1, H=32, T=2^20, per-channel rates, then 4096 decode steps (4 heads, every token);
+           its backward (windowed) on one head's last 1,024 tokens
 """
 import numpy as np
 import pytest
@@ -196,3 +197,41 @@ def test_backward_metric_sampled_heads():
     """Gradients at the headline prefill's size (T=65,536, H=32), two heads checked."""
     w = synth.workload("metric")
     _backward_full(w, w.T, [3, 28], False)
+
+
+@pytest.mark.timeout(900)
+def test_backward_long_context_last_tokens():
+    """The chunked backward of the 2^20-token workload (all 32 heads; its one-pass workspace would
+    be about 274 GiB, so it runs in windows under the 20 GiB cap), checked on one head's last 1,024
+    tokens: the oracle's derivative over those tokens, started from the oracle's own state after
+    the first 2^20 - 1,024 tokens, with the same dL/do and dL/dS_T."""
+    from gated_delta_rule_75_amd import _lib
+
+    w = synth.workload("long")
+    T, H, d, n, h = w.T, w.H, w.dk, 1024, 11
+    ws = kda.workspace_size(_lib.KDA_OP_BACKWARD, 1, T, H, d, d, torch.bfloat16, 64)
+    assert ws <= 24 << 30
+    print(f"[long] backward: generate T={T} H={H} (workspace {ws / 2**30:.1f} GiB)", flush=True)
+    q, k, v, g, b = synth.gen_tokens(w, T)
+    d_out, d_sT = synth.gen_cotangents(w, T, 1)
+    cu = np.array([0, T], np.int32)
+    print("[long] gpu backward", flush=True)
+    grads = kda.chunked_backward(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(g, "f32"), dev(b, "bf16"),
+                                 torch.from_numpy(cu).cuda(), None, d_out=dev(d_out, "f32"),
+                                 d_state_out=dev(d_sT, "f32"), chunk=64, state_grad=False)
+    torch.cuda.synchronize()
+    got = [host(x[T - n:, h:h + 1]) for x in grads[:5]]
+    for x in grads[:5]:
+        assert torch.isfinite(x).all()
+    del grads
+    torch.cuda.empty_cache()
+    print(f"[long] oracle: forward over {T - n} tokens, derivative over the last {n} (head {h})", flush=True)
+    wide = _heads((q, k, v, g, b), [h], "bf16")
+    del q, k, v, g, b
+    _, s_mid = oracle.recurrence(*(x[:T - n] for x in wide), vcols=8)
+    ref = oracle.backward(*(x[T - n:] for x in wide), None, s_mid, d_o=d_out[T - n:, h:h + 1],
+                          d_sT=d_sT[:, h:h + 1])
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dbeta"), got, ref[:5]):
+        if x.ndim == 2:
+            x, y = x[:, :, None], y[:, :, None]
+        assert_close(x, y, TOL, None, name)
