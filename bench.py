@@ -56,11 +56,11 @@ DECODE_BYTES_PER_SEQ_HEAD = 65536 + 65536 + 768 + 512 + 2 + 512         # 132866
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 _KIB = 1024
 _MFMA_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_mfma.hip"
-_MFMA_SHA = "82df15bd320934547fe32a598f83e22a2b4bf160e4e56b607563d4f43466cf6b"
+_MFMA_SHA = "6e1135a7cc1dfa9baa4ab61c2635cf9eadff27018a858962f3e322cb3e3ed2ad"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
-_DECODE_SHA = "0efe675059ee1ae0f51f5a31a1c1c41ff8e96536686270e3140e8030e17def42"
+_DECODE_SHA = "b22d0839d069d021330e24ebbe84d22337c50dc6103a3037d6ec9e2d244feec8"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
-_BWD_SHA = "8786058cb8a1138ef1c2d6bb948ce3ab30a8322623f3ac08012fc9d6ff0c903b"
+_BWD_SHA = "6bfb6e9b17f3036f05488d8be5c7cedc4ca7bb3de3a7a6d9a0f4a89af8f0acb7"
 
 
 def _counted(fetch_kib, write_kib):
@@ -70,15 +70,15 @@ def _counted(fetch_kib, write_kib):
 # kernel name -> where and on what it was measured, and HBM bytes per launch
 MEASURED_TRAFFIC = {
     "kda_prep": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                 "bytes": _counted(1065139.0, 2114563.2)},
+                 "bytes": _counted(1065146.0, 1983489.4)},
     "kda_state": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                  "bytes": _counted(1337457.1, 1052735.4)},
+                  "bytes": _counted(1270852.0, 1050775.4)},
     "kda_decode": {"source": _DECODE_SRC, "sha256": _DECODE_SHA, "workload": "decode N=256 H=32",
-                   "bytes": _counted(267360.2, 528567.1)},
+                   "bytes": _counted(267357.4, 528584.8)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
     "kda_backward": {"source": _BWD_SRC, "sha256": _BWD_SHA, "workload": "backward T=65536 H=32",
-                     "bytes": _counted(3539131.8 + 1602078.2 + 2429950.4 + 3787802.2 + 9393159.3,
-                                       7881839.4 + 3381197.9 + 3390170.0 + 3686916.1 + 4522661.3)},
+                     "bytes": _counted(3556843.1 + 1599053.6 + 2431122.1 + 3791090.6 + 9349948.4,
+                                       7882187.4 + 3317428.8 + 3288020.8 + 3686842.7 + 4488661.2)},
 }
 
 
@@ -101,7 +101,7 @@ def traffic_of(kernel, workload=None):
 # prefill MFMA utilisation from rocprofv3 --pmc MfmaUtil (percent of cycles the matrix cores are
 # busy, per kernel), on the kernel source named by its SHA-256 (profiles/prefill_mfma_utilisation_*)
 MEASURED_MFMA_UTIL = {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                      "kda_prep": 0.063, "kda_state": 0.099}
+                      "kda_prep": 0.062, "kda_state": 0.098}
 # the algorithmic MFMA fraction at the HBM roofline: 139,264 flop per 1,794 B at 8 TB/s = 621
 # TFLOP/s, 24.8% of the dense fp16/bf16 peak
 MFMA_CEILING_AT_HBM_ROOFLINE = PREFILL_FLOP_PER_TOKEN_HEAD / PREFILL_BYTES_PER_TOKEN_HEAD * HBM_PEAK_GBPS / 1e3 / \
@@ -797,8 +797,9 @@ def bench_workloads(args, res):
         "decode_steps": steps, "decode_us_per_step": round(dms * 1e3 / steps, 2),
         "decode_steps_per_s": round(steps / (dms * 1e-3), 1),
         "decode_kernel_avg_us": round(sum(kus) / len(kus), 2),
-        "decode_note": "one sequence: 32 workgroups per step, bound by launch latency, not by HBM; the "
-                       "per-step time includes the host's calls through the Python binding",
+        "decode_note": "one sequence: each head's state split over 8 workgroups of 16 columns (256 per "
+                       "step); bound by launch and memory latency, not by HBM; the per-step time includes "
+                       "the host's calls through the Python binding",
         "parity": {"head": h, "prefill_tokens_checked": T, "decode_steps_checked": steps, "max_rel_err": err,
                    "tol": 2e-3, "ok": bool(err <= 2e-3), "oracle_s": round(t_or, 1)}}
     log(f"[long] prefill {ms:.2f} ms ({T / (ms * 1e-3) / 1e6:.2f} M tokens/s), decode {dms * 1e3 / steps:.1f} "
