@@ -52,6 +52,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;   // tokens per chunk
 constexpr int DK = 128;
@@ -136,10 +137,36 @@ __device__ __forceinline__ floatx4 mm16(const float* Ap, int lda, const float* B
 // ------------------------------------------------------------------------------------------
 // prep kernel: one workgroup (4 waves) per (slot, head); wave w owns token block w
 // ------------------------------------------------------------------------------------------
+// Buffer descriptor for `bytes` bytes at `base`.  Both are wave-uniform here; reading them
+// through readfirstlane tells the compiler so (a descriptor it cannot prove uniform is
+// wrapped in a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void* up = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(up, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// The prep kernel keeps log-decays in base-2 units (G * log2(e)), so that every decay factor is
+// one hardware exp2 with no scaling multiply.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// the diagonal-tile factors leave the fp16 range beyond e^10 = 2^(10 log2 e)
+constexpr float kDiagBound2 = 10.f * kLog2e;
+
+// 8 consecutive floats of an LDS table (32-byte aligned) as two 128-bit reads
+__device__ __forceinline__ void ld8(const float* p, float (&o)[8]) {
+    const float4 x = *reinterpret_cast<const float4*>(p), y = *reinterpret_cast<const float4*>(p + 4);
+    o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    o[4] = y.x; o[5] = y.y; o[6] = y.z; o[7] = y.w;
+}
+
 // 16-byte aligned, so that the compiler may use 128-bit LDS accesses for the fragment and
 // table rows (with the 4-byte alignment of its members it splits every access into 32-bit ones)
 struct alignas(16) PrepLds {
     // per key channel, per 16-token block b (all fp32):
+    // log-decays in base-2 units; factors are 2^(...) = e^(natural-log value)
     float tot[4][DK];     // D_b = sum of g over block b
     float gmid[4][DK];    // within-block cumulative g at the block's 8th token
     float eP[4][DK];      // exp(P_b), P_b = G at the end of block b-1 (0 for b = 0)
@@ -147,11 +174,7 @@ struct alignas(16) PrepLds {
     float emr[4][DK];     // exp(-gmid_b): diagonal-block row factor = exp(gloc) * emr
     float emc[4][DK];     // exp(gmid_b - D_b): diagonal-block column factor = exp(D_b - gloc) * emc
     float Z[3][DK];       // decay between blocks: pairs (2,0), (3,1): exp(D_1), exp(D_2); (3,0): exp(D_1 + D_2)
-    union {
-        _Float16 kdT[DK][C + 8];   // K'^T (transposed through LDS)
-        _Float16 W[C][DK + 8];     // W = T Diag(beta) K+, fp16, after K'^T has been written out
-    } o;
-    _Float16 M[C][C + 8];          // M, fp16
+    _Float16 kdT[DK][C + 8];       // K'^T (transposed through LDS)
     float AT[C][C + 1];            // A below the block diagonal; T on and above it (see inverse)
     union {
         _Float16 kc[3][4][64][8];  // off-diagonal column operands of blocks 0..2, fragment order
@@ -183,8 +206,17 @@ __device__ __forceinline__ float* t_block(PrepLds& L, int i, int j) {
     return i == j ? &L.AT[16 * i][16 * i] : &L.AT[16 * j][16 * i];
 }
 
+// A matrix-core product with the operands in swapped order leaves lane (lr, lg) holding four
+// consecutive columns 4*lg .. 4*lg+3 of row lr of the 16 x 16 result tile.  Those four values
+// are half of one lane's 16-byte operand fragment in a record tile: column block cb (16 wide)
+// of a row block lands in k-step cb / 2, fragment lane 16 * (2 * (cb & 1) + lg / 2) + lr, bytes
+// 8 * (lg & 1) .. +7.  Returns the byte offset of that half inside the tile.
+__device__ __forceinline__ int frag_half_offset(int cb, int lr, int lg) {
+    return (16 * (2 * (cb & 1) + (lg >> 1)) + lr) * 16 + 8 * (lg & 1);
+}
+
 // bfloat16 element i (0..7) of a packed 8-element row fragment
-__device__ __forceinline__ uint32_t bf_elem(const uint4& v, int i) {
+__device__ __forceinline__ uint32_t bf_elem(const u32x4& v, int i) {
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
     return (i & 1) ? (wv[i >> 1] >> 16) : (wv[i >> 1] & 0xFFFF);
 }
@@ -222,55 +254,62 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
     }
 
     // ---- this lane: token r = 16w + lr, channels 32*ks + 8*lg + i (the matrix-core operand
-    //      layout); rows past the chunk end load a clamped row and are zeroed
+    //      layout).  The inputs are read through descriptors that end at the chunk's last token,
+    //      so rows past it read 0 (zero keys, queries and log-decays) with no clamping or selects.
     const int r = 16 * w + lr;
     const bool valid = r < Lc;
-    const int64_t rowk = ((t0 + (valid ? r : Lc - 1)) * H + h) * (int64_t)DK;
-    uint4 kv[4], qv[4];
+    const int64_t rowH = (int64_t)H * DK;  // elements between consecutive tokens
+    const int64_t row0 = (t0 * H + h) * (int64_t)DK;
+    const uint32_t span = (uint32_t)((Lc - 1) * rowH + DK);  // elements from row 0 to the last row's end
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + row0, span * 2), qrs = make_rsrc(q + row0, span * 2);
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(beta + t0 * H + h, (uint32_t)(((Lc - 1) * H + 1) * 2));
+    const int lofs = (int)(r * rowH + 8 * lg);  // this lane's first element
+    u32x4 kv[4], qv[4];
     float4 gv[8];
     // g first: the decay scan needs it before anything else (with one gate per head, the
     // token's single log-decay on every channel)
     if (a.gate_head) {
-        float gs = a.g[(t0 + (valid ? r : Lc - 1)) * H + h];
-        if (PRO) gs = gate_from_raw(gs, a.gate_scale);
+        const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.g + t0 * H + h, (uint32_t)(((Lc - 1) * H + 1) * 4));
+        float gs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, r * H * 4, 0, 0));
+        if (PRO) gs = valid ? gate_from_raw(gs, a.gate_scale) : 0.f;
+        gs *= kLog2e;
 #pragma unroll
         for (int j = 0; j < 8; ++j) gv[j] = make_float4(gs, gs, gs, gs);
     } else {
+        const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.g + row0, span * 4);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int c0 = 32 * ks + 8 * lg;
-            gv[2 * ks] = *reinterpret_cast<const float4*>(a.g + rowk + c0);
-            gv[2 * ks + 1] = *reinterpret_cast<const float4*>(a.g + rowk + c0 + 4);
+            gv[2 * ks] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(grs, lofs * 4, 128 * ks, 0));
+            gv[2 * ks + 1] =
+                __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(grs, lofs * 4, 128 * ks + 16, 0));
         }
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const int c0 = 32 * ks + 8 * lg;
-        kv[ks] = *reinterpret_cast<const uint4*>(k + rowk + c0);
-        qv[ks] = *reinterpret_cast<const uint4*>(q + rowk + c0);
+        kv[ks] = __builtin_amdgcn_raw_buffer_load_b128(krs, lofs * 2, 64 * ks, 0);
+        qv[ks] = __builtin_amdgcn_raw_buffer_load_b128(qrs, lofs * 2, 64 * ks, 0);
     }
     // beta of this lane's token and of the accumulator rows 16w + 4lg + i, requested with the
-    // other inputs so that their latency does not open a later phase
-    const uint16_t beta_r = beta[(t0 + (valid ? r : Lc - 1)) * H + h];
+    // other inputs so that their latency does not open a later phase (0 past the chunk end)
+    const uint16_t beta_r = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, r * H * 2, 0, 0);
     uint16_t beta_q[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * w + 4 * lg + i;
-        beta_q[i] = beta[(t0 + (rr < Lc ? rr : Lc - 1)) * H + h];
-    }
-    // g as floats (zero past the chunk end); k, q stay packed bf16 until used
+    for (int i = 0; i < 4; ++i)
+        beta_q[i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, (16 * w + 4 * lg + i) * H * 2, 0, 0);
+    // g as floats in base-2 units (zero past the chunk end); k, q stay packed bf16 until used
     float gl[4][8];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const float4 g0 = gv[2 * ks], g1 = gv[2 * ks + 1];
         gl[ks][0] = g0.x; gl[ks][1] = g0.y; gl[ks][2] = g0.z; gl[ks][3] = g0.w;
         gl[ks][4] = g1.x; gl[ks][5] = g1.y; gl[ks][6] = g1.z; gl[ks][7] = g1.w;
-        if (PRO && !a.gate_head) {
+        if (!a.gate_head) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) gl[ks][i] = gate_from_raw(gl[ks][i], a.gate_scale);
+            for (int i = 0; i < 8; ++i) {
+                if (PRO) gl[ks][i] = valid ? gate_from_raw(gl[ks][i], a.gate_scale) : 0.f;
+                gl[ks][i] *= kLog2e;
+            }
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gl[ks][i] = valid ? gl[ks][i] : 0.f;
     }
 
     // ---- within-block inclusive cumulative sum of g over the 16 tokens (16-lane rows)
@@ -303,17 +342,17 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float gm = L.gmid[b][ch];
-            L.eP[b][ch] = fast_exp(Pb[b]);
-            L.etail[b][ch] = fast_exp(Ct - Pb[b] - Db[b]);
-            L.emr[b][ch] = fast_exp(-gm);
-            L.emc[b][ch] = fast_exp(gm - Db[b]);
+            L.eP[b][ch] = exp2_hw(Pb[b]);
+            L.etail[b][ch] = exp2_hw(Ct - Pb[b] - Db[b]);
+            L.emr[b][ch] = exp2_hw(-gm);
+            L.emc[b][ch] = exp2_hw(gm - Db[b]);
             // diagonal-block factors are bounded by exp(-gm) (rows) and exp(gm - D_b) (columns);
             // beyond e^10 they leave the fp16 range, and the chunk is redone by the second pass
-            bad |= (-gm > 10.f) || (gm - Db[b] > 10.f);
+            bad |= (-gm > kDiagBound2) || (gm - Db[b] > kDiagBound2);
         }
-        L.Z[0][ch] = fast_exp(d1);
-        L.Z[1][ch] = fast_exp(d2);
-        L.Z[2][ch] = fast_exp(d1 + d2);
+        L.Z[0][ch] = exp2_hw(d1);
+        L.Z[1][ch] = exp2_hw(d2);
+        L.Z[2][ch] = exp2_hw(d1 + d2);
         if (bad) L.exact_diag = 1;  // benign race: every writer stores 1
     }
     __syncthreads();
@@ -352,6 +391,7 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
     // G_rc - G_sc <= 0.  The lanes of row r sum their 8 channels of each k-step for every column
     // s of the block (row s sits in lane s of the same 16-lane row), add their partial sums, and
     // keep their own four columns.
+    float exact_pmax = 0.f;
     if (EXACT) {
         float accA[4] = {0.f, 0.f, 0.f, 0.f}, accM[4] = {0.f, 0.f, 0.f, 0.f};  // columns 4*lg + j
 #pragma unroll
@@ -359,8 +399,8 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
             float kk[8], qq[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                kk[i] = valid ? bf(bf_elem(kv[ks], i)) * inv_k : 0.f;
-                qq[i] = valid ? bf(bf_elem(qv[ks], i)) * inv_q : 0.f;
+                kk[i] = bf(bf_elem(kv[ks], i)) * inv_k;
+                qq[i] = bf(bf_elem(qv[ks], i)) * inv_q;
             }
 #pragma unroll 1
             for (int s2 = 0; s2 < 16; ++s2) {
@@ -368,7 +408,7 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float ksv = __shfl(kk[i], 16 * lg + s2, 64), gs = __shfl(gl[ks][i], 16 * lg + s2, 64);
-                    const float e = fast_exp(fminf(gl[ks][i] - gs, 0.f)) * ksv;
+                    const float e = exp2_hw(fminf(gl[ks][i] - gs, 0.f)) * ksv;
                     pa += kk[i] * e;
                     pm += qq[i] * e;
                 }
@@ -384,12 +424,17 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
                 }
             }
         }
+        // accM holds M[r][16w + 4lg + j]: the layout of a swapped-operand product (see
+        // frag_half_offset), stored straight into the record
+        half4 mh;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int s2 = 4 * lg + j;
             L.AT[r][16 * w + s2] = (s2 < lr) ? brow_r * accA[j] : 0.f;
-            L.M[r][16 * w + s2] = (_Float16)((s2 <= lr) ? accM[j] : 0.f);
+            mh[j] = (_Float16)((s2 <= lr) ? accM[j] : 0.f);
+            exact_pmax = fmaxf(exact_pmax, __builtin_fabsf((float)mh[j]));
         }
+        *reinterpret_cast<half4*>(rec + kOffM + t6(w, w >> 1) * kTile + frag_half_offset(w, lr, lg)) = mh;
     }
     half8 KR[4], QR[4], BKp[4];
     floatx4 diagA = {0.f, 0.f, 0.f, 0.f}, diagM = {0.f, 0.f, 0.f, 0.f};  // tile (w, w)
@@ -401,33 +446,40 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
         half8 kp, qp, kc, krd, qrd, kcd;
         const uint32_t kw[4] = {kv[ks].x, kv[ks].y, kv[ks].z, kv[ks].w};
         const uint32_t qw[4] = {qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w};
+        // this k-step's 8 channels of the factor tables, read together
+        const int c0 = 32 * ks + 8 * lg;
+        float ttot[8], tep[8], ttail[8], tmr[8], tmc[8];
+        ld8(&L.tot[w][c0], ttot);
+        ld8(&L.eP[w][c0], tep);
+        ld8(&L.etail[w][c0], ttail);
+        ld8(&L.emr[w][c0], tmr);
+        ld8(&L.emc[w][c0], tmc);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int ch = 32 * ks + 8 * lg + i;
+            const int ch = c0 + i;
             const float gloc = gl[ks][i];
             const uint32_t kb16 = (i & 1) ? (kw[i >> 1] >> 16) : (kw[i >> 1] & 0xFFFF);
             const uint32_t qb16 = (i & 1) ? (qw[i >> 1] >> 16) : (qw[i >> 1] & 0xFFFF);
-            const float kk = valid ? bf(kb16) * inv_k : 0.f, qq = valid ? bf(qb16) * inv_q : 0.f;
+            const float kk = bf(kb16) * inv_k, qq = bf(qb16) * inv_q;
             qkmax = fmaxf(qkmax, fmaxf(__builtin_fabsf(kk), __builtin_fabsf(qq)));
-            const float eloc = fast_exp(gloc);              // exp(G_r - P_w)          <= 1
-            const float ecol = fast_exp(L.tot[w][ch] - gloc);  // exp(P_{w+1} - G_r)   <= 1
-            const float ep = L.eP[w][ch];
-            kp[i] = (_Float16)(kk * eloc * ep * brow_r);
-            qp[i] = (_Float16)(qq * eloc * ep);
-            L.o.kdT[ch][r] = (_Float16)(kk * ecol * L.etail[w][ch]);
-            KR[ks][i] = (_Float16)(kk * eloc);
-            QR[ks][i] = (_Float16)(qq * eloc);
-            kc[i] = (_Float16)(kk * ecol);
-            const float erd = eloc * L.emr[w][ch], ecd = ecol * L.emc[w][ch];
-            krd[i] = (_Float16)(kk * erd);
-            qrd[i] = (_Float16)(qq * erd);
-            kcd[i] = (_Float16)(kk * ecd);
+            const float eloc = exp2_hw(gloc);            // exp(G_r - P_w)          <= 1
+            const float ecol = exp2_hw(ttot[i] - gloc);  // exp(P_{w+1} - G_r)      <= 1
+            const float kl = kk * eloc, ql = qq * eloc, kcf = kk * ecol;
+            kp[i] = (_Float16)(kl * (tep[i] * brow_r));
+            qp[i] = (_Float16)(ql * tep[i]);
+            L.kdT[ch][r] = (_Float16)(kcf * ttail[i]);
+            KR[ks][i] = (_Float16)kl;
+            QR[ks][i] = (_Float16)ql;
+            kc[i] = (_Float16)kcf;
+            krd[i] = (_Float16)(kl * tmr[i]);
+            qrd[i] = (_Float16)(ql * tmr[i]);
+            kcd[i] = (_Float16)(kcf * tmc[i]);
         }
         // diagonal Gram tile (w, w): this lane's operands are both the row and the column
         // fragments, so it accumulates k-step by k-step with nothing exchanged
         if (!EXACT) {
             diagA = mfma16x16x32(krd, kcd, diagA);
-            diagM = mfma16x16x32(qrd, kcd, diagM);
+            diagM = mfma16x16x32(kcd, qrd, diagM);  // swapped: lane holds M[r][16w + 4lg + i]
         }
         BKp[ks] = kp;  // Diag(beta) K+, consumed by W after T is known
         *reinterpret_cast<half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16) = qp;
@@ -449,25 +501,29 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
     }
     // largest magnitude among the M, T and W values this lane rounds to fp16 (a running maximum;
     // a NaN leaves it unchanged and stays NaN in every result, as on the fp32 path)
-    float pmax = 0.f;
-    if (!EXACT) {  // the second pass has its exact tile in place already
-        const floatx4 accA = diagA, accM = diagM;
-        // accumulator: column s = lr of block j, rows 4*lg + i of block w
+    float pmax = exact_pmax;
+    unsigned char* mrec = rec + kOffM;
+    if (!EXACT) {  // the second pass has its exact tiles in place already
+        // A accumulator: column s = lr of block w, rows 4*lg + i of block w
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rr = 16 * w + 4 * lg + i, ss = 16 * w + lr;
-            L.AT[rr][ss] = (ss < rr) ? brow[i] * accA[i] : 0.f;
-            const float mv = (ss <= rr) ? accM[i] : 0.f;
-            pmax = fmaxf(pmax, __builtin_fabsf(mv));
-            L.M[rr][ss] = (_Float16)mv;
+            L.AT[rr][ss] = (ss < rr) ? brow[i] * diagA[i] : 0.f;
         }
-    } else {
+        // M accumulator (swapped operands): row r = 16w + lr, columns 16w + 4lg + i
+        half4 mh;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pmax = fmaxf(pmax, __builtin_fabsf((float)L.M[r][16 * w + 4 * lg + j]));
+        for (int i = 0; i < 4; ++i) {
+            const float mv = (4 * lg + i <= lr) ? diagM[i] : 0.f;
+            pmax = fmaxf(pmax, __builtin_fabsf(mv));
+            mh[i] = (_Float16)mv;
+        }
+        *reinterpret_cast<half4*>(mrec + t6(w, w >> 1) * kTile + frag_half_offset(w, lr, lg)) = mh;
     }
-    for (int j = w + 1; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) L.M[16 * w + 4 * lg + i][16 * j + lr] = (_Float16)0.f;
+    // the stored M tiles of row blocks 0 and 2 also span the (zero) block to the right of the diagonal
+    if (!(w & 1))
+        *reinterpret_cast<half4*>(mrec + t6(w, w >> 1) * kTile + frag_half_offset(w + 1, lr, lg)) =
+            half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
     __syncthreads();
     for (int j = 0; j < w; ++j) {
         floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
@@ -476,19 +532,23 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
         for (int ks = 0; ks < 4; ++ks) {
             half8 bcol = *reinterpret_cast<const half8*>(&L.u.kc[j][ks][lane][0]);
             if (j + 1 < w) {  // scale by exp(P_w - P_{j+1}), the decay of blocks j+1 .. w-1
+                float z[8];
+                ld8(&L.Z[zi][32 * ks + 8 * lg], z);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) bcol[i] = (_Float16)((float)bcol[i] * L.Z[zi][32 * ks + 8 * lg + i]);
+                for (int i = 0; i < 8; ++i) bcol[i] = (_Float16)((float)bcol[i] * z[i]);
             }
             accA = mfma16x16x32(KR[ks], bcol, accA);
-            accM = mfma16x16x32(QR[ks], bcol, accM);
+            accM = mfma16x16x32(bcol, QR[ks], accM);  // swapped: lane holds M[16w + lr][16j + 4lg + i]
         }
+        half4 mh;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rr = 16 * w + 4 * lg + i, ss = 16 * j + lr;
             L.AT[rr][ss] = brow[i] * accA[i];
             pmax = fmaxf(pmax, __builtin_fabsf(accM[i]));
-            L.M[rr][ss] = (_Float16)accM[i];
+            mh[i] = (_Float16)accM[i];
         }
+        *reinterpret_cast<half4*>(mrec + t6(w, j >> 1) * kTile + frag_half_offset(j, lr, lg)) = mh;
     }
     __syncthreads();
 
@@ -536,65 +596,55 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
 #pragma unroll
         for (int i = 0; i < 8; ++i) L.u.bkT[32 * ks + 8 * lg + i][r] = BKp[ks][i];
 
-    // ---- write T, M (8 tiles each) and K'^T (16 tiles) as fp16 operand tiles
-    for (int t = w; t < 8; t += 4) {
-        const int rb = t >> 1, kb = t & 1;
-        if (rb < 2 && kb == 1) continue;  // all zero, not stored
-        half8 tv;
+    // ---- write K'^T (16 tiles) as fp16 operand tiles
+    for (int t = w; t < 16; t += 4) {
+        const int cb = t >> 1, ks = t & 1;
+        const half8 kd = *reinterpret_cast<const half8*>(&L.kdT[16 * cb + lr][32 * ks + 8 * lg]);
+        *reinterpret_cast<half8*>(rec + kOffKdT + t * kTile + lane * 16) = kd;
+    }
+    __syncthreads();  // Diag(beta) K+ staged
+
+    // ---- T rows of block w: the record's T tiles (w, kb) in operand order, and the right-hand
+    //      operand of W^T below (zero above the diagonal)
+    half8 ta[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int col = 32 * kb + 8 * lg + i, cb = col >> 4;
-            float val = 0.f;
-            if (cb <= rb) val = t_block(L, rb, cb)[lr * (C + 1) + (col & 15)];
+            const float val = cb <= w ? t_block(L, w, cb)[lr * (C + 1) + (col & 15)] : 0.f;
             pmax = fmaxf(pmax, __builtin_fabsf(val));
-            tv[i] = (_Float16)val;
+            ta[kb][i] = (_Float16)val;
         }
-        *reinterpret_cast<half8*>(rec + kOffT + t6(rb, kb) * kTile + lane * 16) = tv;
-        *reinterpret_cast<half8*>(rec + kOffM + t6(rb, kb) * kTile + lane * 16) =
-            *reinterpret_cast<const half8*>(&L.M[16 * rb + lr][32 * kb + 8 * lg]);
-    }
-    for (int t = w; t < 16; t += 4) {
-        const int cb = t >> 1, ks = t & 1;
-        const half8 kd = *reinterpret_cast<const half8*>(&L.o.kdT[16 * cb + lr][32 * ks + 8 * lg]);
-        *reinterpret_cast<half8*>(rec + kOffKdT + t * kTile + lane * 16) = kd;
-    }
-    __syncthreads();  // K'^T read out of its union (W overwrites it); Diag(beta) K+ staged
+    *reinterpret_cast<half8*>(rec + kOffT + t6(w, 0) * kTile + lane * 16) = ta[0];
+    if (w >= 2) *reinterpret_cast<half8*>(rec + kOffT + t6(w, 1) * kTile + lane * 16) = ta[1];
 
-    // ---- W = T Diag(beta) K+ (64 x 128): rows of token block w, all 8 channel blocks
-    {
-        half8 ta[2];  // T rows of block w as matrix-core A operand, k-steps 0..1 (zero above the diagonal)
+    // ---- W = T Diag(beta) K+ (64 x 128), rows of token block w, as W^T = (Diag(beta) K+)^T T^T
+    //      tiles: each lane then holds 4 consecutive channels of its token row and stores them
+    //      straight into the record (see frag_half_offset)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
+            acc = mfma16x16x32(*reinterpret_cast<const half8*>(&L.u.bkT[16 * cb + lr][32 * kb + 8 * lg]), ta[kb],
+                               acc);
+        half4 wh;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int col = 32 * kb + 8 * lg + i, cb = col >> 4;
-                ta[kb][i] = (_Float16)(cb <= w ? t_block(L, w, cb)[lr * (C + 1) + (col & 15)] : 0.f);
-            }
-        for (int cb = 0; cb < 8; ++cb) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                acc = mfma16x16x32(ta[kb], *reinterpret_cast<const half8*>(&L.u.bkT[16 * cb + lr][32 * kb + 8 * lg]),
-                                   acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pmax = fmaxf(pmax, __builtin_fabsf(acc[i]));
-                L.o.W[16 * w + 4 * lg + i][16 * cb + lr] = (_Float16)acc[i];
-            }
+        for (int i = 0; i < 4; ++i) {
+            pmax = fmaxf(pmax, __builtin_fabsf(acc[i]));
+            wh[i] = (_Float16)acc[i];
         }
+        *reinterpret_cast<half4*>(rec + kOffW + (w * 4 + (cb >> 1)) * kTile + frag_half_offset(cb, lr, lg)) = wh;
     }
     if (!(qkmax < 32768.f) || !(pmax < 65504.f)) L.range_bad = 1;  // benign race: every writer stores 1
     __syncthreads();
     if (threadIdx.x == 0) *flag = (L.exact_diag ? kFlagExact : 0) | (L.range_bad ? kFlagRange : 0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        *reinterpret_cast<half8*>(rec + kOffW + (w * 4 + ks) * kTile + lane * 16) =
-            *reinterpret_cast<const half8*>(&L.o.W[16 * w + lr][32 * ks + 8 * lg]);
 
     if (w == 0) {
         float* gam = reinterpret_cast<float*>(rec + kOffGamma);
         for (int ch = lane; ch < DK; ch += 64)
-            gam[ch] = fast_exp(L.tot[0][ch] + L.tot[1][ch] + L.tot[2][ch] + L.tot[3][ch]);
+            gam[ch] = exp2_hw(L.tot[0][ch] + L.tot[1][ch] + L.tot[2][ch] + L.tot[3][ch]);
     }
     return !EXACT && L.exact_diag != 0;  // final since the factor tables' barrier
 }
@@ -625,18 +675,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillArgs a, SeqMap sm, 
 // the state (update).  Two LDS exchanges per chunk: D (all tokens, for M D and K'^T D) and S1
 // (all channels, for the next chunk's products).  beta*V of the next chunk is staged in LDS,
 // in the matrix-core B layout, in the same pass.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor for `bytes` bytes at `base`.  Both are wave-uniform here; reading them
-// through readfirstlane tells the compiler so (a descriptor it cannot prove uniform is
-// wrapped in a per-lane loop).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-    void* up = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(up, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
 
 // Operands of one chunk as held by one lane of compute wave w.
 struct ChunkFrags {
