@@ -126,14 +126,6 @@ struct SeqMap {
 
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_to_f32(b); }
 
-// 16x16 = A(16x16) * B(16x16), fp32 operands from LDS (row strides lda, ldb), four 16x16x4 steps.
-__device__ __forceinline__ floatx4 mm16(const float* Ap, int lda, const float* Bp, int ldb, floatx4 acc, int lane) {
-    const int r = lane & 15, kq = lane >> 4;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x4f32(Ap[r * lda + 4 * ks + kq], Bp[(4 * ks + kq) * ldb + r], acc);
-    return acc;
-}
-
 // ------------------------------------------------------------------------------------------
 // prep kernel: one workgroup (4 waves) per (slot, head); wave w owns token block w
 // ------------------------------------------------------------------------------------------
@@ -178,7 +170,6 @@ struct alignas(16) PrepLds {
     float AT[C][C + 1];            // A below the block diagonal; T on and above it (see inverse)
     union {
         _Float16 kc[3][4][64][8];  // off-diagonal column operands of blocks 0..2, fragment order
-        float X[4][16][17];        // per-wave scratch of the inverse
         _Float16 bkT[DK][C + 8];   // Diag(beta) K+ as [channel][token]: B operand of W
     } u;
     int exact_diag;  // some channel's 8-token decay is beyond the fp16 factors
@@ -525,37 +516,11 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
         *reinterpret_cast<half4*>(mrec + t6(w, w >> 1) * kTile + frag_half_offset(w + 1, lr, lg)) =
             half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
     __syncthreads();
-    for (int j = 0; j < w; ++j) {
-        floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
-        const int zi = (w - j == 2) ? (w == 2 ? 0 : 1) : 2;  // Z table of pair (w, j) when j + 1 < w
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            half8 bcol = *reinterpret_cast<const half8*>(&L.u.kc[j][ks][lane][0]);
-            if (j + 1 < w) {  // scale by exp(P_w - P_{j+1}), the decay of blocks j+1 .. w-1
-                float z[8];
-                ld8(&L.Z[zi][32 * ks + 8 * lg], z);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) bcol[i] = (_Float16)((float)bcol[i] * z[i]);
-            }
-            accA = mfma16x16x32(KR[ks], bcol, accA);
-            accM = mfma16x16x32(bcol, QR[ks], accM);  // swapped: lane holds M[16w + lr][16j + 4lg + i]
-        }
-        half4 mh;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 16 * w + 4 * lg + i, ss = 16 * j + lr;
-            L.AT[rr][ss] = brow[i] * accA[i];
-            pmax = fmaxf(pmax, __builtin_fabsf(accM[i]));
-            mh[i] = (_Float16)accM[i];
-        }
-        *reinterpret_cast<half4*>(mrec + t6(w, j >> 1) * kTile + frag_half_offset(j, lr, lg)) = mh;
-    }
-    __syncthreads();
-
-    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (lane = column);
-    //      T_ww overwrites A_ww (no longer needed)
-    if (lane < 16) {
-        const int j = lane, o = 16 * w;
+    if (w == 0) {
+        // ---- T = (I + A)^{-1}, diagonal 16x16 blocks by forward substitution: wave 0 inverts all
+        //      four at once (lanes 16q .. 16q+15: block q, lane = column) while waves 1..3 form the
+        //      off-diagonal Gram tiles; T_qq overwrites A_qq (no longer needed)
+        const int j = lr, o = 16 * lg;
         float tc[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
@@ -566,26 +531,67 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
         }
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) L.AT[o + rr][o + j] = tc[rr];
+    } else {
+        for (int j = 0; j < w; ++j) {
+            floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+            const int zi = (w - j == 2) ? (w == 2 ? 0 : 1) : 2;  // Z table of pair (w, j) when j + 1 < w
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                half8 bcol = *reinterpret_cast<const half8*>(&L.u.kc[j][ks][lane][0]);
+                if (j + 1 < w) {  // scale by exp(P_w - P_{j+1}), the decay of blocks j+1 .. w-1
+                    float z[8];
+                    ld8(&L.Z[zi][32 * ks + 8 * lg], z);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) bcol[i] = (_Float16)((float)bcol[i] * z[i]);
+                }
+                accA = mfma16x16x32(KR[ks], bcol, accA);
+                accM = mfma16x16x32(bcol, QR[ks], accM);  // swapped: lane holds M[16w + lr][16j + 4lg + i]
+            }
+            half4 mh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * w + 4 * lg + i, ss = 16 * j + lr;
+                L.AT[rr][ss] = brow[i] * accA[i];
+                pmax = fmaxf(pmax, __builtin_fabsf(accM[i]));
+                mh[i] = (_Float16)accM[i];
+            }
+            *reinterpret_cast<half4*>(mrec + t6(w, j >> 1) * kTile + frag_half_offset(j, lr, lg)) = mh;
+        }
     }
     __syncthreads();
-    // off-diagonal blocks: T_ij = -T_ii * (sum_{m=j}^{i-1} A_im T_mj), by distance i - j
-    for (int dist = 1; dist < 4; ++dist) {
-        const int j = w, i = w + dist;
-        if (i < 4) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int m = j; m < i; ++m) acc = mm16(&L.AT[16 * i][16 * m], C + 1, t_block(L, m, j), C + 1, acc, lane);
+    // off-diagonal blocks: T_ij = -T_ii * (sum_{m=j}^{i-1} A_im T_mj).  Wave j forms column j
+    //      (T_{j+1,j}, T_{j+2,j}, T_{j+3,j} in turn), which needs only earlier blocks of the same
+    //      column, so no wave waits for another.  The column's blocks stay in registers in the
+    //      accumulator layout (lane: column lr, rows 4*lg + e); with the contraction index ordered
+    //      k = 4*lg + step, that layout is the right-hand operand of the next product as it is.
+    if (w < 3) {
+        floatx4 tcol[4];  // T_{j+d, j}, d = 0 .. 3 - j
+        const float* tjj = t_block(L, w, w);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) L.u.X[w][4 * lg + e][lr] = acc[e];
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            floatx4 t = {0.f, 0.f, 0.f, 0.f};
-            t = mm16(t_block(L, i, i), C + 1, &L.u.X[w][0][0], 17, t, lane);
-            float* dst = t_block(L, i, j);
+        for (int e = 0; e < 4; ++e) tcol[0][e] = tjj[(4 * lg + e) * (C + 1) + lr];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[(4 * lg + e) * (C + 1) + lr] = -t[e];
+        for (int dist = 1; dist < 4; ++dist) {
+            const int i = w + dist;
+            if (i < 4) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int mm = 0; mm < dist; ++mm) {  // m = w + mm
+                    const float* ap = &L.AT[16 * i + lr][16 * (w + mm) + 4 * lg];
+#pragma unroll
+                    for (int kq = 0; kq < 4; ++kq) acc = mfma16x16x4f32(ap[kq], tcol[mm][kq], acc);
+                }
+                const float* tp = t_block(L, i, i) + lr * (C + 1) + 4 * lg;
+                floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) t = mfma16x16x4f32(tp[kq], acc[kq], t);
+                tcol[dist] = -t;
+                float* dst = t_block(L, i, w);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(4 * lg + e) * (C + 1) + lr] = -t[e];
+            }
         }
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---- W's right-hand operand, Diag(beta) K+, staged transposed ([channel][token]) so that
     //      each matrix-core B fragment (8 consecutive tokens of one channel) is one 16-byte read.
