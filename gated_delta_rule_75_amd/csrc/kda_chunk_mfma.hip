@@ -591,24 +591,34 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
             }
         }
     }
-    __syncthreads();
+    // ---- meanwhile the waves with the shorter columns write gamma and the 16 K'^T operand tiles
+    //      (wave 3: gamma and tiles 0..11, wave 2: tiles 12..15)
+    if (w == 3) {
+        float* gam = reinterpret_cast<float*>(rec + kOffGamma);
+#pragma unroll
+        for (int c2 = 0; c2 < DK / 64; ++c2) {
+            const int ch = 64 * c2 + lane;
+            gam[ch] = exp2_hw(L.tot[0][ch] + L.tot[1][ch] + L.tot[2][ch] + L.tot[3][ch]);
+        }
+    }
+    if (w >= 2) {
+        const int t0k = w == 3 ? 0 : 12, t1k = w == 3 ? 12 : 16;
+        for (int t = t0k; t < t1k; ++t) {
+            const int cb = t >> 1, ks = t & 1;
+            const half8 kd = *reinterpret_cast<const half8*>(&L.kdT[16 * cb + lr][32 * ks + 8 * lg]);
+            *reinterpret_cast<half8*>(rec + kOffKdT + t * kTile + lane * 16) = kd;
+        }
+    }
 
     // ---- W's right-hand operand, Diag(beta) K+, staged transposed ([channel][token]) so that
     //      each matrix-core B fragment (8 consecutive tokens of one channel) is one 16-byte read.
-    //      It shares the union with the inverse scratch, dead since the barrier above, and the
-    //      barrier after the tile write-out below makes it visible.
+    //      It shares the union with the off-diagonal column operands, dead since the barrier
+    //      before the inverse, and the barrier below makes it visible.
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int i = 0; i < 8; ++i) L.u.bkT[32 * ks + 8 * lg + i][r] = BKp[ks][i];
-
-    // ---- write K'^T (16 tiles) as fp16 operand tiles
-    for (int t = w; t < 16; t += 4) {
-        const int cb = t >> 1, ks = t & 1;
-        const half8 kd = *reinterpret_cast<const half8*>(&L.kdT[16 * cb + lr][32 * ks + 8 * lg]);
-        *reinterpret_cast<half8*>(rec + kOffKdT + t * kTile + lane * 16) = kd;
-    }
-    __syncthreads();  // Diag(beta) K+ staged
+    __syncthreads();  // T complete; Diag(beta) K+ staged
 
     // ---- T rows of block w: the record's T tiles (w, kb) in operand order, and the right-hand
     //      operand of W^T below (zero above the diagonal)
@@ -646,12 +656,6 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
     if (!(qkmax < 32768.f) || !(pmax < 65504.f)) L.range_bad = 1;  // benign race: every writer stores 1
     __syncthreads();
     if (threadIdx.x == 0) *flag = (L.exact_diag ? kFlagExact : 0) | (L.range_bad ? kFlagRange : 0);
-
-    if (w == 0) {
-        float* gam = reinterpret_cast<float*>(rec + kOffGamma);
-        for (int ch = lane; ch < DK; ch += 64)
-            gam[ch] = exp2_hw(L.tot[0][ch] + L.tot[1][ch] + L.tot[2][ch] + L.tot[3][ch]);
-    }
     return !EXACT && L.exact_diag != 0;  // final since the factor tables' barrier
 }
 
