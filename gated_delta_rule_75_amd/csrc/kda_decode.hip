@@ -22,8 +22,8 @@
 //
 // Small batches: value columns never interact (each column of S is its own chain), so when
 // there are few (sequence, head) pairs each one is split over DV / 16 workgroups of 16 columns
-// (512 threads, one row each).  A single sequence with 32 heads then launches 256 workgroups
-// instead of 32, one per CU.
+// (256 threads, two rows each).  A single sequence with 32 heads then launches 256 workgroups
+// instead of 32, one per CU, and its state stays in L2 from step to step.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -36,7 +36,10 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 template <int DK, int DVB>
 struct DecodeShape {
     static constexpr int kColThreads = DVB / 4;                   // threads per row
-    static constexpr int kRowGroups = DK < 1024 / kColThreads ? DK : 1024 / kColThreads;
+    // the column-split variant is latency-bound (one small block per workgroup): 256 threads of
+    // two rows each finish sooner than 512 of one (measured at one sequence, 32 heads)
+    static constexpr int kMaxThreads = DVB == 16 ? 256 : 1024;
+    static constexpr int kRowGroups = DK < kMaxThreads / kColThreads ? DK : kMaxThreads / kColThreads;
     static constexpr int kThreads = kColThreads * kRowGroups;
     static constexpr int kWaves = kThreads / 64;
     static constexpr int kRowsPerThread = DK / kRowGroups;
@@ -68,11 +71,16 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     const float* Sin = s_in + nh * (int64_t)DK * DV + col0 + 4 * c4;
     float* Sout = s_out + nh * (int64_t)DK * DV + col0 + 4 * c4;
 
-    // the state loads first: they are the bulk of the traffic
+    // the state loads first: they are the bulk of the traffic.  A large batch streams its state
+    // once per step (non-temporal); the column-split small batches keep theirs in L2 from one step
+    // to the next (the same workgroup index, hence the same XCD, reads the block it wrote).
+    constexpr bool kStream = DVB == DV;
     floatx4 st[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        st[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sin + (int64_t)(rg + i * RG) * DV));
+    for (int i = 0; i < RPT; ++i) {
+        const floatx4* src = reinterpret_cast<const floatx4*>(Sin + (int64_t)(rg + i * RG) * DV);
+        st[i] = kStream ? __builtin_nontemporal_load(src) : *src;
+    }
     // v and beta of this thread's columns, needed only after the reductions, are requested now so
     // that their latency overlaps the state loads instead of following the reductions
     float vv[4];
@@ -172,7 +180,9 @@ __global__ __launch_bounds__(1024) void decode_kernel(
         floatx4 ns;
 #pragma unroll
         for (int j = 0; j < 4; ++j) ns[j] = a[i] * st[i][j] + kk[i] * d[j];
-        __builtin_nontemporal_store(ns, reinterpret_cast<floatx4*>(Sout + (int64_t)(rg + i * RG) * DV));
+        floatx4* dst = reinterpret_cast<floatx4*>(Sout + (int64_t)(rg + i * RG) * DV);
+        if (kStream) __builtin_nontemporal_store(ns, dst);
+        else *dst = ns;
     }
 }
 
