@@ -192,6 +192,9 @@ int run_prefill(const kda::PrefillArgs& a, int32_t dtype, hipStream_t s, const c
 int validate_common(const void* q, const void* k, const void* v, const float* g, const void* beta, int64_t tokens,
                     int32_t H, int32_t dk, int32_t dv, int32_t dtype, size_t qkg_align, bool gate_head) {
     if (H <= 0 || dk <= 0 || dv <= 0) return fail(KDA_ERR_INVALID_ARG, "H, d_k, d_v must be positive");
+    // the kernels address one chunk's rows (up to 64 tokens of H heads) with 32-bit byte offsets
+    if ((int64_t)H * (dk > dv ? dk : dv) >= ((int64_t)1 << 23))
+        return fail(KDA_ERR_INVALID_ARG, "H * max(d_k, d_v) must be below 2^23");
     if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "dtype must be KDA_F32 or KDA_BF16");
     if (tokens > 0 && (!q || !k || !v || !g || !beta))
         return fail(KDA_ERR_INVALID_ARG, "q, k, v, g and beta are required");

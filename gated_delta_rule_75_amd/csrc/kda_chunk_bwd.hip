@@ -172,6 +172,9 @@ struct Map {
     }
 };
 
+// Unconditional loads: where a row may lie past the chunk end, the row index is clamped to the last
+// valid row and the value replaced by zero after the load.  A branch around the load would make
+// the wave wait for the load before the branches merge, which serialises every prefetch.
 __device__ __forceinline__ float gate_at(const float* g, int gate_head, int64_t t, int H, int h, int DK, int c) {
     return gate_head ? g[t * H + h] : g[(t * H + h) * (int64_t)DK + c];
 }
@@ -237,6 +240,15 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
     const TI* beta = static_cast<const TI*>(a.beta);
     float* rec = a.ws + (slot * H + h) * R::kFloats;
     if (tid < C) sB[tid] = tid < L ? ld_in<TI>(beta, (t0 + tid) * H + h) : 0.f;
+    // descriptors over this chunk's rows of k, q, g and v: rows past the chunk end read 0, so the
+    // tile loads need no clamping or selects (and no branch, which would serialise them)
+    const int64_t tok0 = t0 * H + h;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + tok0 * DK, (uint32_t)((((int64_t)L - 1) * H * DK + DK) * sizeof(TI)));
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + tok0 * DK, (uint32_t)((((int64_t)L - 1) * H * DK + DK) * sizeof(TI)));
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + tok0 * DV, (uint32_t)((((int64_t)L - 1) * H * DV + DV) * sizeof(TI)));
+    const __amdgpu_buffer_rsrc_t grs =
+        a.gate_head ? make_rsrc(a.g + tok0, (uint32_t)((((int64_t)L - 1) * H + 1) * 4))
+                    : make_rsrc(a.g + tok0 * DK, (uint32_t)((((int64_t)L - 1) * H * DK + DK) * 4));
 
     // Channel tiles c0 .. c0 + CT - 1 of k, q and g (rows >= L are zero) and value tiles of v go
     // through registers one tile ahead of their use: the tile sequence is the channel tiles of
@@ -252,19 +264,17 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
 #pragma unroll
         for (int m = 0; m < EPT; ++m) {
             const int e = tid + kThreads * m, r = e / CT, cc = e % CT;
-            const bool in = (EPT * kThreads == C * CT || e < C * CT) && r < L;
-            const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + c0 + cc;
-            tr.k[m] = in ? ld_in<TI>(k, idx) : 0.f;
-            tr.q[m] = in ? ld_in<TI>(q, idx) : 0.f;
-            tr.g[m] = in ? gate_at(a.g, a.gate_head, t0 + r, H, h, DK, c0 + cc) : 0.f;
+            const int o = r * H * DK + c0 + cc;  // past the descriptors' ends (r >= L) the loads read 0
+            tr.k[m] = ld_buf<TI>(krs, o);
+            tr.q[m] = ld_buf<TI>(qrs, o);
+            tr.g[m] = ld_buf<float>(grs, a.gate_head ? r * H : o);
         }
     };
     auto fetch_value = [&](int j0) {
 #pragma unroll
         for (int m = 0; m < VPT; ++m) {
             const int e = tid + kThreads * m, r = e / VT, j = e % VT;
-            const bool in = (VPT * kThreads == C * VT || e < C * VT) && r < L;
-            vr[m] = in ? ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
+            vr[m] = ld_buf<TI>(vrs, r * H * DV + j0 + j);
         }
     };
     // registers -> tK, tQ, tG (raw g), then G = tril(ones) g into tG
@@ -750,7 +760,10 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
 #pragma unroll
         for (int m = 0; m < kDoPer; ++m) {
             const int e = tid + m * kThreads, r = e / kBV, j = e % kBV;
-            rdo[m] = (e < C * kBV && t0 + r < eos) ? a.dO[((t0 + r) * H + h) * (int64_t)DV + vb * kBV + j] : 0.f;
+            const bool in = e < C * kBV && t0 + r < eos;
+            const int64_t tr = in ? t0 + r : eos - 1;
+            const float x = a.dO[(tr * H + h) * (int64_t)DV + vb * kBV + j];
+            rdo[m] = in ? x : 0.f;
         }
     };
     if (c1 > c0) fetch(c1 - 1);
@@ -847,7 +860,10 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
 #pragma unroll
         for (int m = 0; m < kDoPer; ++m) {
             const int e = tid + m * kThreads, r = e / JT, j = e % JT;
-            rdo[m] = (e < C * JT && r < L) ? a.dO[((t0 + r) * H + h) * (int64_t)DV + j0 + j] : 0.f;
+            const bool in = e < C * JT && r < L;
+            const int rr = in ? r : L - 1;
+            const float x = a.dO[((t0 + rr) * H + h) * (int64_t)DV + j0 + j];
+            rdo[m] = in ? x : 0.f;
         }
     };
     fetch(0);
@@ -983,10 +999,14 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
         for (int m = 0; m < VPT; ++m) {
             const int e = tid + kThreads * m, r = e / JT, j = e % JT;
-            const bool in = (VPT * kThreads == C * JT || e < C * JT) && r < L;
-            vr.dd[m] = (VPT * kThreads == C * JT || e < C * JT) ? rec[R::dD + r * DV + j0 + j] : 0.f;
-            vr.v[m] = in ? ld_in<TI>(v, ((t0 + r) * H + h) * (int64_t)DV + j0 + j) : 0.f;
-            vr.b[m] = in ? ld_in<TI>(beta, (t0 + r) * H + h) : 0.f;
+            const bool full = VPT * kThreads == C * JT || e < C * JT, in = full && r < L;
+            const int rr = in ? r : L - 1;
+            const float dx = rec[R::dD + (full ? r : 0) * DV + j0 + j];
+            const float vx = ld_in<TI>(v, ((t0 + rr) * H + h) * (int64_t)DV + j0 + j);
+            const float bx = ld_in<TI>(beta, (t0 + rr) * H + h);
+            vr.dd[m] = full ? dx : 0.f;
+            vr.v[m] = in ? vx : 0.f;
+            vr.b[m] = in ? bx : 0.f;
         }
     };
     fetch_value(0);
@@ -1016,11 +1036,16 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         for (int i = 0; i < RPT; ++i) {
             const int r = r0 + 16 * i, ch = 16 * cb + cc;
             const bool in = r < L;
-            const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + ch;
-            br.k[i] = in ? ld_in<TI>(k, idx) : 0.f;
+            const int rr = in ? r : L - 1;  // see the note on unconditional loads
+            const int64_t idx = ((t0 + rr) * H + h) * (int64_t)DK + ch;
+            const float kx = ld_in<TI>(k, idx), gx = gate_at(a.g, a.gate_head, t0 + rr, H, h, DK, ch);
+            br.k[i] = in ? kx : 0.f;
             br.dw[i] = rec[R::dW + r * DK + ch];
-            br.g[i] = in ? gate_at(a.g, a.gate_head, t0 + r, H, h, DK, ch) : 0.f;
-            if (second) br.q[i] = in ? ld_in<TI>(q, idx) : 0.f;
+            br.g[i] = in ? gx : 0.f;
+            if (second) {
+                const float qx = ld_in<TI>(q, idx);
+                br.q[i] = in ? qx : 0.f;
+            }
         }
         if (second && w < NR) {
             const int ch = 16 * cb + lr;

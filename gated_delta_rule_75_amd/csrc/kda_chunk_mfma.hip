@@ -129,17 +129,6 @@ __device__ __forceinline__ float bf(uint16_t b) { return bf16_to_f32(b); }
 // ------------------------------------------------------------------------------------------
 // prep kernel: one workgroup (4 waves) per (slot, head); wave w owns token block w
 // ------------------------------------------------------------------------------------------
-// Buffer descriptor for `bytes` bytes at `base`.  Both are wave-uniform here; reading them
-// through readfirstlane tells the compiler so (a descriptor it cannot prove uniform is
-// wrapped in a per-lane loop).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-    void* up = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(up, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-
 // The prep kernel keeps log-decays in base-2 units (G * log2(e)), so that every decay factor is
 // one hardware exp2 with no scaling multiply.
 constexpr float kLog2e = 1.4426950408889634f;

@@ -23,6 +23,31 @@ __device__ __forceinline__ float ld_in<uint16_t>(const uint16_t* p, int64_t i) {
     return bf16_to_f32(p[i]);
 }
 
+// Buffer descriptor for `bytes` bytes at `base`; loads past the end return 0.  Both are
+// wave-uniform where it is used; reading them through readfirstlane tells the compiler so (a
+// descriptor it cannot prove uniform is wrapped in a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void* up = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(up, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Element i of a descriptor over storage type TI, as float (0 past the descriptor's end).
+template <typename TI>
+__device__ __forceinline__ float ld_buf(__amdgpu_buffer_rsrc_t r, int i);
+
+template <>
+__device__ __forceinline__ float ld_buf<float>(__amdgpu_buffer_rsrc_t r, int i) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0));
+}
+
+template <>
+__device__ __forceinline__ float ld_buf<uint16_t>(__amdgpu_buffer_rsrc_t r, int i) {
+    return bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, i * 2, 0, 0));
+}
+
 // exp(x) through the hardware base-2 exponential (v_exp_f32).
 __device__ __forceinline__ float fast_exp(float x) {
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);

@@ -23,6 +23,8 @@
  *     contiguous and row-major.  Alignment: for prefill and append, q, k and g
  *     16 bytes and the workspace 256 bytes; for decode, both states 16 bytes;
  *     every other pointer its element size.
+ *   - Sizes: H * max(d_k, d_v) must be below 2^23 (a chunk's rows are
+ *     addressed with 32-bit byte offsets); KDA_ERR_INVALID_ARG otherwise.
  *   - q, k, v and beta have the storage type `dtype` (KDA_F32: float,
  *     KDA_BF16: bfloat16).  g = log(alpha) is always float (fp32, values <= 0
  *     expected), states and outputs are always float.

@@ -61,6 +61,12 @@ def test_validation_errors_launch_nothing():
     assert L.kda_prefill_chunked(P, P, P, P, P, None, P, None, 1, 64, 2, 16, 16, 7, 16, None, 0, None) == -1
     # missing inputs
     assert L.kda_prefill_chunked(None, P, P, P, P, None, P, None, 1, 64, 2, 16, 16, 0, 16, None, 0, None) == -1
+    # a chunk's rows must fit 32-bit byte offsets: H * max(d_k, d_v) below 2^23
+    rc = L.kda_prefill_chunked(P, P, P, P, P, None, P, None, 1, 64, 1 << 16, 128, 128, 1, 64, None, 0, None)
+    assert rc == _l.KDA_ERR_INVALID_ARG and b"2^23" in L.kda_last_error()
+    S = 1 << 41
+    rc = L.kda_decode_step(P, P + 4096, P + 8192, P + 12288, P + 16384, S, S, 1 << 42, 1, 1 << 19, 16, 16, 0, None)
+    assert rc == _l.KDA_ERR_INVALID_ARG and b"2^23" in L.kda_last_error()
     # misaligned (q must be 16-byte aligned for prefill; decode states too)
     assert L.kda_prefill_chunked(P + 4, P, P, P, P, None, P, None, 1, 64, 2, 16, 16, 0, 16, None, 0, None) == -3
     assert L.kda_decode_step(P, P, P, P, P, 1 << 41, (1 << 41) + 4, 1 << 42, 1, 1, 16, 16, 0, None) == -3
