@@ -989,6 +989,14 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
     const TI* v = static_cast<const TI*>(a.v);
     const TI* beta = static_cast<const TI*>(a.beta);
     const float* rec = a.ws + (slot * H + h) * R::kFloats;
+    // outputs through descriptors that end at the chunk's last token: stores of rows past it are
+    // dropped, so no store needs a branch (a branch hides the count of outstanding memory
+    // operations from the compiler, and the next prefetch wait then drains every store too)
+    const int64_t tok0 = t0 * H + h;
+    const __amdgpu_buffer_rsrc_t gvrs = make_rsrc(a.gv + tok0 * DV, (uint32_t)((((int64_t)L - 1) * H * DV + DV) * 4));
+    const __amdgpu_buffer_rsrc_t gqrs = make_rsrc(a.gq + tok0 * DK, (uint32_t)((((int64_t)L - 1) * H * DK + DK) * 4));
+    const __amdgpu_buffer_rsrc_t gkrs = make_rsrc(a.gk + tok0 * DK, (uint32_t)((((int64_t)L - 1) * H * DK + DK) * 4));
+    const __amdgpu_buffer_rsrc_t ggrs = make_rsrc(a.gg + tok0 * DK, (uint32_t)((((int64_t)L - 1) * H * DK + DK) * 4));
 
     // value tiles (dD, v, beta), loaded into registers one tile ahead
     constexpr int VPT = (C * JT + kThreads - 1) / kThreads;
@@ -1103,7 +1111,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rb + 4 * (lane >> 4) + e, j = 16 * jb + (lane & 15);
                 part[e] = tV[r * LJ + j] * x[e];
-                if (r < L) a.gv[((t0 + r) * H + h) * (int64_t)DV + j0 + j] = sB[r] * x[e];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB[r] * x[e]), gvrs, (r * H * DV + j0 + j) * 4, 0, 0);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1312,19 +1320,19 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             float colsum = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                // rows past the chunk end have zero k and q, so their dG and column-sum terms are
+                // zero; their dq and dk stores fall past the descriptors' ends and are dropped
                 const int r = 16 * w + 4 * lg + e;
-                if (r < L) {
-                    const float kr = tK[r * LB + lr], qr = tQ[r * LB + lr];
-                    const float eg = fast_exp(Gr[e]), ed = fast_exp(glast - Gr[e]);
-                    const float dq = rdq[e] * eg + rq[e];
-                    const float dk = xk[e] * eg + rdk[e] * ed + rk[e] + ck[e];
-                    dGr[e] = xk[e] * kr * eg + rdq[e] * qr * eg - rdk[e] * kr * ed + qr * rq[e] + kr * rk[e] -
-                             kr * ck[e];
-                    colsum += rdk[e] * kr * ed;
-                    const int64_t go = ((t0 + r) * H + h) * (int64_t)DK + ch;
-                    a.gq[go] = dq;
-                    a.gk[go] = dk;
-                }
+                const float kr = tK[r * LB + lr], qr = tQ[r * LB + lr];
+                const float eg = fast_exp(Gr[e]), ed = fast_exp(glast - Gr[e]);
+                const float dq = rdq[e] * eg + rq[e];
+                const float dk = xk[e] * eg + rdk[e] * ed + rk[e] + ck[e];
+                dGr[e] = xk[e] * kr * eg + rdq[e] * qr * eg - rdk[e] * kr * ed + qr * rq[e] + kr * rk[e] -
+                         kr * ck[e];
+                colsum += rdk[e] * kr * ed;
+                const int go = (r * H * DK + ch) * 4;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq), gqrs, go, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk), gkrs, go, 0, 0);
             }
             colsum += __shfl_xor(colsum, 16);
             colsum += __shfl_xor(colsum, 32);
@@ -1357,7 +1365,8 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rr = 16 * w + 4 * lg + e;
-                if (!a.gate_head && rr < L) a.gg[((t0 + rr) * H + h) * (int64_t)DK + ch] = acc[e];
+                if (!a.gate_head)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), ggrs, (rr * H * DK + ch) * 4, 0, 0);
                 hsum[e] = sum16(acc[e]);
             }
             if (a.gate_head && lr == 0)
