@@ -896,9 +896,17 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
             if (t < NTM && sb <= rb)
                 dm[m] = mma_k4<JT / 16>(sdO + 16 * rb * LJ, LJ, sD + 16 * sb * LJ, LJ, dm[m], lane);
         }
-        // dgamma = rowsum(dS1 * S0)
-        if (tid < DK)
-            for (int j = 0; j < JT; ++j) dgam += sdS1[tid * LJ + j] * sS0[tid * LJ + j];
+        // dgamma = rowsum(dS1 * S0): two threads per key channel (half the tile's columns each, so
+        // that all four waves share the work), 16-byte reads
+        if (tid < 2 * DK) {
+            const int off = (tid >> 1) * LJ + (tid & 1) * (JT / 2);
+#pragma unroll
+            for (int j = 0; j < JT / 2; j += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(sdS1 + off + j);
+                const float4 y = *reinterpret_cast<const float4*>(sS0 + off + j);
+                dgam += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+            }
+        }
         lds_barrier();
     }
 #pragma unroll
@@ -923,7 +931,8 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
                 rec[R::dM + r * C + s] = s <= r ? dm[m][e] : 0.f;
             }
     }
-    if (tid < DK) rec[R::dgam + tid] = dgam;
+    dgam += __shfl_xor(dgam, 1);
+    if (tid < 2 * DK && !(tid & 1)) rec[R::dgam + (tid >> 1)] = dgam;
 }
 
 // ------------------------------------------------------------------------------------------
