@@ -772,6 +772,38 @@ def bench_workloads(args, res):
         torch.cuda.synchronize()
     dms = e0.elapsed_time(e1)
     kus = [m * 1e3 for n, m in kt.records if n == "kda_decode"]
+    # the first G of those steps captured in a HIP graph and replayed: time per step on the GPU with
+    # no host call between the kernels; one replay is first checked bitwise against the same steps run
+    # eagerly
+    G = 64
+    Sg, Se = sT.clone(), sT.clone()
+    gout, eout = torch.empty_like(dout), torch.empty_like(dout)
+
+    def gsteps(state, o_):
+        for t in range(G):
+            kda.decode_step(sq[t:t + 1], sk[t:t + 1], sv[t:t + 1], sg[t:t + 1], sb[t:t + 1], state, out=o_)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gsteps(Sg, gout)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gsteps(Sg, gout)
+    Sg.copy_(sT)
+    graph.replay()
+    gsteps(Se, eout)
+    torch.cuda.synchronize()
+    graph_same = bool(torch.equal(Sg, Se) and torch.equal(gout, eout))
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    gus = e0.elapsed_time(e1) * 1e3 / (reps * G)
+    del graph, Sg, Se
     h = 11
     log(f"[long] oracle on head {h}")
     wide = [synth.to_f64(x[:, h:h + 1], "bf16") for x in (q, k, v)] + [g[:, h:h + 1].astype(np.float64),
@@ -797,13 +829,19 @@ def bench_workloads(args, res):
         "decode_steps": steps, "decode_us_per_step": round(dms * 1e3 / steps, 2),
         "decode_steps_per_s": round(steps / (dms * 1e-3), 1),
         "decode_kernel_avg_us": round(sum(kus) / len(kus), 2),
+        "decode_graph_us_per_step": round(gus, 2),
+        "decode_graph_matches_eager": graph_same,
         "decode_note": "one sequence: each head's state split over 8 workgroups of 16 columns (256 per "
-                       "step); bound by launch and memory latency, not by HBM; the per-step time includes "
-                       "the host's calls through the Python binding",
+                       "step); bound by launch and memory latency, not by HBM.  decode_us_per_step includes "
+                       "the host's calls through the Python binding; decode_kernel_avg_us is timed with HIP "
+                       "events around each launch (the events add their own overhead); "
+                       "decode_graph_us_per_step is the time per step of 64 steps replayed back to back "
+                       "from a HIP graph",
         "parity": {"head": h, "prefill_tokens_checked": T, "decode_steps_checked": steps, "max_rel_err": err,
                    "tol": 2e-3, "ok": bool(err <= 2e-3), "oracle_s": round(t_or, 1)}}
     log(f"[long] prefill {ms:.2f} ms ({T / (ms * 1e-3) / 1e6:.2f} M tokens/s), decode {dms * 1e3 / steps:.1f} "
-        f"us/step (kernel {sum(kus) / len(kus):.1f} us); parity {err:.2e}")
+        f"us/step (kernel {sum(kus) / len(kus):.1f} us with events, {gus:.2f} us per step from a graph, "
+        f"graph == eager: {graph_same}); parity {err:.2e}")
     res["workloads"] = out
 
 
