@@ -56,11 +56,11 @@ DECODE_BYTES_PER_SEQ_HEAD = 65536 + 65536 + 768 + 512 + 2 + 512         # 132866
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 _KIB = 1024
 _MFMA_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_mfma.hip"
-_MFMA_SHA = "6e1135a7cc1dfa9baa4ab61c2635cf9eadff27018a858962f3e322cb3e3ed2ad"
+_MFMA_SHA = "f8584934e85030d09e0ceed6c3bf4bb7e05d2d6bee10740197b7fb6908bda442"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
-_DECODE_SHA = "b22d0839d069d021330e24ebbe84d22337c50dc6103a3037d6ec9e2d244feec8"
+_DECODE_SHA = "8f6da261804d588a7c98da378838a326741fe49876b995ac0c4a84bf7b3318b3"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
-_BWD_SHA = "6bfb6e9b17f3036f05488d8be5c7cedc4ca7bb3de3a7a6d9a0f4a89af8f0acb7"
+_BWD_SHA = "e604779f94527f67f084096d821014aeb6b64e08679074339bca3d7040e7dbf6"
 
 
 def _counted(fetch_kib, write_kib):
@@ -70,15 +70,15 @@ def _counted(fetch_kib, write_kib):
 # kernel name -> where and on what it was measured, and HBM bytes per launch
 MEASURED_TRAFFIC = {
     "kda_prep": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                 "bytes": _counted(1065146.0, 1983489.4)},
+                 "bytes": _counted(1065150.5, 1983494.5)},
     "kda_state": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                  "bytes": _counted(1270852.0, 1050775.4)},
+                  "bytes": _counted(1271581.2, 1050756.3)},
     "kda_decode": {"source": _DECODE_SRC, "sha256": _DECODE_SHA, "workload": "decode N=256 H=32",
-                   "bytes": _counted(267357.4, 528584.8)},
+                   "bytes": _counted(267359.5, 528576.9)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
     "kda_backward": {"source": _BWD_SRC, "sha256": _BWD_SHA, "workload": "backward T=65536 H=32",
-                     "bytes": _counted(3556843.1 + 1599053.6 + 2431122.1 + 3791090.6 + 9349948.4,
-                                       7882187.4 + 3317428.8 + 3288020.8 + 3686842.7 + 4488661.2)},
+                     "bytes": _counted(3479289.1 + 1597344.3 + 2391567.3 + 3795304.9 + 9163319.0,
+                                       7897689.2 + 3308311.5 + 3216348.1 + 3686813.9 + 4498756.8)},
 }
 
 
@@ -101,7 +101,7 @@ def traffic_of(kernel, workload=None):
 # prefill MFMA utilisation from rocprofv3 --pmc MfmaUtil (percent of cycles the matrix cores are
 # busy, per kernel), on the kernel source named by its SHA-256 (profiles/prefill_mfma_utilisation_*)
 MEASURED_MFMA_UTIL = {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                      "kda_prep": 0.062, "kda_state": 0.098}
+                      "kda_prep": 0.082, "kda_state": 0.101}
 # the algorithmic MFMA fraction at the HBM roofline: 139,264 flop per 1,794 B at 8 TB/s = 621
 # TFLOP/s, 24.8% of the dense fp16/bf16 peak
 MFMA_CEILING_AT_HBM_ROOFLINE = PREFILL_FLOP_PER_TOKEN_HEAD / PREFILL_BYTES_PER_TOKEN_HEAD * HBM_PEAK_GBPS / 1e3 / \
