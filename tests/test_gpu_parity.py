@@ -114,6 +114,48 @@ def test_decode_steps_match_oracle(dtype, d, N):
     assert_close(host(S), sref, 1e-5, None, "state")
 
 
+@pytest.mark.parametrize("N", [1, 130])
+def test_decode_steps_replayed_from_a_hip_graph_equal_eager_steps(N):
+    """Decode steps captured in a HIP graph (the column-split layout at N=1, one workgroup per pair at
+    130 x 4 pairs) and replayed three times, with eager calls and synchronisations in between: every
+    replay's outputs and final state equal the same steps run eagerly, bit for bit."""
+    print(f"decode graph N={N}", flush=True)
+    w = _w("bf16", H=4, d=128, seed=9, s0_std=0.02)
+    w.q_unit = False
+    G = 8
+    s0 = dev(synth.gen_state(w, N), "f32")
+    steps = []
+    for t in range(G):
+        st, _ = make_inputs(w, N, offset_tokens=t * N)
+        steps.append(upload(w, st))
+    Sg = s0.clone()
+    outs = [torch.empty(N, w.H, w.dv, device="cuda") for _ in range(G)]
+
+    def run(S, os_):
+        for t in range(G):
+            kda.decode_step(*steps[t], S, out=os_[t])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(Sg, outs)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(Sg, outs)
+    for rep in range(3):
+        Se = s0.clone()
+        eouts = [torch.empty_like(o) for o in outs]
+        run(Se, eouts)  # eager work between the replays
+        torch.cuda.synchronize()
+        Sg.copy_(s0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Sg, Se), f"state, replay {rep}"
+        for t in range(G):
+            assert torch.equal(outs[t], eouts[t]), f"output of step {t}, replay {rep}"
+
+
 def test_decode_out_of_place_equals_in_place():
     w = _w("bf16", H=2, seed=6, s0_std=0.02)
     N = 3
