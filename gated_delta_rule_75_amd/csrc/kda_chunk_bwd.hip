@@ -936,6 +936,148 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
 }
 
 // ------------------------------------------------------------------------------------------
+// grad_state with split-bf16 operands (bfloat16 storage at d_k = d_v = 128, chunk 64).  Each fp32
+// operand x is staged in LDS as hi = bf16(x) and lo = bf16(x - hi), so x = hi + lo to within 2^-18
+// of |x|, and every product is three bf16 matrix-core steps (hi hi + hi lo + lo hi; the lo lo term is
+// below 2^-18 of the product), with fp32 accumulation and fp32's exponent range.  A value tile of 32
+// columns is one 16x16x32 step, where the fp32 16x16x4 form needs eight steps of twice the cost.
+// dgamma is summed from the staged fp32 values themselves.
+// ------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split4(float4 x, bf16x4& hi, bf16x4& lo) {
+    const float v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = (__bf16)v[i];
+        lo[i] = (__bf16)(v[i] - (float)hi[i]);
+    }
+}
+
+__device__ __forceinline__ floatx4 mfma_split(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, floatx4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+}
+
+template <int DK, int DV, int C>
+__global__ __launch_bounds__(kThreads) void grad_state_split_kernel(BwdArgs a, Map<C> mp) {
+    using R = Rec<DK, DV, C>;
+    static_assert(DK == 128 && DV == 128 && C == 64, "split-bf16 grad_state covers the d = 128, chunk 64 shape");
+    constexpr int JT = 32, LH = JT + 8;  // value columns per tile; bf16 row stride (80 bytes)
+    constexpr int NR = C / 16;
+    // hi and lo of D, dD, dO ([C][LH]) and of S0, dS1 ([DK][LH])
+    __shared__ __attribute__((aligned(16))) __bf16 sD[2][C * LH];
+    __shared__ __attribute__((aligned(16))) __bf16 sdD[2][C * LH];
+    __shared__ __attribute__((aligned(16))) __bf16 sdO[2][C * LH];
+    __shared__ __attribute__((aligned(16))) __bf16 sS0[2][DK * LH];
+    __shared__ __attribute__((aligned(16))) __bf16 sdS1[2][DK * LH];
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int64_t slot = blockIdx.x;
+    int64_t n, c, t0;
+    int L;
+    if (!mp.locate(slot, n, c, t0, L)) return;
+    const int H = a.H;
+    float* rec = a.ws + (slot * H + h) * R::kFloats;
+    // dO rows of this chunk through a descriptor that ends at its last token (rows past it read 0)
+    const __amdgpu_buffer_rsrc_t dors =
+        make_rsrc(a.dO + (t0 * H + h) * (int64_t)DV, (uint32_t)((((int64_t)L - 1) * H * DV + DV) * 4));
+    floatx4 kd[8], qp[8], dw[8], dm[4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) kd[m] = qp[m] = dw[m] = zero4();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dm[m] = zero4();
+    float dgam[4] = {0.f, 0.f, 0.f, 0.f};  // rows (tid >> 3) + 32 m, summed over this thread's columns
+    // value tile j0 .. j0 + 31, one tile ahead: thread tid holds rows tid / 8 + 32 m, columns 4 (tid % 8) .. +3
+    Stage<C, JT> pD, pdD, pdO;
+    Stage<DK, JT> pS, pdS;
+    auto fetch = [&](int j0) {
+        pD.load(rec + R::D + j0, DV);
+        pdD.load(rec + R::dD + j0, DV);
+        pS.load(rec + R::S0 + j0, DV);
+        pdS.load(rec + R::dS1 + j0, DV);
+#pragma unroll
+        for (int m = 0; m < Stage<C, JT>::kPer; ++m) {
+            const int e = tid + m * kThreads, row = e / (JT / 4), c4 = e % (JT / 4);
+            pdO.r[m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      dors, (row * H * DV + j0 + 4 * c4) * 4, 0, 0));
+        }
+    };
+    auto store_split = [&](const float4* r, int kper, __bf16* hi, __bf16* lo) {
+        for (int m = 0; m < kper; ++m) {
+            const int e = tid + m * kThreads, row = e / (JT / 4), c4 = e % (JT / 4);
+            bf16x4 bh, bl;
+            split4(r[m], bh, bl);
+            *reinterpret_cast<bf16x4*>(hi + row * LH + 4 * c4) = bh;
+            *reinterpret_cast<bf16x4*>(lo + row * LH + 4 * c4) = bl;
+        }
+    };
+    auto frag = [&](const __bf16* base, int rb) {
+        return *reinterpret_cast<const bf16x8*>(base + (16 * rb + lr) * LH + 8 * lg);
+    };
+    fetch(0);
+    for (int j0 = 0; j0 < DV; j0 += JT) {
+#pragma unroll
+        for (int m = 0; m < Stage<DK, JT>::kPer; ++m) {  // dgamma from the fp32 values
+            const float4 x = pS.r[m], y = pdS.r[m];
+            dgam[m] += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+        }
+        store_split(pD.r, Stage<C, JT>::kPer, sD[0], sD[1]);
+        store_split(pdD.r, Stage<C, JT>::kPer, sdD[0], sdD[1]);
+        store_split(pdO.r, Stage<C, JT>::kPer, sdO[0], sdO[1]);
+        store_split(pS.r, Stage<DK, JT>::kPer, sS0[0], sS0[1]);
+        store_split(pdS.r, Stage<DK, JT>::kPer, sdS1[0], sdS1[1]);
+        fetch(j0 + JT < DV ? j0 + JT : j0);
+        lds_barrier();
+        // token block w: D, dO, dD rows (A operands of the three [C][DK] products, and D the B
+        // operand of dM)
+        const bf16x8 aDh = frag(sD[0], w), aDl = frag(sD[1], w);
+        const bf16x8 aOh = frag(sdO[0], w), aOl = frag(sdO[1], w);
+        const bf16x8 adh = frag(sdD[0], w), adl = frag(sdD[1], w);
+        // dK' = D dS1^T, dQ+ = dO S0^T, dW = -dD S0^T: tile (w, m) for key channel block m
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const bf16x8 sh = frag(sS0[0], m), sl = frag(sS0[1], m);
+            const bf16x8 gh = frag(sdS1[0], m), gl = frag(sdS1[1], m);
+            kd[m] = mfma_split(aDh, aDl, gh, gl, kd[m]);
+            qp[m] = mfma_split(aOh, aOl, sh, sl, qp[m]);
+            dw[m] = mfma_split(adh, adl, sh, sl, dw[m]);
+        }
+        // dM = tril(dO D^T): tile (m, w) for token blocks m >= w
+#pragma unroll
+        for (int m = 0; m < NR; ++m)
+            if (w <= m) dm[m] = mfma_split(frag(sdO[0], m), frag(sdO[1], m), aDh, aDl, dm[m]);
+        lds_barrier();
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t o = (16 * w + 4 * lg + e) * DK + 16 * m + lr;
+            rec[R::dKd + o] = kd[m][e];
+            rec[R::dQp + o] = qp[m][e];
+            rec[R::dW + o] = -dw[m][e];
+        }
+#pragma unroll
+    for (int m = 0; m < NR; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * m + 4 * lg + e, s2 = 16 * w + lr;
+            rec[R::dM + r * C + s2] = (w <= m && s2 <= r) ? dm[m][e] : 0.f;
+        }
+    // each row's sum over its 8 threads (columns 4 (tid % 8) .. +3 of every tile)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        float x = dgam[m];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        if ((tid & 7) == 0) rec[R::dgam + (tid >> 3) + 32 * m] = x;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // grad_chunk: one workgroup per (chunk slot, head); dq, dk, dv, dg, dbeta.  Under 80 KB of LDS
 // (two workgroups per CU): the key channels are visited in blocks of 16, and each block's
 // cumulative log-decay is recomputed there as a product with a lower-triangular matrix of ones.
@@ -1482,7 +1624,10 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (timed) timed_end(s);
         if (timed) timed_begin(kKernelBwdGradState, s);
-        hipLaunchKernelGGL((grad_state_kernel<DK, DV, C>), per_chunk, dim3(kThreads), 0, s, x, mp);
+        if constexpr (std::is_same<TI, uint16_t>::value && DK == 128 && DV == 128 && C == 64)
+            hipLaunchKernelGGL((grad_state_split_kernel<DK, DV, C>), per_chunk, dim3(kThreads), 0, s, x, mp);
+        else
+            hipLaunchKernelGGL((grad_state_kernel<DK, DV, C>), per_chunk, dim3(kThreads), 0, s, x, mp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (timed) timed_end(s);
         if (timed) timed_begin(kKernelBwdGradChunk, s);
