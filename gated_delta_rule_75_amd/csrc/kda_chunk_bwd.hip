@@ -33,6 +33,7 @@
 // exponents are <= 0.  Inside a block one factor can exceed 1; where a block's 16-token decay
 // exceeds e^64 those pairs take their own exponentials on the vector ALUs instead.
 #include <cstdlib>
+#include <type_traits>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -105,6 +106,55 @@ __device__ __forceinline__ float sum16(float x) {
     x += __shfl_xor(x, 4);
     x += __shfl_xor(x, 8);
     return x;
+}
+
+// Split-bf16 operands (bfloat16 storage at d_k = d_v = 128, chunk 64): an fp32 value x is kept as
+// hi = bf16(x) and lo = bf16(x - hi), so x = hi + lo to within 2^-18 of |x|, and a product takes
+// three bf16 matrix-core steps (hi hi + hi lo + lo hi; lo lo is below 2^-18 of the product), with
+// fp32 accumulation and fp32's exponent range.  A 32-deep contraction is then one 16x16x32 step
+// where the fp32 16x16x4 form needs eight steps of twice the cost.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split4(float4 x, bf16x4& hi, bf16x4& lo) {
+    const float v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = (__bf16)v[i];
+        lo[i] = (__bf16)(v[i] - (float)hi[i]);
+    }
+}
+
+__device__ __forceinline__ floatx4 mfma_split(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, floatx4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+}
+
+template <int DK, int DV, int C, typename TI>
+struct SplitShape {
+    static constexpr bool value = std::is_same<TI, uint16_t>::value && DK == 128 && DV == 128 && C == 64;
+};
+
+// Elements i and i + 1 (i even) of an n-element chain operand array at rec + off, split: bf16 hi in
+// the array's first half and bf16 lo in its second half (the bytes of n floats), one 4-byte store
+// for each.
+__device__ __forceinline__ void put_pair(float* rec, int64_t off, int n, int i, float x0, float x1) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 hi, lo;
+    hi[0] = (__bf16)x0;
+    hi[1] = (__bf16)x1;
+    lo[0] = (__bf16)(x0 - (float)hi[0]);
+    lo[1] = (__bf16)(x1 - (float)hi[1]);
+    bf16x2* p = reinterpret_cast<bf16x2*>(rec + off);
+    p[i >> 1] = hi;
+    p[(n + i) >> 1] = lo;
+}
+
+// A 16x32 bf16 operand fragment from LDS holding bf16 pairs packed in floats (row stride ldf
+// floats): rows row0 + (lane & 15), k = 32 ks + 8 (lane >> 4) .. +7.
+__device__ __forceinline__ bf16x8 frag16(const float* base, int row0, int ldf, int ks, int lane) {
+    return *reinterpret_cast<const bf16x8*>(base + (row0 + (lane & 15)) * ldf + 16 * ks + 4 * (lane >> 4));
 }
 
 // Workspace record of one (chunk slot, head), in floats.
@@ -214,6 +264,7 @@ struct FactorsLds {
 template <int DK, int DV, int C, typename TI>
 __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
+    constexpr bool SPLIT = SplitShape<DK, DV, C, TI>::value;  // chain operands stored as bf16 hi and lo
     using Lds = FactorsLds<DK, DV, C>;
     constexpr int LC = Lds::LC, LT = Lds::LT, NR = C / 16;
     constexpr int CT = DK < Lds::CT ? DK : Lds::CT;  // channels per tile
@@ -436,10 +487,18 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
                 sM[r * LC + s2] = accM[m][e];
             }
     lds_barrier();
-    for (int e = tid; e < C * C; e += kThreads) {
-        const int r = e / C, s2 = e % C;
-        rec[R::MT + e] = sM[s2 * LC + r];  // M^T[r][s2] = M[s2][r]
-        rec[R::P + e] = sP[r * LC + s2];
+    if constexpr (SPLIT) {
+        for (int e = 2 * tid; e < C * C; e += 2 * kThreads) {  // element pairs along a row
+            const int r = e / C, s2 = e % C;
+            put_pair(rec, R::MT, C * C, e, sM[s2 * LC + r], sM[(s2 + 1) * LC + r]);  // M^T[r][s2] = M[s2][r]
+            *reinterpret_cast<float2*>(rec + R::P + e) = make_float2(sP[r * LC + s2], sP[r * LC + s2 + 1]);
+        }
+    } else {
+        for (int e = tid; e < C * C; e += kThreads) {
+            const int r = e / C, s2 = e % C;
+            rec[R::MT + e] = sM[s2 * LC + r];  // M^T[r][s2] = M[s2][r]
+            rec[R::P + e] = sP[r * LC + s2];
+        }
     }
     lds_barrier();
     // A = Diag(beta) P into M's buffer; T zeroed
@@ -497,28 +556,67 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             fetch_tile((ti + 1) * CT);
         else
             fetch_value(0);
-        for (int e = tid; e < C * CT; e += kThreads) {  // channel-major outputs (token index fastest)
-            const int cc = e / C, r = e % C;
-            const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc];
-            rec[R::QpT + (c0 + cc) * C + r] = tQ[r * LT + cc] * fast_exp(g);
-            rec[R::KdT + (c0 + cc) * C + r] = tK[r * LT + cc] * fast_exp(gl - g);
+        if constexpr (SPLIT) {
+            for (int e = 2 * tid; e < C * CT; e += 2 * kThreads) {  // channel-major, token pairs
+                const int cc = e / C, r = e % C;
+                const float g0 = tG[r * LT + cc], g1 = tG[(r + 1) * LT + cc], gl = tG[(C - 1) * LT + cc];
+                put_pair(rec, R::QpT, DK * C, (c0 + cc) * C + r, tQ[r * LT + cc] * fast_exp(g0),
+                         tQ[(r + 1) * LT + cc] * fast_exp(g1));
+                put_pair(rec, R::KdT, DK * C, (c0 + cc) * C + r, tK[r * LT + cc] * fast_exp(gl - g0),
+                         tK[(r + 1) * LT + cc] * fast_exp(gl - g1));
+            }
+        } else {
+            for (int e = tid; e < C * CT; e += kThreads) {  // channel-major outputs (token index fastest)
+                const int cc = e / C, r = e % C;
+                const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc];
+                rec[R::QpT + (c0 + cc) * C + r] = tQ[r * LT + cc] * fast_exp(g);
+                rec[R::KdT + (c0 + cc) * C + r] = tK[r * LT + cc] * fast_exp(gl - g);
+            }
         }
         lds_barrier();
-        for (int e = tid; e < C * CT; e += kThreads) {  // token-major outputs; K becomes beta K+ in place
-            const int r = e / CT, cc = e % CT;
-            const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc], kk = tK[r * LT + cc];
-            rec[R::Kd + r * DK + c0 + cc] = kk * fast_exp(gl - g);
-            tK[r * LT + cc] = sB[r] * kk * fast_exp(g);
+        if constexpr (SPLIT) {
+            for (int e = 2 * tid; e < C * CT; e += 2 * kThreads) {  // token-major, channel pairs
+                const int r = e / CT, cc = e % CT;
+                const float g0 = tG[r * LT + cc], g1 = tG[r * LT + cc + 1];
+                const float gl0 = tG[(C - 1) * LT + cc], gl1 = tG[(C - 1) * LT + cc + 1];
+                const float k0 = tK[r * LT + cc], k1 = tK[r * LT + cc + 1];
+                put_pair(rec, R::Kd, C * DK, r * DK + c0 + cc, k0 * fast_exp(gl0 - g0), k1 * fast_exp(gl1 - g1));
+                tK[r * LT + cc] = sB[r] * k0 * fast_exp(g0);
+                tK[r * LT + cc + 1] = sB[r] * k1 * fast_exp(g1);
+            }
+        } else {
+            for (int e = tid; e < C * CT; e += kThreads) {  // token-major outputs; K becomes beta K+ in place
+                const int r = e / CT, cc = e % CT;
+                const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc], kk = tK[r * LT + cc];
+                rec[R::Kd + r * DK + c0 + cc] = kk * fast_exp(gl - g);
+                tK[r * LT + cc] = sB[r] * kk * fast_exp(g);
+            }
         }
         if (tid < CT) rec[R::gam + c0 + tid] = fast_exp(tG[(C - 1) * LT + tid]);
         lds_barrier();
         for (int t = w; t < NR * (CT / 16); t += 4) {
             const int rb = t % NR, cb = t / NR;
             const floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, tK + 16 * cb, LT, 1, zero4(), lane);
+            if constexpr (SPLIT) {
+                // W: the lanes of a column pair swap half their rows, so each writes two rows of a
+                // column pair
+                const bool odd = lr & 1;
+                const float r0 = __shfl_xor(odd ? acc[0] : acc[2], 1), r1 = __shfl_xor(odd ? acc[1] : acc[3], 1);
+                const int row = 16 * rb + 4 * lg + (odd ? 2 : 0), col = c0 + 16 * cb + (lr & ~1);
+                put_pair(rec, R::W, C * DK, row * DK + col, odd ? r0 : acc[0], odd ? acc[2] : r0);
+                put_pair(rec, R::W, C * DK, (row + 1) * DK + col, odd ? r1 : acc[1], odd ? acc[3] : r1);
+                bf16x4 hi, lo;
+                split4(make_float4(acc[0], acc[1], acc[2], acc[3]), hi, lo);
+                const int64_t i = (int64_t)(c0 + 16 * cb + lr) * C + 16 * rb + 4 * lg;
+                bf16x4* p = reinterpret_cast<bf16x4*>(rec + R::WT);
+                p[i >> 2] = hi;
+                p[(DK * C + i) >> 2] = lo;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rec[R::W + (16 * rb + 4 * lg + e) * DK + c0 + 16 * cb + lr] = acc[e];
-            *reinterpret_cast<float4*>(rec + R::WT + (int64_t)(c0 + 16 * cb + lr) * C + 16 * rb + 4 * lg) =
-                make_float4(acc[0], acc[1], acc[2], acc[3]);
+                for (int e = 0; e < 4; ++e) rec[R::W + (16 * rb + 4 * lg + e) * DK + c0 + 16 * cb + lr] = acc[e];
+                *reinterpret_cast<float4*>(rec + R::WT + (int64_t)(c0 + 16 * cb + lr) * C + 16 * rb + 4 * lg) =
+                    make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
         }
         lds_barrier();
     }
@@ -711,6 +809,129 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
 }
 
 // ------------------------------------------------------------------------------------------
+// fwd_chain with split-bf16 operands (bfloat16 storage at d = 128, chunk 64).  W and K'^T arrive as
+// bf16 hi and lo from the factors kernel and are staged as they are; the state block is kept in
+// fp32 (for gamma * S and the stored S0) and, beside it, as bf16 hi and lo for the product W S; D
+// likewise for K'^T D.
+// ------------------------------------------------------------------------------------------
+template <int DK, int DV, int C>
+__global__ __launch_bounds__(kThreads) void fwd_chain_split_kernel(BwdArgs a, Map<C> mp) {
+    using R = Rec<DK, DV, C>;
+    static_assert(DK == 128 && DV == 128 && C == 64, "split-bf16 chains cover the d = 128, chunk 64 shape");
+    // row strides in floats; the bf16 arrays hold packed pairs (k + 8 bf16 per row)
+    constexpr int NVB = DV / kBV, NR = C / 16, LW = DK + 4, LWh = DK / 2 + 4, LTh = C / 2 + 4;
+    __shared__ __attribute__((aligned(16))) float sW[2][C * LWh];    // W hi, lo [token][channel]: A of W S
+    __shared__ __attribute__((aligned(16))) float sKT[2][DK * LTh];  // K'^T hi, lo [channel][token]: A of K'^T D
+    __shared__ __attribute__((aligned(16))) float sU[C * kBV];
+    __shared__ __attribute__((aligned(16))) float sg[DK];
+    __shared__ __attribute__((aligned(16))) float sSt[kBV * LW];     // state block, fp32 [column][channel]
+    __shared__ __attribute__((aligned(16))) float sSh[2][kBV * LWh]; // its hi, lo: B of W S
+    __shared__ __attribute__((aligned(16))) float sDh[2][kBV * LTh]; // D hi, lo [column][token]: B of K'^T D
+    __shared__ __attribute__((aligned(16))) float sDummy[64];        // sink of the L2 warm-up loads
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    int64_t nh;
+    int vb;
+    chain_unit<NVB>(blockIdx.x, mp.N * a.H, nh, vb);
+    auto* dummy = reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&sDummy[0]));
+    const int h = (int)(nh % a.H);
+    const int64_t n = nh / a.H;
+    const int H = a.H;
+    for (int e = tid; e < DK * kBV; e += kThreads) {
+        const int i = e / kBV, j = e % kBV;
+        const float x = a.s0 ? a.s0[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] : 0.f;
+        sSt[j * LW + i] = x;
+        const __bf16 hi = (__bf16)x;
+        reinterpret_cast<__bf16*>(sSh[0])[j * 2 * LWh + i] = hi;
+        reinterpret_cast<__bf16*>(sSh[1])[j * 2 * LWh + i] = (__bf16)(x - (float)hi);
+    }
+    const int64_t slot0 = mp.base(n);
+    int64_t c0, c1;
+    mp.range(n, c0, c1);
+    float* s_fin = a.s_fin ? a.s_fin + ((n * H + h) * DK) * (int64_t)DV + vb * kBV : nullptr;
+    if (c0 >= c1) {  // uniform: no chunk here, the state passes through (each thread its own elements)
+        if (s_fin)
+            for (int e = tid; e < DK * kBV; e += kThreads) s_fin[(e / kBV) * DV + e % kBV] = sSt[(e % kBV) * LW + e / kBV];
+        return;
+    }
+    Stage<C, DK / 2> pWh, pWl;
+    Stage<DK, C / 2> pKh, pKl;
+    Stage<C, kBV> pU;
+    Stage<1, DK> pg;
+    auto fetch = [&](int64_t c) {
+        const float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
+        pWh.load(rec + R::W, DK / 2);
+        pWl.load(rec + R::W + C * DK / 2, DK / 2);
+        pKh.load(rec + R::KdT, C / 2);
+        pKl.load(rec + R::KdT + DK * C / 2, C / 2);
+        pU.load(rec + R::U + vb * kBV, DV);
+        pg.load(rec + R::gam, DK);
+    };
+    fetch(c0);
+    for (int64_t c = c0; c < c1; ++c) {
+        float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
+        lds_barrier();  // the previous chunk is done with the LDS operands; the state is its final state
+        pWh.store(sW[0], LWh);
+        pWl.store(sW[1], LWh);
+        pKh.store(sKT[0], LTh);
+        pKl.store(sKT[1], LTh);
+        pU.store(sU, kBV);
+        pg.store(sg, DK);
+        for (int e = tid; e < DK * kBV; e += kThreads)
+            rec[R::S0 + (e / kBV) * DV + vb * kBV + e % kBV] = sSt[(e % kBV) * LW + e / kBV];
+        lds_barrier();
+        // D = U - W S (rows 16 w .. 16 w + 15)
+        if (w < NR) {
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks)
+                acc = mfma_split(frag16(sW[0], 16 * w, LWh, ks, lane), frag16(sW[1], 16 * w, LWh, ks, lane),
+                                 frag16(sSh[0], 0, LWh, ks, lane), frag16(sSh[1], 0, LWh, ks, lane), acc);
+            float4 dv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + 4 * lg + e;
+                const float d = sU[r * kBV + lr] - acc[e];
+                (&dv.x)[e] = d;
+                rec[R::D + r * DV + vb * kBV + lr] = d;
+            }
+            bf16x4 dh, dl;
+            split4(dv, dh, dl);
+            *reinterpret_cast<bf16x4*>(sDh[0] + lr * LTh + 8 * w + 2 * lg) = dh;
+            *reinterpret_cast<bf16x4*>(sDh[1] + lr * LTh + 8 * w + 2 * lg) = dl;
+        }
+        lds_barrier();
+        // the next chunk's operands and the L2 warm-up are requested here, after D
+        fetch(c + 1 < c1 ? c + 1 : c);
+        {  // W, U and K'^T (one contiguous range) of the chunk kWarm ahead
+            const float* wrec = a.ws + ((slot0 + (c + kWarm < c1 ? c + kWarm : c1 - 1)) * H + h) * R::kFloats;
+            warm_range<R::Kd>(wrec, 0, vb, NVB, dummy);
+        }
+        // S <- Diag(gamma) S + K'^T D
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int cb = w + 4 * t;
+            const int i0 = 16 * cb + 4 * lg;
+            const float4 s4 = *reinterpret_cast<const float4*>(sSt + lr * LW + i0);
+            floatx4 acc = {sg[i0] * s4.x, sg[i0 + 1] * s4.y, sg[i0 + 2] * s4.z, sg[i0 + 3] * s4.w};
+#pragma unroll
+            for (int ks = 0; ks < C / 32; ++ks)
+                acc = mfma_split(frag16(sKT[0], 16 * cb, LTh, ks, lane), frag16(sKT[1], 16 * cb, LTh, ks, lane),
+                                 frag16(sDh[0], 0, LTh, ks, lane), frag16(sDh[1], 0, LTh, ks, lane), acc);
+            const float4 ns = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<float4*>(sSt + lr * LW + i0) = ns;
+            bf16x4 hh, ll;
+            split4(ns, hh, ll);
+            *reinterpret_cast<bf16x4*>(sSh[0] + lr * LWh + 8 * cb + 2 * lg) = hh;
+            *reinterpret_cast<bf16x4*>(sSh[1] + lr * LWh + 8 * cb + 2 * lg) = ll;
+        }
+    }
+    if (s_fin) {  // the state after the last chunk (a checkpoint for a later window)
+        lds_barrier();
+        for (int e = tid; e < DK * kBV; e += kThreads) s_fin[(e / kBV) * DV + e % kBV] = sSt[(e % kBV) * LW + e / kBV];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // rev_chain: one workgroup per (sequence, head, 16 value columns); chunks in reverse.  dS, dO and
 // dD are kept transposed in LDS ([value column][contraction index]).
 // ------------------------------------------------------------------------------------------
@@ -809,6 +1030,158 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
             const floatx4 wd = mma_k4<C / 16>(sWT + 16 * cb * LT, LT, sdDt, LT, zero4(), lane);
             *reinterpret_cast<float4*>(sdSt + lr * LW + i0) =
                 make_float4(acc[0] - wd[0], acc[1] - wd[1], acc[2] - wd[2], acc[3] - wd[3]);
+        }
+    }
+    lds_barrier();
+    if (a.gs0)
+        for (int e = tid; e < DK * kBV; e += kThreads) {
+            const int i = e / kBV, j = e % kBV;
+            a.gs0[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] = sdSt[j * LW + i];
+        }
+}
+
+// ------------------------------------------------------------------------------------------
+// rev_chain with split-bf16 operands (bfloat16 storage at d = 128, chunk 64): K', M^T, Q+^T and W^T
+// arrive as bf16 hi and lo; dS is kept in fp32 (for gamma * dS and the stored dS1) and, beside it,
+// as bf16 hi and lo for K' dS; dO and dD as bf16 hi and lo.
+// ------------------------------------------------------------------------------------------
+template <int DK, int DV, int C>
+__global__ __launch_bounds__(kThreads) void rev_chain_split_kernel(BwdArgs a, Map<C> mp) {
+    using R = Rec<DK, DV, C>;
+    static_assert(DK == 128 && DV == 128 && C == 64, "split-bf16 chains cover the d = 128, chunk 64 shape");
+    constexpr int NVB = DV / kBV, NR = C / 16, LW = DK + 4, LWh = DK / 2 + 4, LTh = C / 2 + 4;
+    __shared__ __attribute__((aligned(16))) float sK[2][C * LWh];     // K' hi, lo [token][channel]: A of K' dS
+    __shared__ __attribute__((aligned(16))) float sM[2][C * LTh];     // M^T hi, lo: A of M^T dO
+    __shared__ __attribute__((aligned(16))) float sQ[2][DK * LTh];    // Q+^T hi, lo: A of Q+^T dO
+    __shared__ __attribute__((aligned(16))) float sW[2][DK * LTh];    // W^T hi, lo: A of W^T dD
+    __shared__ __attribute__((aligned(16))) float sg[DK];
+    __shared__ __attribute__((aligned(16))) float sdSt[kBV * LW];     // dS, fp32 [column][channel]
+    __shared__ __attribute__((aligned(16))) float sdSh[2][kBV * LWh]; // its hi, lo: B of K' dS
+    __shared__ __attribute__((aligned(16))) float sdOh[2][kBV * LTh]; // dO hi, lo [column][token]
+    __shared__ __attribute__((aligned(16))) float sdDh[2][kBV * LTh]; // dD hi, lo [column][token]
+    __shared__ __attribute__((aligned(16))) float sDummy[64];         // sink of the L2 warm-up loads
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    int64_t nh;
+    int vb;
+    chain_unit<NVB>(blockIdx.x, mp.N * a.H, nh, vb);
+    auto* dummy = reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&sDummy[0]));
+    const int h = (int)(nh % a.H);
+    const int64_t n = nh / a.H;
+    const int H = a.H;
+    for (int e = tid; e < DK * kBV; e += kThreads) {
+        const int i = e / kBV, j = e % kBV;
+        const float x = a.dsT ? a.dsT[((n * H + h) * DK + i) * (int64_t)DV + vb * kBV + j] : 0.f;
+        sdSt[j * LW + i] = x;
+        const __bf16 hi = (__bf16)x;
+        reinterpret_cast<__bf16*>(sdSh[0])[j * 2 * LWh + i] = hi;
+        reinterpret_cast<__bf16*>(sdSh[1])[j * 2 * LWh + i] = (__bf16)(x - (float)hi);
+    }
+    const int64_t bos = mp.cu[n], eos = mp.cu[n + 1];
+    const int64_t slot0 = mp.base(n);
+    int64_t c0, c1;
+    mp.range(n, c0, c1);
+    Stage<C, DK / 2> pKh, pKl;
+    Stage<C, C / 2> pMh, pMl;
+    Stage<DK, C / 2> pQh, pQl, pWh, pWl;
+    Stage<1, DK> pg;
+    constexpr int kDoPer = (C * kBV + kThreads - 1) / kThreads;
+    float rdo[kDoPer];
+    auto fetch = [&](int64_t c) {
+        const float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
+        pKh.load(rec + R::Kd, DK / 2);
+        pKl.load(rec + R::Kd + C * DK / 2, DK / 2);
+        pMh.load(rec + R::MT, C / 2);
+        pMl.load(rec + R::MT + C * C / 2, C / 2);
+        pQh.load(rec + R::QpT, C / 2);
+        pQl.load(rec + R::QpT + DK * C / 2, C / 2);
+        pWh.load(rec + R::WT, C / 2);
+        pWl.load(rec + R::WT + DK * C / 2, C / 2);
+        pg.load(rec + R::gam, DK);
+        // dO rows of the chunk through a descriptor that ends at the sequence's last token (0 past it),
+        // so no select waits on the loads
+        const int64_t t0 = bos + c * C;
+        const int64_t L = eos - t0 < C ? eos - t0 : C;
+        const __amdgpu_buffer_rsrc_t drs =
+            make_rsrc(a.dO + (t0 * H + h) * (int64_t)DV + vb * kBV, (uint32_t)(((L - 1) * H * DV + kBV) * 4));
+        static_assert(kDoPer * kThreads == C * kBV, "dO tile split evenly over the threads");
+#pragma unroll
+        for (int m = 0; m < kDoPer; ++m) {
+            const int e = tid + m * kThreads, r = e / kBV, j = e % kBV;
+            rdo[m] = ld_buf<float>(drs, r * H * DV + j);
+        }
+    };
+    if (c1 > c0) fetch(c1 - 1);
+    for (int64_t c = c1 - 1; c >= c0; --c) {
+        float* rec = a.ws + ((slot0 + c) * H + h) * R::kFloats;
+        lds_barrier();  // the previous chunk is done with the LDS operands; dS is its result
+        pKh.store(sK[0], LWh);
+        pKl.store(sK[1], LWh);
+        pMh.store(sM[0], LTh);
+        pMl.store(sM[1], LTh);
+        pQh.store(sQ[0], LTh);
+        pQl.store(sQ[1], LTh);
+        pWh.store(sW[0], LTh);
+        pWl.store(sW[1], LTh);
+        pg.store(sg, DK);
+#pragma unroll
+        for (int m = 0; m < kDoPer; ++m) {
+            const int e = tid + m * kThreads;
+            if (e < C * kBV) {
+                const int r = e / kBV, j = e % kBV;
+                const __bf16 hi = (__bf16)rdo[m];  // rows past the sequence's end read 0
+                reinterpret_cast<__bf16*>(sdOh[0])[j * 2 * LTh + r] = hi;
+                reinterpret_cast<__bf16*>(sdOh[1])[j * 2 * LTh + r] = (__bf16)(rdo[m] - (float)hi);
+            }
+        }
+        for (int e = tid; e < DK * kBV; e += kThreads)
+            rec[R::dS1 + (e / kBV) * DV + vb * kBV + e % kBV] = sdSt[(e % kBV) * LW + e / kBV];
+        lds_barrier();
+        // dD = K' dS + M^T dO (rows 16 w .. 16 w + 15)
+        if (w < NR) {
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks)
+                acc = mfma_split(frag16(sK[0], 16 * w, LWh, ks, lane), frag16(sK[1], 16 * w, LWh, ks, lane),
+                                 frag16(sdSh[0], 0, LWh, ks, lane), frag16(sdSh[1], 0, LWh, ks, lane), acc);
+#pragma unroll
+            for (int ks = 0; ks < C / 32; ++ks)
+                acc = mfma_split(frag16(sM[0], 16 * w, LTh, ks, lane), frag16(sM[1], 16 * w, LTh, ks, lane),
+                                 frag16(sdOh[0], 0, LTh, ks, lane), frag16(sdOh[1], 0, LTh, ks, lane), acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rec[R::dD + (16 * w + 4 * lg + e) * DV + vb * kBV + lr] = acc[e];
+            bf16x4 dh, dl;
+            split4(make_float4(acc[0], acc[1], acc[2], acc[3]), dh, dl);
+            *reinterpret_cast<bf16x4*>(sdDh[0] + lr * LTh + 8 * w + 2 * lg) = dh;
+            *reinterpret_cast<bf16x4*>(sdDh[1] + lr * LTh + 8 * w + 2 * lg) = dl;
+        }
+        lds_barrier();
+        // the previous chunk's operands and the L2 warm-up are requested here, after dD
+        fetch(c > c0 ? c - 1 : c);
+        {  // K', Q+^T, W^T and M^T (one contiguous range) of the chunk kWarm behind
+            const float* wrec = a.ws + ((slot0 + (c - kWarm >= c0 ? c - kWarm : c0)) * H + h) * R::kFloats;
+            warm_range<R::T - R::Kd>(wrec, R::Kd, vb, NVB, dummy);
+        }
+        // dS <- Diag(gamma) dS + Q+^T dO - W^T dD
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int cb = w + 4 * t;
+            const int i0 = 16 * cb + 4 * lg;
+            const float4 s4 = *reinterpret_cast<const float4*>(sdSt + lr * LW + i0);
+            floatx4 acc = {sg[i0] * s4.x, sg[i0 + 1] * s4.y, sg[i0 + 2] * s4.z, sg[i0 + 3] * s4.w};
+            floatx4 wd = zero4();
+#pragma unroll
+            for (int ks = 0; ks < C / 32; ++ks) {
+                acc = mfma_split(frag16(sQ[0], 16 * cb, LTh, ks, lane), frag16(sQ[1], 16 * cb, LTh, ks, lane),
+                                 frag16(sdOh[0], 0, LTh, ks, lane), frag16(sdOh[1], 0, LTh, ks, lane), acc);
+                wd = mfma_split(frag16(sW[0], 16 * cb, LTh, ks, lane), frag16(sW[1], 16 * cb, LTh, ks, lane),
+                                frag16(sdDh[0], 0, LTh, ks, lane), frag16(sdDh[1], 0, LTh, ks, lane), wd);
+            }
+            const float4 ns = make_float4(acc[0] - wd[0], acc[1] - wd[1], acc[2] - wd[2], acc[3] - wd[3]);
+            *reinterpret_cast<float4*>(sdSt + lr * LW + i0) = ns;
+            bf16x4 hh, ll;
+            split4(ns, hh, ll);
+            *reinterpret_cast<bf16x4*>(sdSh[0] + lr * LWh + 8 * cb + 2 * lg) = hh;
+            *reinterpret_cast<bf16x4*>(sdSh[1] + lr * LWh + 8 * cb + 2 * lg) = ll;
         }
     }
     lds_barrier();
@@ -943,24 +1316,6 @@ __global__ __launch_bounds__(kThreads) void grad_state_kernel(BwdArgs a, Map<C> 
 // columns is one 16x16x32 step, where the fp32 16x16x4 form needs eight steps of twice the cost.
 // dgamma is summed from the staged fp32 values themselves.
 // ------------------------------------------------------------------------------------------
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void split4(float4 x, bf16x4& hi, bf16x4& lo) {
-    const float v[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = (__bf16)v[i];
-        lo[i] = (__bf16)(v[i] - (float)hi[i]);
-    }
-}
-
-__device__ __forceinline__ floatx4 mfma_split(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, floatx4 acc) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-}
-
 template <int DK, int DV, int C>
 __global__ __launch_bounds__(kThreads) void grad_state_split_kernel(BwdArgs a, Map<C> mp) {
     using R = Rec<DK, DV, C>;
@@ -1601,6 +1956,7 @@ BwdPlan plan_bwd(int64_t N, int64_t T_total, int H, int DK, int DV, int C, size_
 
 template <int DK, int DV, int C, typename TI>
 hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
+    constexpr bool kSplit = SplitShape<DK, DV, C, TI>::value;
     const bool timed = timing_on();
     hipError_t e;
     constexpr size_t f_lds = FactorsLds<DK, DV, C>::kBytes, c_lds = ChunkLds<DK, DV, C>::kBytes;
@@ -1615,16 +1971,22 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (timed) timed_end(s);
         if (timed) timed_begin(kKernelBwdFwdChain, s);
-        hipLaunchKernelGGL((fwd_chain_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, x, mp);
+        if constexpr (kSplit)
+            hipLaunchKernelGGL((fwd_chain_split_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, x, mp);
+        else
+            hipLaunchKernelGGL((fwd_chain_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, x, mp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (timed) timed_end(s);
         if (forward_only) return hipSuccess;
         if (timed) timed_begin(kKernelBwdRevChain, s);
-        hipLaunchKernelGGL((rev_chain_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, x, mp);
+        if constexpr (kSplit)
+            hipLaunchKernelGGL((rev_chain_split_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, x, mp);
+        else
+            hipLaunchKernelGGL((rev_chain_kernel<DK, DV, C>), chains, dim3(kThreads), 0, s, x, mp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (timed) timed_end(s);
         if (timed) timed_begin(kKernelBwdGradState, s);
-        if constexpr (std::is_same<TI, uint16_t>::value && DK == 128 && DV == 128 && C == 64)
+        if constexpr (kSplit)
             hipLaunchKernelGGL((grad_state_split_kernel<DK, DV, C>), per_chunk, dim3(kThreads), 0, s, x, mp);
         else
             hipLaunchKernelGGL((grad_state_kernel<DK, DV, C>), per_chunk, dim3(kThreads), 0, s, x, mp);
