@@ -60,7 +60,7 @@ _MFMA_SHA = "f8584934e85030d09e0ceed6c3bf4bb7e05d2d6bee10740197b7fb6908bda442"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
 _DECODE_SHA = "8f6da261804d588a7c98da378838a326741fe49876b995ac0c4a84bf7b3318b3"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
-_BWD_SHA = "e604779f94527f67f084096d821014aeb6b64e08679074339bca3d7040e7dbf6"
+_BWD_SHA = "f88f9df608112584fe8c834eca6bbc7b75778d79ecf381eef6627aa6ede974d4"
 
 
 def _counted(fetch_kib, write_kib):
@@ -77,8 +77,8 @@ MEASURED_TRAFFIC = {
                    "bytes": _counted(267359.5, 528576.9)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
     "kda_backward": {"source": _BWD_SRC, "sha256": _BWD_SHA, "workload": "backward T=65536 H=32",
-                     "bytes": _counted(3479289.1 + 1597344.3 + 2391567.3 + 3795304.9 + 9163319.0,
-                                       7897689.2 + 3308311.5 + 3216348.1 + 3686813.9 + 4498756.8)},
+                     "bytes": _counted(3479168.3 + 1607097.6 + 2389228.6 + 3709399.4 + 9179037.4,
+                                       8286672.5 + 3463850.1 + 3145737.2 + 3688268.0 + 4475061.6)},
 }
 
 
@@ -532,6 +532,9 @@ def bench_backward(args, res, wide_all):
     res["next_rows"]["chunked_backward"] = {
         "workload": f"gradients of the headline prefill (T={T}, H={H}, d={d}, chunk {C}, bf16 inputs, fp32 "
                     "arithmetic); dL/do ~ N(0,1)",
+        "arithmetic": "fp32 accumulation; at d=128, chunk 64 with bf16 inputs the chain and state-side products "
+                      "take split-bf16 operands (hi + lo, three bf16 matrix-core steps per product, about 2^-18 "
+                      "relative), the rest fp32 matrix-core steps",
         "ms_per_pass": round(avg_ms, 3), "min_pass_ms": round(min(ms), 3),
         "tokens_per_s": round(T / (avg_ms * 1e-3), 1), "kernels_ms_per_pass": kernels,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F32_PEAK_TFLOPS,

@@ -259,7 +259,11 @@ int kda_append_prefill_noalloc(const void* q, const void* k, const void* v, cons
  *   d_state_in   [N, H, d_k, d_v]          dL/dS_0, or NULL (not wanted)
  * q, k, v, g, beta, cu_seqlens, state_in, dtype and chunk are as for
  * kda_append_prefill (a batch of B equal sequences is cu_seqlens = 0, T, 2T,
- * ...).  The arithmetic is fp32 whatever dtype is.  Supported shapes:
+ * ...).  Accumulation is fp32 whatever dtype is; with KDA_BF16 at d = 128,
+ * chunk 64 the chain and state-side products multiply split-bf16 operands
+ * (each fp32 value as bf16 hi plus bf16 lo, three bf16 matrix-core steps per
+ * product, within about 2^-16 of the fp32 product), the rest fp32 operands.
+ * Supported shapes:
  * d_k = d_v in {16, 32, 64, 128}, chunk in {16, 32, 64}.  options may be NULL;
  * only options->gate is honoured, and snapshot_every and prologue must be 0
  * (KDA_ERR_UNSUPPORTED otherwise).  workspace: at least
