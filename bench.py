@@ -56,7 +56,7 @@ DECODE_BYTES_PER_SEQ_HEAD = 65536 + 65536 + 768 + 512 + 2 + 512         # 132866
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 _KIB = 1024
 _MFMA_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_mfma.hip"
-_MFMA_SHA = "f8584934e85030d09e0ceed6c3bf4bb7e05d2d6bee10740197b7fb6908bda442"
+_MFMA_SHA = "6c4a05405bdcb1d57d471965b4de7627f2eb4e3f956caac226f03ae2219e73cb"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
 _DECODE_SHA = "8f6da261804d588a7c98da378838a326741fe49876b995ac0c4a84bf7b3318b3"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
@@ -70,9 +70,9 @@ def _counted(fetch_kib, write_kib):
 # kernel name -> where and on what it was measured, and HBM bytes per launch
 MEASURED_TRAFFIC = {
     "kda_prep": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                 "bytes": _counted(1065150.5, 1983494.5)},
+                 "bytes": _counted(1065120.0, 1983493.2)},
     "kda_state": {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                  "bytes": _counted(1271581.2, 1050756.3)},
+                  "bytes": _counted(1271087.6, 1050785.0)},
     "kda_decode": {"source": _DECODE_SRC, "sha256": _DECODE_SHA, "workload": "decode N=256 H=32",
                    "bytes": _counted(267359.5, 528576.9)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
@@ -101,7 +101,7 @@ def traffic_of(kernel, workload=None):
 # prefill MFMA utilisation from rocprofv3 --pmc MfmaUtil (percent of cycles the matrix cores are
 # busy, per kernel), on the kernel source named by its SHA-256 (profiles/prefill_mfma_utilisation_*)
 MEASURED_MFMA_UTIL = {"source": _MFMA_SRC, "sha256": _MFMA_SHA, "workload": "prefill T=65536 H=32",
-                      "kda_prep": 0.082, "kda_state": 0.101}
+                      "kda_prep": 0.081, "kda_state": 0.101}
 # the algorithmic MFMA fraction at the HBM roofline: 139,264 flop per 1,794 B at 8 TB/s = 621
 # TFLOP/s, 24.8% of the dense fp16/bf16 peak
 MFMA_CEILING_AT_HBM_ROOFLINE = PREFILL_FLOP_PER_TOKEN_HEAD / PREFILL_BYTES_PER_TOKEN_HEAD * HBM_PEAK_GBPS / 1e3 / \

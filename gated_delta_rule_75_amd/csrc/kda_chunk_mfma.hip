@@ -414,7 +414,7 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
             mh[j] = (_Float16)((s2 <= lr) ? accM[j] : 0.f);
             exact_pmax = fmaxf(exact_pmax, __builtin_fabsf((float)mh[j]));
         }
-        *reinterpret_cast<half4*>(rec + kOffM + t6(w, w >> 1) * kTile + frag_half_offset(w, lr, lg)) = mh;
+        __builtin_nontemporal_store(mh, reinterpret_cast<half4*>(rec + kOffM + t6(w, w >> 1) * kTile + frag_half_offset(w, lr, lg)));
     }
     half8 KR[4], QR[4], BKp[4];
     floatx4 diagA = {0.f, 0.f, 0.f, 0.f}, diagM = {0.f, 0.f, 0.f, 0.f};  // tile (w, w)
@@ -462,7 +462,7 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
             diagM = mfma16x16x32(kcd, qrd, diagM);  // swapped: lane holds M[r][16w + 4lg + i]
         }
         BKp[ks] = kp;  // Diag(beta) K+, consumed by W after T is known
-        *reinterpret_cast<half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16) = qp;
+        __builtin_nontemporal_store(qp, reinterpret_cast<half8*>(rec + kOffQp + (w * 4 + ks) * kTile + lane * 16));
         if (w < 3) *reinterpret_cast<half8*>(&L.u.kc[w][ks][lane][0]) = kc;
         // keep the per-channel table reads of one k-step from being hoisted above the previous
         // one (bounds register pressure)
@@ -498,12 +498,11 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
             pmax = fmaxf(pmax, __builtin_fabsf(mv));
             mh[i] = (_Float16)mv;
         }
-        *reinterpret_cast<half4*>(mrec + t6(w, w >> 1) * kTile + frag_half_offset(w, lr, lg)) = mh;
+        __builtin_nontemporal_store(mh, reinterpret_cast<half4*>(mrec + t6(w, w >> 1) * kTile + frag_half_offset(w, lr, lg)));
     }
     // the stored M tiles of row blocks 0 and 2 also span the (zero) block to the right of the diagonal
     if (!(w & 1))
-        *reinterpret_cast<half4*>(mrec + t6(w, w >> 1) * kTile + frag_half_offset(w + 1, lr, lg)) =
-            half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+        __builtin_nontemporal_store(half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f}, reinterpret_cast<half4*>(mrec + t6(w, w >> 1) * kTile + frag_half_offset(w + 1, lr, lg)));
     __syncthreads();
     if (w == 0) {
         // ---- T = (I + A)^{-1}, diagonal 16x16 blocks by forward substitution: wave 0 inverts all
@@ -544,7 +543,7 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
                 pmax = fmaxf(pmax, __builtin_fabsf(accM[i]));
                 mh[i] = (_Float16)accM[i];
             }
-            *reinterpret_cast<half4*>(mrec + t6(w, j >> 1) * kTile + frag_half_offset(j, lr, lg)) = mh;
+            __builtin_nontemporal_store(mh, reinterpret_cast<half4*>(mrec + t6(w, j >> 1) * kTile + frag_half_offset(j, lr, lg)));
         }
     }
     __syncthreads();
@@ -595,7 +594,7 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
         for (int t = t0k; t < t1k; ++t) {
             const int cb = t >> 1, ks = t & 1;
             const half8 kd = *reinterpret_cast<const half8*>(&L.kdT[16 * cb + lr][32 * ks + 8 * lg]);
-            *reinterpret_cast<half8*>(rec + kOffKdT + t * kTile + lane * 16) = kd;
+            __builtin_nontemporal_store(kd, reinterpret_cast<half8*>(rec + kOffKdT + t * kTile + lane * 16));
         }
     }
 
@@ -621,8 +620,8 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
             pmax = fmaxf(pmax, __builtin_fabsf(val));
             ta[kb][i] = (_Float16)val;
         }
-    *reinterpret_cast<half8*>(rec + kOffT + t6(w, 0) * kTile + lane * 16) = ta[0];
-    if (w >= 2) *reinterpret_cast<half8*>(rec + kOffT + t6(w, 1) * kTile + lane * 16) = ta[1];
+    __builtin_nontemporal_store(ta[0], reinterpret_cast<half8*>(rec + kOffT + t6(w, 0) * kTile + lane * 16));
+    if (w >= 2) __builtin_nontemporal_store(ta[1], reinterpret_cast<half8*>(rec + kOffT + t6(w, 1) * kTile + lane * 16));
 
     // ---- W = T Diag(beta) K+ (64 x 128), rows of token block w, as W^T = (Diag(beta) K+)^T T^T
     //      tiles: each lane then holds 4 consecutive channels of its token row and stores them
@@ -640,7 +639,7 @@ __device__ __forceinline__ bool prep_unit(const PrefillArgs& a, const SeqMap& sm
             pmax = fmaxf(pmax, __builtin_fabsf(acc[i]));
             wh[i] = (_Float16)acc[i];
         }
-        *reinterpret_cast<half4*>(rec + kOffW + (w * 4 + (cb >> 1)) * kTile + frag_half_offset(cb, lr, lg)) = wh;
+        __builtin_nontemporal_store(wh, reinterpret_cast<half4*>(rec + kOffW + (w * 4 + (cb >> 1)) * kTile + frag_half_offset(cb, lr, lg)));
     }
     if (!(qkmax < 32768.f) || !(pmax < 65504.f)) L.range_bad = 1;  // benign race: every writer stores 1
     __syncthreads();
