@@ -3,8 +3,10 @@ reverse-mode derivative of the recurrence.
 
 Every gradient (dq, dk, dv, dg, dbeta per (sequence, head) token slice; dS0 per state) is
 compared with max|gpu - oracle| / max|oracle| <= 2e-3 for bfloat16 storage and 1e-5 for fp32
-storage.  The backward computes in fp32 either way, so both sides see the same stored inputs
-and the error is fp32 rounding.
+storage.  Both sides see the same stored inputs.  The backward accumulates in fp32 either way; with
+bfloat16 storage at d = 128, chunk 64 its chain and state-side products multiply split-bf16
+operands (bf16 hi + bf16 lo of each fp32 value, about 2^-16 relative per product), elsewhere fp32
+ones, so the error is fp32 rounding plus that split.
 """
 import numpy as np
 import pytest
@@ -21,10 +23,12 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(),
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 
 
-def _run(dtype, d, chunk, lengths, with_state, with_dsT, head_gate=False, seed=5, H=3, g_override=None):
+def _run(dtype, d, chunk, lengths, with_state, with_dsT, head_gate=False, seed=5, H=3, g_override=None,
+         v_std=1.0, s0_std=0.05):
     print(f"backward dtype={dtype} d={d} chunk={chunk} lengths={lengths} state={with_state} dsT={with_dsT} "
-          f"head_gate={head_gate}", flush=True)
-    w = synth.Workload("bwd", seed, H=H, dk=d, dv=d, dtype=dtype, chunk=chunk, s0_std=0.05 if with_state else 0.0)
+          f"head_gate={head_gate} v_std={v_std} s0_std={s0_std}", flush=True)
+    w = synth.Workload("bwd", seed, H=H, dk=d, dv=d, dtype=dtype, chunk=chunk, s0_std=s0_std if with_state else 0.0,
+                       v_std=v_std)
     cu = synth.cu_seqlens(lengths)
     T, N = int(cu[-1]), len(lengths)
     st, wide = make_inputs(w, T)
@@ -72,6 +76,13 @@ def _run(dtype, d, chunk, lengths, with_state, with_dsT, head_gate=False, seed=5
 ])
 def test_backward_matches_oracle(dtype, d, chunk, lengths, with_state, with_dsT):
     _run(dtype, d, chunk, lengths, with_state, with_dsT)
+
+
+def test_backward_large_magnitudes():
+    """The split-bf16 products keep fp32's exponent range: v ~ N(0, (2e4)^2) and S0 ~ N(0, (1e4)^2),
+    far beyond fp16's range, at the shape that uses them (bf16, d = 128, chunk 64)."""
+    got, ref = _run("bf16", 128, 64, [300, 130], True, True, v_std=2e4, s0_std=1e4)
+    assert np.abs(ref[0]).max() > 1e2 and np.abs(ref[1]).max() > 1e2  # dq and dk scale with v and S0
 
 
 @pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("f32", 32, 16)])
