@@ -55,7 +55,7 @@ __device__ __forceinline__ floatx4 mma(const float* A, int ar, int ak, const flo
     const int r = lane & 15, kq = lane >> 4;
     const float* pa = A + r * ar + kq * ak;
     const float* pb = B + kq * bk + r * bc;
-#pragma unroll 4
+#pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * ks * ak], pb[4 * ks * bk], acc, 0, 0, 0);
     return acc;
