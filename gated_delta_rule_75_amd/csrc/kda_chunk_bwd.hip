@@ -1504,10 +1504,10 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
     const __amdgpu_buffer_rsrc_t gkrs = make_rsrc(a.gk + tok0 * DK, (uint32_t)((((int64_t)L - 1) * H * DK + DK) * 4));
     const __amdgpu_buffer_rsrc_t ggrs = make_rsrc(a.gg + tok0 * DK, (uint32_t)((((int64_t)L - 1) * H * DK + DK) * 4));
 
-    // value tiles (dD, v, beta), loaded into registers one tile ahead
+    // value tiles (dD, v), loaded into registers one tile ahead (beta comes from sB)
     constexpr int VPT = (C * JT + kThreads - 1) / kThreads;
     struct ValueRegs {
-        float dd[VPT], v[VPT], b[VPT];
+        float dd[VPT], v[VPT];
     } vr;
     auto fetch_value = [&](int j0) {
 #pragma unroll
@@ -1517,10 +1517,8 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             const int rr = in ? r : L - 1;
             const float dx = rec[R::dD + (full ? r : 0) * DV + j0 + j];
             const float vx = ld_in<TI>(v, ((t0 + rr) * H + h) * (int64_t)DV + j0 + j);
-            const float bx = ld_in<TI>(beta, (t0 + rr) * H + h);
             vr.dd[m] = full ? dx : 0.f;
             vr.v[m] = in ? vx : 0.f;
-            vr.b[m] = in ? bx : 0.f;
         }
     };
     fetch_value(0);
@@ -1590,6 +1588,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
     floatx4 dT[TPW];
 #pragma unroll
     for (int m = 0; m < TPW; ++m) dT[m] = zero4();
+    lds_barrier();  // sB (read by the value-tile staging) is complete
     for (int j0 = 0; j0 < DV; j0 += JT) {
         // this tile from registers; the next one is loaded while this one is used
 #pragma unroll
@@ -1598,7 +1597,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             if (VPT * kThreads == C * JT || e < C * JT) {
                 tdD[r * LJ + j] = vr.dd[m];
                 tV[r * LJ + j] = vr.v[m];
-                tBV[r * LJ + j] = vr.b[m] * vr.v[m];
+                tBV[r * LJ + j] = sB[r] * vr.v[m];  // sB is 0 past the chunk end
             }
         }
         fetch_value(j0 + JT < DV ? j0 + JT : j0);
