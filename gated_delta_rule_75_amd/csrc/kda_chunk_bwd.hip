@@ -1,5 +1,5 @@
 // KDA chunked backward: gradients of the chunked prefill with respect to q, k, v, g = log(alpha),
-// beta and the initial state, given dL/do and dL/dS_T.  fp32 arithmetic throughout.
+// beta and the initial state, given dL/do and dL/dS_T.  fp32 accumulation throughout.
 //
 // "Kimi K3, explained" says that training runs the recurrence in chunks ("How is KDA trained
 // efficiently if it is a recurrence?", "Training in chunks") and gives no gradient equations.  The
@@ -27,8 +27,10 @@
 //   grad_chunk  (chunk, head)          dq, dk, dv, dg, dbeta
 // The two chains are sequential over chunks and split by 16 value columns (columns of S and dS
 // never interact); the three per-chunk kernels are fully parallel.  Every product is a 16x16
-// tile on the fp32 matrix cores (v_mfma_f32_16x16x4f32), the pairwise products P, M and their
-// gradients included: the decay exp(G_r - G_s) of a pair is split at a 16-row block boundary m,
+// tile on the matrix cores: fp32 steps (v_mfma_f32_16x16x4f32), or, for bfloat16 storage at
+// d = 128, chunk 64, split-bf16 steps in the two chains and grad_state (see SplitShape).  The
+// pairwise products P, M and their gradients are included: the decay exp(G_r - G_s) of a pair is
+// split at a 16-row block boundary m,
 // exp(G_r - G_m) exp(G_m - G_s), and the two factors scale the two operands.  Across blocks both
 // exponents are <= 0.  Inside a block one factor can exceed 1; where a block's 16-token decay
 // exceeds e^64 those pairs take their own exponentials on the vector ALUs instead.
