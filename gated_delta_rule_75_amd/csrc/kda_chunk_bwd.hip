@@ -1442,7 +1442,8 @@ __global__ __launch_bounds__(kThreads) void grad_state_split_kernel(BwdArgs a, M
 template <int DK, int DV, int C>
 struct ChunkLds {
     static constexpr int LC = C + 1, LB = 17;
-    static constexpr int JT = DV < 32 ? DV : 32, LJ = JT + 1;  // value columns per staged tile
+    // value columns per staged tile; rows padded to a multiple of 4 floats for 16-byte operand reads
+    static constexpr int JT = DV < 32 ? DV : 32, LJ = JT + 4;
     static constexpr int kStage0 = 3 * LJ > 6 * LB ? 3 * LJ : 6 * LB;
     static constexpr int kStage = kStage0 > LC ? kStage0 : LC;  // floats per row of the staging area
     static constexpr size_t kFloats = 3 * (size_t)C * LC      // T, dM, dT -> dP
@@ -1607,8 +1608,8 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int t = w + 4 * m, rb = t / NR, sb = t % NR;
-            if (t < NT && sb <= rb)
-                dT[m] = mma<JT / 4>(tdD + 16 * rb * LJ, LJ, 1, tBV + 16 * sb * LJ, 1, LJ, dT[m], lane);
+            if (t < NT && sb <= rb)  // both operands contiguous along the value columns
+                dT[m] = mma_k4<JT / 16>(tdD + 16 * rb * LJ, LJ, tBV + 16 * sb * LJ, LJ, dT[m], lane);
         }
         for (int t = w; t < NR * (JT / 16); t += 4) {
             const int rb = t % NR, jb = t / NR;
