@@ -70,6 +70,10 @@ def _ptr(t):
 
 
 def _check(t, name, dtype=None, shape=None, device=None):
+    # fast path: a plain tensor that passes every test (the checks below raise with a message)
+    if (type(t) is torch.Tensor and (dtype is None or t.dtype == dtype) and (device is None or t.device == device)
+            and t.is_cuda and (shape is None or t.shape == shape) and t.is_contiguous()):
+        return
     if t is None:
         return
     if not isinstance(t, torch.Tensor):
@@ -98,8 +102,16 @@ def _gate(g, shape_channel, shape_head):
     return _lib.KDA_GATE_CHANNEL
 
 
+_PLAIN_OPTIONS = {}  # gate kind -> options with nothing else set (kept alive for byref)
+
+
 def _options(gate, every=0, snapshots=None, snapshot_cu=None, gate_scale=None):
     """kda_options; gate_scale given = fused prologue (raw q, k, beta logits, raw gate inputs)."""
+    if every == 0 and snapshots is None and snapshot_cu is None and gate_scale is None:
+        opts = _PLAIN_OPTIONS.get(gate)
+        if opts is None:
+            opts = _PLAIN_OPTIONS[gate] = _lib.Options(gate, 0, None, None, 0, 0.0)
+        return ctypes.byref(opts)
     return ctypes.byref(_lib.Options(gate, every, _ptr(snapshots), _ptr(snapshot_cu), int(gate_scale is not None),
                                      float(gate_scale or 0.0)))
 
