@@ -231,24 +231,24 @@ __device__ __forceinline__ float gate_at(const float* g, int gate_head, int64_t 
     return gate_head ? g[t * H + h] : g[(t * H + h) * (int64_t)DK + c];
 }
 
-// Rows 16 w .. 16 w + 15 of G = tril(ones) g for one 16-channel block (g staged as [C][ldg]);
-// the result has the MFMA accumulator layout (row 16 w + 4 (lane >> 4) + e, column lane & 15).
-template <int C>
-__device__ __forceinline__ floatx4 prefix_rows(const float* g, int ldg, int w, int lane) {
-    const int r = lane & 15, kq = lane >> 4;
-    floatx4 acc = zero4();
-#pragma unroll 4
-    for (int ks = 0; ks < C / 4; ++ks) {
-        const int s = 4 * ks + kq;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s <= 16 * w + r ? 1.f : 0.f, g[s * ldg + r], acc, 0, 0, 0);
-    }
-    return acc;
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order: within each row of 16 lanes by
+// DPP right shifts of 1, 2, 4 and 8 (lanes shifted in from outside the row add 0), then rows 1 and
+// 3 add the last lane of the row before them (DPP row_bcast:15) and rows 2 and 3 add lane 31 (DPP
+// row_bcast:31); rows left out by the row mask add 0.
+__device__ __forceinline__ float wave_prefix64(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
+    return x;
 }
 
 // ------------------------------------------------------------------------------------------
 // factors: one workgroup per (chunk slot, head), under 80 KB of LDS (two per CU).  Key channels
-// are visited in tiles of 32, each tile's cumulative log-decay recomputed there as a product with
-// a lower-triangular matrix of ones.
+// are visited in tiles of 32, each tile's cumulative log-decay recomputed there by a prefix sum over
+// the rows (one lane per row, wave_prefix64).
 //   pass 1: P and M.  Pairs (r, s) in different 16-row blocks i > j use the matrix cores with the
 //           decay split at m, the last row of block j: exp(G_r - G_s) = exp(G_r - G_m) exp(G_m - G_s),
 //           both exponents <= 0, applied to the operands as they are loaded.  Pairs inside a block
@@ -342,20 +342,13 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             }
         }
         lds_barrier();
-        constexpr int NCT = CT / 16;
-        floatx4 G[(NR * NCT + 3) / 4];
+        // G = tril(ones) g, a prefix sum over the rows: wave w scans columns w, w + 4, ... with one
+        // lane per row (each wave reads and writes only its own columns)
+        static_assert(C <= 64, "one lane per chunk row");
 #pragma unroll
-        for (int m = 0; m < (NR * NCT + 3) / 4; ++m) {
-            const int t = w + 4 * m, rb = t % NR, cb = t / NR;
-            if (t < NR * NCT) G[m] = prefix_rows<C>(tG + 16 * cb, LT, rb, lane);
-        }
-        lds_barrier();
-#pragma unroll
-        for (int m = 0; m < (NR * NCT + 3) / 4; ++m) {
-            const int t = w + 4 * m, rb = t % NR, cb = t / NR;
-            if (t < NR * NCT)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tG[(16 * rb + 4 * lg + e) * LT + 16 * cb + lr] = G[m][e];
+        for (int j = w; j < CT; j += 4) {
+            const float x = wave_prefix64(lane < C ? tG[lane * LT + j] : 0.f);
+            if (lane < C) tG[lane * LT + j] = x;
         }
         lds_barrier();
     };
@@ -1437,7 +1430,7 @@ __global__ __launch_bounds__(kThreads) void grad_state_split_kernel(BwdArgs a, M
 // ------------------------------------------------------------------------------------------
 // grad_chunk: one workgroup per (chunk slot, head); dq, dk, dv, dg, dbeta.  Under 80 KB of LDS
 // (two workgroups per CU): the key channels are visited in blocks of 16, and each block's
-// cumulative log-decay is recomputed there as a product with a lower-triangular matrix of ones.
+// cumulative log-decay is recomputed there by a prefix sum over the rows (wave_prefix64).
 // ------------------------------------------------------------------------------------------
 template <int DK, int DV, int C>
 struct ChunkLds {
@@ -1635,13 +1628,12 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         put_block(br, false);
         fetch_block(cb + 1 < NCB ? cb + 1 : cb, false, br);
         lds_barrier();
-        if (w < NR) {  // G rows of block w, then beta K+ = beta k exp(G) into tKp
-            const floatx4 G = prefix_rows<C>(tdG, LB, w, lane);
+        // G = tril(ones) g by columns (wave w: columns w, w + 4, ...; one lane per row), then
+        // beta K+ = beta k exp(G) into tKp
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * w + 4 * (lane >> 4) + e, cc = lane & 15;
-                tKp[r * LB + cc] = sB[r] * tK[r * LB + cc] * fast_exp(G[e]);
-            }
+        for (int j = w; j < 16; j += 4) {
+            const float G = wave_prefix64(lane < C ? tdG[lane * LB + j] : 0.f);
+            if (lane < C) tKp[lane * LB + j] = sB[lane] * tK[lane * LB + j] * fast_exp(G);
         }
         lds_barrier();
 #pragma unroll
@@ -1728,18 +1720,23 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         put_block(br, true);
         fetch_block(cb + 1 < NCB ? cb + 1 : cb, true, br);
         lds_barrier();
+        // G = tril(ones) g into tG by columns (wave w: columns w, w + 4, ...; one lane per row)
+#pragma unroll
+        for (int j = w; j < 16; j += 4) {
+            const float G = wave_prefix64(lane < C ? tdG[lane * LB + j] : 0.f);
+            if (lane < C) tG[lane * LB + j] = G;
+        }
+        lds_barrier();
         float Gr[4] = {0.f, 0.f, 0.f, 0.f}, xk[4] = {0.f, 0.f, 0.f, 0.f};
         if (w < NR) {
-            const floatx4 G = prefix_rows<C>(tdG, LB, w, lane);
             const floatx4 x = mma<C / 4>(sT + 16 * w, 1, LC, tW, LB, 1, zero4(), lane);
             float part[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + 4 * lg + e;
-                Gr[e] = G[e];
-                tG[r * LB + lr] = G[e];
+                Gr[e] = tG[r * LB + lr];
                 xk[e] = sB[r] * x[e];
-                part[e] = tK[r * LB + lr] * fast_exp(G[e]) * x[e];
+                part[e] = tK[r * LB + lr] * fast_exp(Gr[e]) * x[e];
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
