@@ -1854,25 +1854,24 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
                 tdG[r * LB + lr] = dGr[e] + (r == L - 1 ? col + dgam * fast_exp(glast) : 0.f);
             }
         lds_barrier();
-        // dg = suffix sums over the chunk's rows: dg = Triu(ones) dG
-        if (w < NR) {
-            floatx4 acc = zero4(), acc1 = zero4();
+        // dg = suffix sums over the chunk's rows, by columns: wave w scans columns w, w + 4, ..., lane
+        // l on row C - 1 - l, so that its prefix sum is that row's suffix sum (in place)
 #pragma unroll
-            for (int ks = 0; ks < C / 4; ks += 2) {
-                const int s2 = 4 * ks + lg, s3 = s2 + 4;
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s2 >= 16 * w + lr ? 1.f : 0.f, tdG[s2 * LB + lr], acc, 0, 0,
-                                                           0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(s3 >= 16 * w + lr ? 1.f : 0.f, tdG[s3 * LB + lr], acc1, 0,
-                                                            0, 0);
-            }
-            acc += acc1;
+        for (int j = w; j < 16; j += 4) {
+            const int row = lane < C ? C - 1 - lane : 0;
+            const float sfx = wave_prefix64(lane < C ? tdG[row * LB + j] : 0.f);
+            if (lane < C) tdG[row * LB + j] = sfx;
+        }
+        lds_barrier();
+        if (w < NR) {
             float hsum[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rr = 16 * w + 4 * lg + e;
+                const float dg = tdG[rr * LB + lr];
                 if (!a.gate_head)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), ggrs, (rr * H * DK + ch) * 4, 0, 0);
-                hsum[e] = sum16(acc[e]);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dg), ggrs, (rr * H * DK + ch) * 4, 0, 0);
+                hsum[e] = sum16(dg);
             }
             if (a.gate_head && lr == 0)
 #pragma unroll
