@@ -1518,10 +1518,23 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         }
     };
     fetch_value(0);
-    for (int e = tid; e < C * C; e += kThreads) {
-        const int r = e / C, s = e % C;
-        sT[r * LC + s] = rec[R::T + e];
-        sdM[r * LC + s] = rec[R::dM + e];
+    {  // T and dM: every load requested before the stores (a static trip count lets them batch)
+        constexpr int TPT = (C * C + kThreads - 1) / kThreads;
+        float tv[TPT], mv[TPT];
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) {
+            const int e = tid + kThreads * m, ec = e < C * C ? e : C * C - 1;
+            tv[m] = rec[R::T + ec];
+            mv[m] = rec[R::dM + ec];
+        }
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) {
+            const int e = tid + kThreads * m;
+            if (TPT * kThreads == C * C || e < C * C) {
+                sT[(e / C) * LC + e % C] = tv[m];
+                sdM[(e / C) * LC + e % C] = mv[m];
+            }
+        }
     }
     if (tid < C) {
         sB[tid] = tid < L ? ld_in<TI>(beta, (t0 + tid) * H + h) : 0.f;
