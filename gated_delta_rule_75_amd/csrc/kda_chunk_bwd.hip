@@ -65,6 +65,19 @@ __device__ __forceinline__ floatx4 mma(const float* A, int ar, int ak, const flo
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// f(e) for e = tid, tid + S kThreads, tid + 2 S kThreads, ... below N (S = 1, or 2 for element pairs
+// at even e = S tid + ...), unrolled over a static trip count so that the compiler can issue the
+// loop's memory operations together instead of one iteration at a time.
+template <int N, int S = 1, typename F>
+__device__ __forceinline__ void for_each_elem(int tid, F&& f) {
+    constexpr int IT = (N + S * kThreads - 1) / (S * kThreads);
+#pragma unroll
+    for (int m = 0; m < IT; ++m) {
+        const int e = S * tid + S * kThreads * m;
+        if (IT * S * kThreads == N || e < N) f(e);
+    }
+}
+
 // acc += A (16 x 16 KS) * B (16 KS x 16) with both operands contiguous along k in LDS:
 // A(r, k) = A[r * ar + k] and B(k, c) = Bt[c * bc + k], ar and bc multiples of 4.  Lane (r, kq) feeds
 // k = 16 s + 4 kq + i at the i-th of the four steps of group s (any assignment of k to steps gives the
@@ -446,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         if (tid == 0) *sFlag = 0;
     }
     // P, M into LDS: zero above the blocks' diagonal, then the two kinds of pairs
-    for (int e = tid; e < C * C; e += kThreads) {
+    for_each_elem<C * C>(tid, [&](int e) {
         const int r = e / C, s2 = e % C;
         if (s2 / 16 > r / 16) {
             sP[r * LC + s2] = 0.f;
@@ -455,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             sP[r * LC + s2] = 0.f;
             sM[r * LC + s2] = 0.f;
         }
-    }
+    });
     if (w < NR)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -483,26 +496,26 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
             }
     lds_barrier();
     if constexpr (SPLIT) {
-        for (int e = 2 * tid; e < C * C; e += 2 * kThreads) {  // element pairs along a row
+        for_each_elem<C * C, 2>(tid, [&](int e) {  // element pairs along a row
             const int r = e / C, s2 = e % C;
             put_pair(rec, R::MT, C * C, e, sM[s2 * LC + r], sM[(s2 + 1) * LC + r]);  // M^T[r][s2] = M[s2][r]
             *reinterpret_cast<float2*>(rec + R::P + e) = make_float2(sP[r * LC + s2], sP[r * LC + s2 + 1]);
-        }
+        });
     } else {
-        for (int e = tid; e < C * C; e += kThreads) {
+        for_each_elem<C * C>(tid, [&](int e) {
             const int r = e / C, s2 = e % C;
             rec[R::MT + e] = sM[s2 * LC + r];  // M^T[r][s2] = M[s2][r]
             rec[R::P + e] = sP[r * LC + s2];
-        }
+        });
     }
     lds_barrier();
     // A = Diag(beta) P into M's buffer; T zeroed
     float* sA = sM;
-    for (int e = tid; e < C * C; e += kThreads) {
+    for_each_elem<C * C>(tid, [&](int e) {
         const int r = e / C, s2 = e % C;
         sA[r * LC + s2] = sB[r] * sP[r * LC + s2];
         sT[r * LC + s2] = 0.f;
-    }
+    });
     lds_barrier();
 
     // T = (I + A)^{-1}, unit lower triangular.  Diagonal 16x16 blocks by forward substitution (lane =
@@ -540,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         }
         lds_barrier();
     }
-    for (int e = tid; e < C * C; e += kThreads) rec[R::T + e] = sT[(e / C) * LC + e % C];
+    for_each_elem<C * C>(tid, [&](int e) { rec[R::T + e] = sT[(e / C) * LC + e % C]; });
 
     // ---- pass 2: Q+^T, K', K'^T, gamma and W = T (beta K+), channel tile by channel tile
 #pragma unroll
@@ -552,25 +565,25 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         else
             fetch_value(0);
         if constexpr (SPLIT) {
-            for (int e = 2 * tid; e < C * CT; e += 2 * kThreads) {  // channel-major, token pairs
+            for_each_elem<C * CT, 2>(tid, [&](int e) {  // channel-major, token pairs
                 const int cc = e / C, r = e % C;
                 const float g0 = tG[r * LT + cc], g1 = tG[(r + 1) * LT + cc], gl = tG[(C - 1) * LT + cc];
                 put_pair(rec, R::QpT, DK * C, (c0 + cc) * C + r, tQ[r * LT + cc] * fast_exp(g0),
                          tQ[(r + 1) * LT + cc] * fast_exp(g1));
                 put_pair(rec, R::KdT, DK * C, (c0 + cc) * C + r, tK[r * LT + cc] * fast_exp(gl - g0),
                          tK[(r + 1) * LT + cc] * fast_exp(gl - g1));
-            }
+            });
         } else {
-            for (int e = tid; e < C * CT; e += kThreads) {  // channel-major outputs (token index fastest)
+            for_each_elem<C * CT>(tid, [&](int e) {  // channel-major outputs (token index fastest)
                 const int cc = e / C, r = e % C;
                 const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc];
                 rec[R::QpT + (c0 + cc) * C + r] = tQ[r * LT + cc] * fast_exp(g);
                 rec[R::KdT + (c0 + cc) * C + r] = tK[r * LT + cc] * fast_exp(gl - g);
-            }
+            });
         }
         lds_barrier();
         if constexpr (SPLIT) {
-            for (int e = 2 * tid; e < C * CT; e += 2 * kThreads) {  // token-major, channel pairs
+            for_each_elem<C * CT, 2>(tid, [&](int e) {  // token-major, channel pairs
                 const int r = e / CT, cc = e % CT;
                 const float g0 = tG[r * LT + cc], g1 = tG[r * LT + cc + 1];
                 const float gl0 = tG[(C - 1) * LT + cc], gl1 = tG[(C - 1) * LT + cc + 1];
@@ -578,14 +591,14 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
                 put_pair(rec, R::Kd, C * DK, r * DK + c0 + cc, k0 * fast_exp(gl0 - g0), k1 * fast_exp(gl1 - g1));
                 tK[r * LT + cc] = sB[r] * k0 * fast_exp(g0);
                 tK[r * LT + cc + 1] = sB[r] * k1 * fast_exp(g1);
-            }
+            });
         } else {
-            for (int e = tid; e < C * CT; e += kThreads) {  // token-major outputs; K becomes beta K+ in place
+            for_each_elem<C * CT>(tid, [&](int e) {  // token-major outputs; K becomes beta K+ in place
                 const int r = e / CT, cc = e % CT;
                 const float g = tG[r * LT + cc], gl = tG[(C - 1) * LT + cc], kk = tK[r * LT + cc];
                 rec[R::Kd + r * DK + c0 + cc] = kk * fast_exp(gl - g);
                 tK[r * LT + cc] = sB[r] * kk * fast_exp(g);
-            }
+            });
         }
         if (tid < CT) rec[R::gam + c0 + tid] = fast_exp(tG[(C - 1) * LT + tid]);
         lds_barrier();
@@ -763,8 +776,9 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
         pK.store(sKT, LT);
         pU.store(sU, kBV);
         pg.store(sg, DK);
-        for (int e = tid; e < DK * kBV; e += kThreads)
+        for_each_elem<DK * kBV>(tid, [&](int e) {
             rec[R::S0 + (e / kBV) * DV + vb * kBV + e % kBV] = sSt[(e % kBV) * LW + e / kBV];
+        });
         lds_barrier();
         // D = U - W S (rows 16 w .. 16 w + 15 per wave)
         for (int rb = w; rb < C / 16; rb += 4) {
@@ -871,8 +885,9 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_split_kernel(BwdArgs a, Ma
         pKl.store(sKT[1], LTh);
         pU.store(sU, kBV);
         pg.store(sg, DK);
-        for (int e = tid; e < DK * kBV; e += kThreads)
+        for_each_elem<DK * kBV>(tid, [&](int e) {
             rec[R::S0 + (e / kBV) * DV + vb * kBV + e % kBV] = sSt[(e % kBV) * LW + e / kBV];
+        });
         lds_barrier();
         // D = U - W S (rows 16 w .. 16 w + 15)
         if (w < NR) {
@@ -996,8 +1011,9 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
             const int e = tid + m * kThreads;
             if (e < C * kBV) sdOt[(e % kBV) * LT + e / kBV] = rdo[m];
         }
-        for (int e = tid; e < DK * kBV; e += kThreads)
+        for_each_elem<DK * kBV>(tid, [&](int e) {
             rec[R::dS1 + (e / kBV) * DV + vb * kBV + e % kBV] = sdSt[(e % kBV) * LW + e / kBV];
+        });
         lds_barrier();
         // dD = K' dS + M^T dO
         for (int rb = w; rb < C / 16; rb += 4) {
@@ -1128,8 +1144,9 @@ __global__ __launch_bounds__(kThreads) void rev_chain_split_kernel(BwdArgs a, Ma
                 reinterpret_cast<__bf16*>(sdOh[1])[j * 2 * LTh + r] = (__bf16)(rdo[m] - (float)hi);
             }
         }
-        for (int e = tid; e < DK * kBV; e += kThreads)
+        for_each_elem<DK * kBV>(tid, [&](int e) {
             rec[R::dS1 + (e / kBV) * DV + vb * kBV + e % kBV] = sdSt[(e % kBV) * LW + e / kBV];
+        });
         lds_barrier();
         // dD = K' dS + M^T dO (rows 16 w .. 16 w + 15)
         if (w < NR) {
