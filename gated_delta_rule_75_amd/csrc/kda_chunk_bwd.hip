@@ -78,6 +78,18 @@ __device__ __forceinline__ void for_each_elem(int tid, F&& f) {
     }
 }
 
+// f(i) for i = w, w + 4, w + 8, ... below N (w = this wave, one of 4), unrolled over a static trip
+// count like for_each_elem.
+template <int N, typename F>
+__device__ __forceinline__ void for_each_wave(int w, F&& f) {
+    constexpr int IT = (N + 3) / 4;
+#pragma unroll
+    for (int m = 0; m < IT; ++m) {
+        const int i = w + 4 * m;
+        if (4 * IT == N || i < N) f(i);
+    }
+}
+
 // acc += A (16 x 16 KS) * B (16 KS x 16) with both operands contiguous along k in LDS:
 // A(r, k) = A[r * ar + k] and B(k, c) = Bt[c * bc + k], ar and bc multiples of 4.  Lane (r, kq) feeds
 // k = 16 s + 4 kq + i at the i-th of the four steps of group s (any assignment of k to steps gives the
@@ -358,11 +370,10 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         // G = tril(ones) g, a prefix sum over the rows: wave w scans columns w, w + 4, ... with one
         // lane per row (each wave reads and writes only its own columns)
         static_assert(C <= 64, "one lane per chunk row");
-#pragma unroll
-        for (int j = w; j < CT; j += 4) {
+        for_each_wave<CT>(w, [&](int j) {
             const float x = wave_prefix64(lane < C ? tG[lane * LT + j] : 0.f);
             if (lane < C) tG[lane * LT + j] = x;
-        }
+        });
         lds_barrier();
     };
     fetch_tile(0);
@@ -602,7 +613,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         }
         if (tid < CT) rec[R::gam + c0 + tid] = fast_exp(tG[(C - 1) * LT + tid]);
         lds_barrier();
-        for (int t = w; t < NR * (CT / 16); t += 4) {
+        for_each_wave<NR * (CT / 16)>(w, [&](int t) {
             const int rb = t % NR, cb = t / NR;
             const floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, tK + 16 * cb, LT, 1, zero4(), lane);
             if constexpr (SPLIT) {
@@ -625,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
                 *reinterpret_cast<float4*>(rec + R::WT + (int64_t)(c0 + 16 * cb + lr) * C + 16 * rb + 4 * lg) =
                     make_float4(acc[0], acc[1], acc[2], acc[3]);
             }
-        }
+        });
         lds_barrier();
     }
     // ---- pass 3: U = T (beta V), value tile by value tile (beta V staged in q's buffer)
@@ -638,12 +649,12 @@ __global__ __launch_bounds__(kThreads, 2) void factors_kernel(BwdArgs a, Map<C> 
         }
         fetch_value(j0 + VT < DV ? j0 + VT : j0);
         lds_barrier();
-        for (int t = w; t < NR * (VT / 16); t += 4) {
+        for_each_wave<NR * (VT / 16)>(w, [&](int t) {
             const int rb = t % NR, cb = t / NR;
             const floatx4 acc = mma<C / 4>(sT + 16 * rb * LC, LC, 1, tQ + 16 * cb, LT, 1, zero4(), lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) rec[R::U + (16 * rb + 4 * lg + e) * DV + j0 + 16 * cb + lr] = acc[e];
-        }
+        });
         lds_barrier();
     }
 }
@@ -781,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
         });
         lds_barrier();
         // D = U - W S (rows 16 w .. 16 w + 15 per wave)
-        for (int rb = w; rb < C / 16; rb += 4) {
+        for_each_wave<C / 16>(w, [&](int rb) {
             const floatx4 acc = mma_k4<DK / 16>(sW + 16 * rb * LW, LW, sSt, LW, zero4(), lane);
             float4 dv;
 #pragma unroll
@@ -792,7 +803,7 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
                 rec[R::D + r * DV + vb * kBV + lr] = d;
             }
             *reinterpret_cast<float4*>(sDt + lr * LT + 16 * rb + 4 * lg) = dv;
-        }
+        });
         lds_barrier();
         // the next chunk's operands and the L2 warm-up are requested here, after D: issued before
         // it, their loads held up the product that the next barrier waits for
@@ -802,14 +813,13 @@ __global__ __launch_bounds__(kThreads) void fwd_chain_kernel(BwdArgs a, Map<C> m
             warm_range<R::Kd>(wrec, 0, vb, NVB, dummy);
         }
         // S <- Diag(gamma) S + K'^T D
-#pragma unroll
-        for (int cb = w; cb < DK / 16; cb += 4) {
+        for_each_wave<DK / 16>(w, [&](int cb) {
             const int i0 = 16 * cb + 4 * lg;
             const float4 s4 = *reinterpret_cast<const float4*>(sSt + lr * LW + i0);
             floatx4 acc = {sg[i0] * s4.x, sg[i0 + 1] * s4.y, sg[i0 + 2] * s4.z, sg[i0 + 3] * s4.w};
             acc = mma_k4<C / 16>(sKT + 16 * cb * LT, LT, sDt, LT, acc, lane);
             *reinterpret_cast<float4*>(sSt + lr * LW + i0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        }
+        });
     }
     if (s_fin) {  // the state after the last chunk (a checkpoint for a later window)
         lds_barrier();
@@ -1016,13 +1026,13 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
         });
         lds_barrier();
         // dD = K' dS + M^T dO
-        for (int rb = w; rb < C / 16; rb += 4) {
+        for_each_wave<C / 16>(w, [&](int rb) {
             floatx4 acc = mma_k4<DK / 16>(sKd + 16 * rb * LW, LW, sdSt, LW, zero4(), lane);
             acc = mma_k4<C / 16>(sMT + 16 * rb * LT, LT, sdOt, LT, acc, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) rec[R::dD + (16 * rb + 4 * lg + e) * DV + vb * kBV + lr] = acc[e];
             *reinterpret_cast<float4*>(sdDt + lr * LT + 16 * rb + 4 * lg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        }
+        });
         lds_barrier();
         // the previous chunk's operands and the L2 warm-up are requested here, after dD (see
         // fwd_chain)
@@ -1032,8 +1042,7 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
             warm_range<R::T - R::Kd>(wrec, R::Kd, vb, NVB, dummy);
         }
         // dS <- Diag(gamma) dS + Q+^T dO - W^T dD
-#pragma unroll
-        for (int cb = w; cb < DK / 16; cb += 4) {
+        for_each_wave<DK / 16>(w, [&](int cb) {
             const int i0 = 16 * cb + 4 * lg;
             const float4 s4 = *reinterpret_cast<const float4*>(sdSt + lr * LW + i0);
             floatx4 acc = {sg[i0] * s4.x, sg[i0 + 1] * s4.y, sg[i0 + 2] * s4.z, sg[i0 + 3] * s4.w};
@@ -1041,7 +1050,7 @@ __global__ __launch_bounds__(kThreads) void rev_chain_kernel(BwdArgs a, Map<C> m
             const floatx4 wd = mma_k4<C / 16>(sWT + 16 * cb * LT, LT, sdDt, LT, zero4(), lane);
             *reinterpret_cast<float4*>(sdSt + lr * LW + i0) =
                 make_float4(acc[0] - wd[0], acc[1] - wd[1], acc[2] - wd[2], acc[3] - wd[3]);
-        }
+        });
     }
     lds_barrier();
     if (a.gs0)
@@ -1634,7 +1643,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
             if (t < NT && sb <= rb)  // both operands contiguous along the value columns
                 dT[m] = mma_k4<JT / 16>(tdD + 16 * rb * LJ, LJ, tBV + 16 * sb * LJ, LJ, dT[m], lane);
         }
-        for (int t = w; t < NR * (JT / 16); t += 4) {
+        for_each_wave<NR * (JT / 16)>(w, [&](int t) {
             const int rb = t % NR, jb = t / NR;
             const floatx4 x = mma<C / 4>(sT + 16 * rb, 1, LC, tdD + 16 * jb, LJ, 1, zero4(), lane);
             float part[4];
@@ -1649,7 +1658,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
                 const float p = sum16(part[e]);
                 if ((lane & 15) == 0) sdbw[w * C + 16 * rb + 4 * (lane >> 4) + e] += p;
             }
-        }
+        });
         lds_barrier();
     }
     BlockRegs br;
@@ -1660,11 +1669,10 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         lds_barrier();
         // G = tril(ones) g by columns (wave w: columns w, w + 4, ...; one lane per row), then
         // beta K+ = beta k exp(G) into tKp
-#pragma unroll
-        for (int j = w; j < 16; j += 4) {
+        for_each_wave<16>(w, [&](int j) {
             const float G = wave_prefix64(lane < C ? tdG[lane * LB + j] : 0.f);
             if (lane < C) tKp[lane * LB + j] = sB[lane] * tK[lane * LB + j] * fast_exp(G);
-        }
+        });
         lds_barrier();
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
@@ -1751,11 +1759,10 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         fetch_block(cb + 1 < NCB ? cb + 1 : cb, true, br);
         lds_barrier();
         // G = tril(ones) g into tG by columns (wave w: columns w, w + 4, ...; one lane per row)
-#pragma unroll
-        for (int j = w; j < 16; j += 4) {
+        for_each_wave<16>(w, [&](int j) {
             const float G = wave_prefix64(lane < C ? tdG[lane * LB + j] : 0.f);
             if (lane < C) tG[lane * LB + j] = G;
-        }
+        });
         lds_barrier();
         float Gr[4] = {0.f, 0.f, 0.f, 0.f}, xk[4] = {0.f, 0.f, 0.f, 0.f};
         if (w < NR) {
@@ -1886,12 +1893,11 @@ __global__ __launch_bounds__(kThreads, 2) void grad_chunk_kernel(BwdArgs a, Map<
         lds_barrier();
         // dg = suffix sums over the chunk's rows, by columns: wave w scans columns w, w + 4, ..., lane
         // l on row C - 1 - l, so that its prefix sum is that row's suffix sum (in place)
-#pragma unroll
-        for (int j = w; j < 16; j += 4) {
+        for_each_wave<16>(w, [&](int j) {
             const int row = lane < C ? C - 1 - lane : 0;
             const float sfx = wave_prefix64(lane < C ? tdG[row * LB + j] : 0.f);
             if (lane < C) tdG[row * LB + j] = sfx;
-        }
+        });
         lds_barrier();
         if (w < NR) {
             float hsum[4];
