@@ -60,7 +60,7 @@ _MFMA_SHA = "6c4a05405bdcb1d57d471965b4de7627f2eb4e3f956caac226f03ae2219e73cb"
 _DECODE_SRC = "gated_delta_rule_75_amd/csrc/kda_decode.hip"
 _DECODE_SHA = "8f6da261804d588a7c98da378838a326741fe49876b995ac0c4a84bf7b3318b3"
 _BWD_SRC = "gated_delta_rule_75_amd/csrc/kda_chunk_bwd.hip"
-_BWD_SHA = "987057366f7c0285fe492e97d8d33d1b69475633b50b06a65b495509a1bcfe68"
+_BWD_SHA = "f1543487f96d6ce26799a14ce5f61491ee8107969deb57afc14457435247bf76"
 
 
 def _counted(fetch_kib, write_kib):
@@ -77,8 +77,8 @@ MEASURED_TRAFFIC = {
                    "bytes": _counted(267359.5, 528576.9)},
     # the five backward kernels of one pass (factors, fwd_chain, rev_chain, grad_state, grad_chunk)
     "kda_backward": {"source": _BWD_SRC, "sha256": _BWD_SHA, "workload": "backward T=65536 H=32",
-                     "bytes": _counted(3469321.9 + 1605898.6 + 2389694.2 + 3708312.2 + 9041862.8,
-                                       8275342.5 + 3477244.6 + 3145738.5 + 3688142.3 + 4440684.8)},
+                     "bytes": _counted(3422889.8 + 1601701.1 + 2378565.3 + 3704807.7 + 8924465.5,
+                                       8270730.2 + 3372507.2 + 3161753.2 + 3687807.8 + 4414699.4)},
 }
 
 
