@@ -882,7 +882,7 @@ def bench_workloads(args, res):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        print("bench.py: the library runs on one GPU (it has no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 
