@@ -90,7 +90,14 @@ def _check(t, name, dtype=None, shape=None, device=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+# torch's raw accessor of the current stream handle (no Stream object per call: about 0.1 us
+# against 1.9 us for torch.cuda.current_stream(device).cuda_stream); the public call otherwise
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device):
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(device.index if device.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(device).cuda_stream
 
 
