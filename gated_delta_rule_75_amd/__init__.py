@@ -70,10 +70,13 @@ def _ptr(t):
 
 
 def _check(t, name, dtype=None, shape=None, device=None):
-    # fast path: a plain tensor that passes every test (the checks below raise with a message)
-    if (type(t) is torch.Tensor and (dtype is None or t.dtype == dtype) and (device is None or t.device == device)
-            and t.is_cuda and (shape is None or t.shape == shape) and t.is_contiguous()):
-        return
+    # fast path: a plain tensor that passes every test (the checks below raise with a message);
+    # get_device() is an int (-1 on the CPU), cheaper than building the tensor's device object
+    if type(t) is torch.Tensor:
+        di = t.get_device()
+        if (di >= 0 and (device is None or di == device.index) and (dtype is None or t.dtype == dtype)
+                and (shape is None or t.shape == shape) and t.is_contiguous()):
+            return
     if t is None:
         return
     if not isinstance(t, torch.Tensor):
