@@ -173,7 +173,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20, help="timed prefill steps")
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20, help="untimed prefill passes first (the clocks settle within about 20)")
     ap.add_argument("--T", type=int, default=65536, help="prefill tokens")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--decode-warmup", type=int, default=10)
